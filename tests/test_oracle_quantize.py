@@ -1,0 +1,287 @@
+"""Tensor-level pins of the oracle's quantizer, dequantizer and GEMM reference.
+
+Each test checks the oracle against something other than itself: a worked
+example printed on the pages, an invariant the pages state, a library routine
+(numpy matmul, torch fp8 decode), brute force, or a statistical law of
+Full-Stack FP4 Appendix 7 (eq. 5 and the Theta(N) growth).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load_example():
+    d = {}
+    with open(os.path.join(GOLDEN, "opt_outlier_example.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                k, *v = line.split()
+                d[k] = [float(t) for t in v]
+    return d
+
+
+def grid_value(codes):
+    """Decode 4-bit codes with the golden E2M1 table (independent of the oracle)."""
+    pos = {}
+    with open(os.path.join(GOLDEN, "e2m1_grid.txt")) as f:
+        for line in f:
+            t = line.split()
+            if len(t) == 3 and not line.startswith("#"):
+                pos[(int(t[0]) << 1) | int(t[1])] = float(t[2])
+    table = np.array([pos[c & 7] * (-1.0 if c & 8 else 1.0) for c in range(16)])
+    return table[codes]
+
+
+def scale_value(scodes):
+    """E4M3 decode via torch's float8_e4m3fn (library routine)."""
+    t = torch.from_numpy(np.ascontiguousarray(scodes)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def dequant64(oracle, q):
+    """Exact dequantized values in binary64, decoded independently of the oracle."""
+    v = grid_value(oracle.unpack_codes(q.codes))
+    s = np.repeat(scale_value(q.scales), 16, axis=1)
+    return v * s * np.float64(q.sg)
+
+
+# ------------------------------------------------------------------ worked example
+def test_outlier_example_from_optitrain_readme(oracle):
+    ex = load_example()
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, :8] = ex["input"]
+    x[0, 16] = 2688.0            # second block fixes amax_t = 6*448, so s_g = 1 exactly
+    row, _ = oracle.quantize(x)
+    assert row.sg == 1.0
+    assert oracle.e4m3_value(row.scales[0, 0]) == ex["block_scale_e4m3"][0]
+    deq = oracle.dequantize(row)
+    assert deq[0, :8].tolist() == ex["decoded"]
+    assert np.all(deq[0, 8:16] == 0.0)
+
+
+# ------------------------------------------------------------------ scale invariants
+@pytest.mark.parametrize("kind", ["normal", "spiky", "outliers", "tiny_values"])
+def test_block_amax_maps_to_fp4_max(oracle, kind):
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((64, 256)).astype(np.float32)
+    if kind == "spiky":
+        x[rng.random(x.shape) < 0.01] *= 50
+    if kind == "outliers":
+        x[:, [3, 77, 200]] *= 30
+    if kind == "tiny_values":
+        x *= 1e-6
+    row, _ = oracle.quantize(x)
+    codes = oracle.unpack_codes(row.codes)
+    blocks = np.abs(x).reshape(64, 16, 16)
+    arg = blocks.argmax(axis=2)
+    sc = row.scales
+    amax_t = np.abs(x).max()
+    assert row.sg == np.float32(amax_t) / np.float32(2688.0)
+    for r in range(64):
+        for b in range(16):
+            c = codes[r, b * 16 + arg[r, b]]
+            if sc[r, b] >= 8:                       # normal E4M3 scale
+                assert c & 7 == 7
+                dec = oracle.e2m1_value(c & 7) * oracle.e4m3_value(sc[r, b]) * row.sg
+                true = blocks[r, b, arg[r, b]]
+                assert abs(dec - true) <= true / 16 * 1.0001   # NVFP4 sec. 2: near-FP8 element
+            if blocks[r, b].max() == amax_t:
+                assert sc[r, b] == 0x7E                # tensor amax block gets s = 448
+
+
+def test_zero_and_negative_zero_tensor(oracle):
+    x = np.zeros((16, 32), dtype=np.float32)
+    x[3, 5] = -0.0
+    row, col = oracle.quantize(x, colwise=True)
+    assert row.sg == 1.0 and col.sg == 1.0
+    codes = oracle.unpack_codes(row.codes)
+    assert codes[3, 5] == 8 and codes.sum() == 8
+    assert np.all(row.scales == 0)
+    assert np.all(oracle.dequantize(row) == 0.0)
+
+
+def test_rne_reconstruction_error_is_half_a_step(oracle):
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((32, 128)).astype(np.float32) * 3
+    row, _ = oracle.quantize(x)
+    deq = dequant64(oracle, row)
+    d = np.repeat(scale_value(row.scales), 16, axis=1) * row.sg
+    u = np.abs(x) / d
+    pos = np.array([oracle.e2m1_value(c) for c in range(8)])
+    step = np.interp(u, pos[:-1], np.diff(pos), right=2.0)
+    # half a local step of the grid times the block's decode scale (+ scale-rounding slack)
+    assert np.all(np.abs(deq - x) <= (step / 2 * d) * 1.01 + 1e-12)
+
+
+def test_dequantize_matches_independent_decode(oracle):
+    x = np.random.default_rng(12).standard_normal((48, 64)).astype(np.float32)
+    row, _ = oracle.quantize(x)
+    d64 = dequant64(oracle, row)
+    assert np.array_equal(oracle.dequantize(row), d64.astype(np.float32))
+
+
+def test_2d_blocks_give_one_representation_for_both_directions(oracle):
+    # NVFP4 report sec. 4 / E.2: 2D weight scaling keeps the forward and the
+    # transposed backward copies identical.
+    rng = np.random.default_rng(13)
+    w = (rng.standard_normal((48, 80)) * 0.02).astype(np.float32)
+    row, col = oracle.quantize(w, colwise=True, block2d=True)
+    assert row.sg == col.sg
+    assert np.array_equal(oracle.unpack_codes(col.codes), oracle.unpack_codes(row.codes).T)
+    assert np.array_equal(np.repeat(col.scales, 16, axis=1), np.repeat(row.scales, 16, axis=1).T)
+    # and 1D copies of the same tensor differ (the inconsistency 2D removes)
+    r1, c1 = oracle.quantize(w, colwise=True)
+    assert not np.array_equal(oracle.unpack_codes(c1.codes), oracle.unpack_codes(r1.codes).T)
+
+
+def test_2d_tile_scale_uses_tile_amax(oracle):
+    rng = np.random.default_rng(14)
+    w = rng.standard_normal((32, 32)).astype(np.float32)
+    row, _ = oracle.quantize(w, block2d=True)
+    for ti in range(2):
+        for tj in range(2):
+            amax = np.abs(w[ti*16:ti*16+16, tj*16:tj*16+16]).max()
+            want = oracle.e4m3_encode(np.float32(np.float32(amax) / np.float32(6.0)) / np.float32(row.sg))
+            assert np.all(row.scales[ti*16:ti*16+16, tj] == want)
+
+
+# ------------------------------------------------------------------ GEMM reference
+def test_gemm_reference_equals_numpy_matmul(oracle, ):
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    t = synthetic.tiny()
+    qa, _ = oracle.quantize(t["X"].numpy())
+    qb, _ = oracle.quantize(t["W"].numpy())
+    C, absdot = oracle.gemm_f64(qa, qb)
+    A, B = dequant64(oracle, qa), dequant64(oracle, qb)
+    ref = A @ B.T
+    assert np.allclose(C, ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
+    assert np.allclose(absdot, np.abs(A) @ np.abs(B).T, rtol=1e-13)
+    em = np.array([0, 5, 127, 64]); en = np.array([0, 99, 127, 1])
+    e, ead = oracle.gemm_f64_entries(qa, qb, em, en)
+    assert np.array_equal(e, C[em, en]) and np.array_equal(ead, absdot[em, en])
+
+
+def test_rht_cancels_across_gemm_operands(oracle):
+    # NVFP4 report B.4: the same orthogonal transform on both operands cancels
+    # (H H^T = I), so the rotated quantized GEMM approximates the plain product.
+    rng = np.random.default_rng(15)
+    tok, m, n = 256, 48, 32
+    dy = rng.standard_t(3, (tok, m)).astype(np.float32) * 1e-3
+    x = rng.standard_normal((tok, n)).astype(np.float32)
+    exact = dy.astype(np.float64).T @ x.astype(np.float64)
+    _, qa = oracle.quantize(dy, rowwise=False, colwise=True, rht_col=True, seed=7)
+    _, qb = oracle.quantize(x, rowwise=False, colwise=True, rht_col=True, seed=7)
+    C, _ = oracle.gemm_f64(qa, qb)
+    rel = np.linalg.norm(C - exact) / np.linalg.norm(exact)
+    _, qb2 = oracle.quantize(x, rowwise=False, colwise=True, rht_col=True, seed=8)
+    C2, _ = oracle.gemm_f64(qa, qb2)
+    rel2 = np.linalg.norm(C2 - exact) / np.linalg.norm(exact)
+    assert rel < 0.25 and rel2 > 0.8
+
+
+# ------------------------------------------------------------------ stochastic rounding, statistics
+def test_sr_quantize_is_unbiased_over_seeds(oracle):
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal((16, 64)).astype(np.float32)
+    x[0, 0] = 8.0                 # keep block scales fixed across seeds
+    acc = np.zeros_like(x, dtype=np.float64)
+    acc2 = np.zeros_like(acc)
+    n = 600
+    for s in range(n):
+        row, _ = oracle.quantize(x, round_row=oracle.SR, seed=1000 + s)
+        d = dequant64(oracle, row)
+        acc += d
+        acc2 += d * d
+    mean = acc / n
+    var = acc2 / n - mean * mean
+    row0, _ = oracle.quantize(x)
+    dscale = np.repeat(scale_value(row0.scales), 16, axis=1) * row0.sg
+    u = np.abs(x) / dscale
+    # standard error from the Appendix 7 conditional variance d (Delta - d), not from
+    # the sample (an element just above a grid point may never round up in n draws)
+    pos = np.array([oracle.e2m1_value(c) for c in range(8)])
+    k = np.clip(np.searchsorted(pos, u, side="right") - 1, 0, 6)
+    dd = u - pos[k]
+    delta = pos[k + 1] - pos[k]
+    se = np.sqrt(np.maximum(dd * (delta - dd), 0) * dscale ** 2 / n)
+    bias_bound = 2.0 * dscale / 65536
+    inside = u <= 6.0            # Appendix 7: the saturation cell [6, inf) is treated apart
+    assert inside.mean() > 0.9
+    assert np.all((np.abs(mean - x) <= 5 * se + bias_bound + 1e-9)[inside])
+    assert np.all(np.abs(mean[~inside]) == (6.0 * dscale)[~inside])
+    # the draws differ between seeds and copies
+    a, b = oracle.quantize(x, colwise=True, round_row=oracle.SR, round_col=oracle.SR, seed=1)
+    assert oracle.sr_bits(1, 0, 5) != oracle.sr_bits(1, 1, 5)
+
+
+def _eq5_prediction(oracle, x, w, qx, qw):
+    """Appendix 7 eq. (5) with sigma^2 = d (Delta - d) per element (SR variance)."""
+    pos = np.array([oracle.e2m1_value(c) for c in range(8)])
+
+    def sig2(v, q):
+        d = np.repeat(scale_value(q.scales), 16, axis=1) * np.float64(q.sg)
+        u = np.abs(v.astype(np.float64)) / d
+        k = np.clip(np.searchsorted(pos, u, side="right") - 1, 0, 6)
+        lo, delta = pos[k], pos[k + 1] - pos[k]
+        dd = np.clip(u - lo, 0, None)
+        s = np.where(u >= 6, 0.0, dd * (delta - dd))
+        return s * d * d
+    sx, sw = sig2(x, qx), sig2(w, qw)
+    xx, ww = x.astype(np.float64), w.astype(np.float64)
+    return (xx ** 2 * sw + ww ** 2 * sx + sx * sw).sum()
+
+
+@pytest.mark.parametrize("N", [256, 1024])
+def test_eq5_variance_of_sr_dot_product(oracle, N):
+    rng = np.random.default_rng(17 + N)
+    x = rng.standard_normal((1, N)).astype(np.float32)
+    w = rng.standard_normal((1, N)).astype(np.float32)
+    y = float(np.dot(x[0].astype(np.float64), w[0].astype(np.float64)))
+    qx0, _ = oracle.quantize(x)
+    qw0, _ = oracle.quantize(w)
+    pred = _eq5_prediction(oracle, x, w, qx0, qw0)
+    errs = []
+    for s in range(1500):
+        qx, _ = oracle.quantize(x, round_row=oracle.SR, seed=2 * s + 1)
+        qw, _ = oracle.quantize(w, round_row=oracle.SR, seed=2 * s + 2)
+        c, _ = oracle.gemm_f64(qx, qw)
+        errs.append(c[0, 0] - y)
+    errs = np.array(errs)
+    assert abs(errs.mean()) < 5 * np.sqrt(pred / len(errs))      # E[dY] = 0 under SR
+    assert abs(errs.var() / pred - 1.0) < 0.15                    # eq. (5)
+
+
+def test_dot_product_error_grows_linearly_with_n(oracle):
+    # Appendix 7: Var(dY) = Theta(N) for i.i.d. inputs.
+    rng = np.random.default_rng(18)
+    vs = {}
+    for N in [256, 1024, 4096]:
+        x = rng.standard_normal((1, N)).astype(np.float32)
+        w = rng.standard_normal((1, N)).astype(np.float32)
+        y = float(np.dot(x[0].astype(np.float64), w[0].astype(np.float64)))
+        e = []
+        for s in range(400):
+            qx, _ = oracle.quantize(x, round_row=oracle.SR, seed=3 * s + 1)
+            qw, _ = oracle.quantize(w, round_row=oracle.SR, seed=3 * s + 2)
+            e.append(oracle.gemm_f64(qx, qw)[0][0, 0] - y)
+        vs[N] = np.var(e)
+    r1, r2 = vs[1024] / vs[256], vs[4096] / vs[1024]
+    assert 2.8 < r1 < 5.5 and 2.8 < r2 < 5.5
+
+
+# ------------------------------------------------------------------ argument checks
+def test_oracle_rejects_bad_shapes_and_nonfinite(oracle):
+    with pytest.raises(ValueError):
+        oracle.quantize_rows(np.zeros((4, 20), dtype=np.float32))
+    with pytest.raises(ValueError):
+        oracle.quantize_rows(np.zeros((20, 32), dtype=np.float32), block2d=True)
+    bad = np.zeros((16, 16), dtype=np.float32)
+    bad[1, 1] = np.inf
+    with pytest.raises(ValueError):
+        oracle.quantize_rows(bad)
+    with pytest.raises(ValueError):
+        oracle.qadamw_v_encode(-np.ones((16, 16), dtype=np.float32))
