@@ -1,0 +1,176 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 quantized-linear library.
+ *
+ * The library implements the data-parallel hot path of NVFP4 training as the
+ * pages describe it:
+ *   - Full-Stack FP4 (academ.us 2607.04422), sec. 2 "Preliminaries": NVFP4 =
+ *     E2M1 elements, one E4M3 scale per 1x16 or 16x16 block, one FP32 tensor
+ *     scale; x_hat = x_E2M1 * s * s_g.  Sec. 3.2 eq. (1)-(2): the three GEMMs of
+ *     a linear layer take Q_1x16 / Q_16x1 / Q_16x16 operands, with a fresh
+ *     16x16 random Hadamard transform in the weight-gradient GEMM.  Sec. 3.3:
+ *     the quantized-state AdamW second-moment pipeline.
+ *   - "Pretraining Large Language Models with NVFP4" (paperlayer.ai summary of
+ *     arXiv 2509.25149v2), sec. 2 "NVFP4 Format" (amax of each block maps to the
+ *     FP4 maximum; FP32 tensor scale keeps block scales in E4M3), sec. 4
+ *     "Training Methodology" (RNE for weights/activations, stochastic rounding
+ *     for gradients, 2D weight blocks, RHT on Wgrad inputs), B.4 (scale computed
+ *     in the rotated space), A.2 (decode scales stored for the GEMM).
+ *
+ * Conventions shared by every call
+ *   - Every data pointer is DEVICE memory allocated and owned by the caller;
+ *     struct arguments themselves are host memory read during the call only.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *     validate their arguments on the host, enqueue kernels on `stream` and
+ *     return; they never allocate, free or synchronise the device.
+ *   - Status: NVFP4_OK or a negative NVFP4_ERR_* code.  Argument errors are
+ *     returned before anything is enqueued.  A failed kernel launch returns
+ *     NVFP4_ERR_HIP (from hipGetLastError); faults inside a kernel surface at
+ *     the caller's next synchronisation.
+ *   - Matrices are row-major.  Block dimensions must be multiples of 16 (the
+ *     pages give no padding rule); every other extent may be any size >= 0.
+ *   - Input values must be finite.  Tensors whose largest magnitude is below
+ *     2^-96 give unspecified (but in-bounds) codes.
+ *   - Calls on one stream are ordered; the library holds no state, so calls on
+ *     different streams may run concurrently on distinct buffers.
+ *
+ * Quantized tensor layout (one "copy"): an n x k matrix quantized along its
+ * rows has
+ *   codes  uint8 [n][k/2]   element 2i in the low nibble, 2i+1 in the high
+ *                           nibble; a nibble is sign<<3 | exponent<<1 | mantissa
+ *   scales uint8 [n][k/16]  E4M3 (OCP "fn") code of the block scale; 16x16
+ *                           blocks are stored expanded (each of the 16 rows of a
+ *                           tile repeats its scale)
+ *   gscale float [1]        the FP32 tensor scale s_g
+ * The rowwise copy of an R x C tensor X is X quantized along its rows (n = R,
+ * k = C); the columnwise copy is X^T quantized along its rows (n = C, k = R).
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+enum nvfp4_status {
+    NVFP4_OK = 0,
+    NVFP4_ERR_NULL = -1,      /* a required pointer is NULL */
+    NVFP4_ERR_SHAPE = -2,     /* negative extent, or a block dimension not a multiple of 16 */
+    NVFP4_ERR_ALIGN = -3,     /* pointer or leading dimension not aligned as documented */
+    NVFP4_ERR_DTYPE = -4,     /* unknown dtype enum */
+    NVFP4_ERR_MODE = -5,      /* unknown or unsupported combination of options */
+    NVFP4_ERR_WORKSPACE = -6, /* workspace missing or smaller than required */
+    NVFP4_ERR_HIP = -7        /* kernel launch failed */
+};
+
+enum nvfp4_dtype { NVFP4_F32 = 0, NVFP4_BF16 = 1 };
+enum nvfp4_rounding { NVFP4_RNE = 0, NVFP4_SR = 1 };
+enum nvfp4_block { NVFP4_BLOCK_1D = 0, NVFP4_BLOCK_2D = 1 };
+
+/* Options of one nvfp4_quantize call.
+ *   rowwise, colwise   produce the rowwise and/or the columnwise copy (at least one)
+ *   block              NVFP4_BLOCK_1D: 1x16 blocks along each copy's rows (Q_1x16 for
+ *                      the rowwise copy, Q_16x1 for the columnwise one);
+ *                      NVFP4_BLOCK_2D: 16x16 tiles shared by both copies (Q_16x16), so
+ *                      the columnwise copy is bit-identical to the transposed rowwise
+ *                      copy (NVFP4 report sec. 4).  2D requires RNE and no RHT.
+ *   round_row/col      NVFP4_RNE or NVFP4_SR per copy (the report: RNE for weights and
+ *                      activations, SR for gradients)
+ *   rht_row/col        0/1: apply the random Hadamard transform T(v) = 1/4 H16 (D v) to
+ *                      every 16-chunk along the copy's rows before scaling; D is one
+ *                      random sign vector per call derived from `seed` (Full-Stack FP4
+ *                      sec. 3.2: one random 16x16 Hadamard matrix per backward pass; both
+ *                      Wgrad operands must use the same seed so the transforms cancel)
+ *   seed               key of the Philox4x32-10 generator behind D and the SR draws */
+typedef struct {
+    int32_t rowwise, colwise;
+    int32_t block;
+    int32_t round_row, round_col;
+    int32_t rht_row, rht_col;
+    uint64_t seed;
+} nvfp4_quant_params;
+
+/* One quantized copy (pointers to device memory; see the layout above). */
+typedef struct {
+    uint8_t* codes;
+    uint8_t* scales;
+    float* gscale;
+} nvfp4_qtensor;
+
+/* Device workspace (bytes) nvfp4_quantize needs for a rows x cols input. */
+size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols, const nvfp4_quant_params* p);
+
+/* Quantize X[rows][cols] (row pitch ld_x elements, ld_x >= cols) to NVFP4.
+ * Passages: Full-Stack FP4 sec. 2 (format, x_hat = x_E2M1 s s_g), sec. 3.2 eq. (1)-(2)
+ * (Q_1x16, Q_16x1, Q_16x16, H16^r); NVFP4 report sec. 2 (amax -> FP4 max, FP32 tensor
+ * scale), sec. 4 and E.2 (RNE, SR on gradients, 2D weights, RHT on Wgrad inputs), B.4
+ * (scale computed after the rotation).  Per copy: s_g = amax/(6*448) over the
+ * (rotated) values (1 if that is 0); block scale s = E4M3_rne_sat((amax_b/6)/s_g);
+ * elements u = x * 1/(s*s_g) rounded to E2M1 (nearest-even saturating at 6, or
+ * stochastic: up iff frac + r/2^16 >= 1 with 16 Philox bits r per element).
+ *   x       bf16 or f32 per `dtype`, 16-byte aligned, ld_x * element size a multiple of 16
+ *   row_out rowwise copy ([rows][cols/2] codes, [rows][cols/16] scales, 1 float); may be
+ *           NULL when p->rowwise == 0
+ *   col_out columnwise copy ([cols][rows/2], [cols][rows/16], 1 float); may be NULL when
+ *           p->colwise == 0
+ *   ws      device workspace of at least nvfp4_quantize_workspace_bytes() bytes,
+ *           16-byte aligned; its contents need no initialisation
+ * rows and cols must be multiples of 16; codes arrays 8-byte aligned. */
+int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                   const nvfp4_quant_params* p, const nvfp4_qtensor* row_out,
+                   const nvfp4_qtensor* col_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Decode one copy: out[n][k] = (value(code) * s) * s_g, rounded once to binary32
+ * (Full-Stack FP4 sec. 2), then to bfloat16 nearest-even if out_dtype is NVFP4_BF16.
+ * Rotated copies decode to the rotated values.  out has row pitch ld_out elements
+ * (ld_out >= k); k must be a multiple of 16; codes 8-byte aligned. */
+int nvfp4_dequantize(const nvfp4_qtensor* q, int64_t n, int64_t k, int out_dtype, void* out,
+                     int64_t ld_out, void* stream);
+
+/* W4A4 GEMM: C[M][N] = s_gA s_gB * sum_k (v(qA[m,k]) sA[m,k/16]) (v(qB[n,k]) sB[n,k/16]),
+ * both operands K-major copies (A: M x K, B: N x K, as produced by nvfp4_quantize), FP32
+ * accumulation, FP32 output with row pitch ldc >= N.
+ * Passages: Full-Stack FP4 sec. 2 and eq. (1)-(2) (Fprop Y = X W^T, Dgrad, Wgrad on
+ * NVFP4 operands); NVFP4 report sec. 4 (FP4 inputs, FP32 output) and A.2 (decode scales
+ * stored for the GEMM).  Every product of a decoded element and its block scale is
+ * exact in binary16, so the only rounding is the FP32 accumulation.
+ * K must be a multiple of 16; M and N any size >= 0; codes 16-byte aligned with row pitch
+ * K/2 a multiple of 16 bytes (K % 32 == 0), C 4-byte aligned. */
+int nvfp4_gemm(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
+               int64_t K, float* c, int64_t ldc, void* stream);
+
+/* Device workspace (bytes) qadamw_v_encode needs. */
+size_t qadamw_v_workspace_bytes(int64_t rows, int64_t cols);
+
+/* Quantized-state AdamW second moment (Full-Stack FP4 sec. 3.3; gist.science summary
+ * sec. 2.2): y = sqrt(v); mu = per-16x16-tile mean of y stored as bfloat16; residual
+ * y - mu; random Hadamard transform of each 1x16 chunk along the rows (signs from
+ * `seed` when use_signs != 0, plain normalised H16 otherwise); NVFP4 1x16
+ * nearest-even quantization of the residual.
+ *   v       f32 [rows][cols], non-negative, 16-byte aligned
+ *   mu      bf16 bits [rows/16][cols/16]
+ *   q       one copy: codes [rows][cols/2], scales [rows][cols/16], gscale
+ *   ws      workspace of at least qadamw_v_workspace_bytes() bytes
+ * rows and cols must be multiples of 16. */
+int qadamw_v_encode(const float* v, int64_t rows, int64_t cols, uint64_t seed, int32_t use_signs,
+                    uint16_t* mu, const nvfp4_qtensor* q, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Inverse pipeline: v_out = (D (1/4 H16 x_hat) + mu)^2 with x_hat the dequantized
+ * residual (reconstruction formula of Full-Stack FP4 sec. 3.3).  Same layouts; seed and
+ * use_signs must match the encode call. */
+int qadamw_v_decode(const uint16_t* mu, const nvfp4_qtensor* q, int64_t rows, int64_t cols,
+                    uint64_t seed, int32_t use_signs, float* v_out, void* stream);
+
+/* Static string naming a status code. */
+const char* nvfp4_status_string(int status);
+/* NVFP4_ABI_VERSION of the loaded library. */
+int nvfp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

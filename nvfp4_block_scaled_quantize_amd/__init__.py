@@ -1,0 +1,243 @@
+"""NVFP4 quantized-linear hot path for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding of the C ABI in ``include/nvfp4.h`` (``libnvfp4.so``, built from
+``csrc/*.hip``).  This module only marshals arguments: torch supplies device memory
+and the current HIP stream, and every step of the method runs in the library's
+kernels.  There is no CPU fallback; if the library is missing or no GPU is present the
+calls raise.
+
+Entry points (same names as the C ABI):
+  nvfp4_quantize     rowwise and/or columnwise NVFP4 copies of a bf16/fp32 matrix
+  nvfp4_dequantize   decode one copy to fp32 or bf16
+  nvfp4_gemm         W4A4 GEMM C = A B^T over two K-major copies, fp32 output
+  qadamw_v_encode    Q-AdamW second-moment encode (sqrt, bf16 tile mean, RHT, NVFP4)
+  qadamw_v_decode    its inverse
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+NVFP4_F32, NVFP4_BF16 = 0, 1
+NVFP4_RNE, NVFP4_SR = 0, 1
+NVFP4_BLOCK_1D, NVFP4_BLOCK_2D = 0, 1
+
+EXPORTED = ["nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantize",
+            "nvfp4_gemm", "qadamw_v_workspace_bytes", "qadamw_v_encode", "qadamw_v_decode",
+            "nvfp4_status_string", "nvfp4_abi_version"]
+
+
+class Nvfp4Error(RuntimeError):
+    pass
+
+
+class QuantParams(ctypes.Structure):
+    _fields_ = [("rowwise", ctypes.c_int32), ("colwise", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("round_row", ctypes.c_int32),
+                ("round_col", ctypes.c_int32), ("rht_row", ctypes.c_int32),
+                ("rht_col", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+class QTensorC(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("gscale", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libnvfp4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise Nvfp4Error(f"{p} is missing: build the HIP library first (__graft_entry__.build())")
+    lib = ctypes.CDLL(p)
+    vp, i64, i32, u64, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64,
+                             ctypes.c_size_t)
+    P = ctypes.POINTER
+    lib.nvfp4_quantize_workspace_bytes.restype = sz
+    lib.nvfp4_quantize_workspace_bytes.argtypes = [i64, i64, P(QuantParams)]
+    lib.nvfp4_quantize.restype = ctypes.c_int
+    lib.nvfp4_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, P(QuantParams),
+                                   P(QTensorC), P(QTensorC), vp, sz, vp]
+    lib.nvfp4_dequantize.restype = ctypes.c_int
+    lib.nvfp4_dequantize.argtypes = [P(QTensorC), i64, i64, ctypes.c_int, vp, i64, vp]
+    lib.nvfp4_gemm.restype = ctypes.c_int
+    lib.nvfp4_gemm.argtypes = [P(QTensorC), P(QTensorC), i64, i64, i64, vp, i64, vp]
+    lib.qadamw_v_workspace_bytes.restype = sz
+    lib.qadamw_v_workspace_bytes.argtypes = [i64, i64]
+    lib.qadamw_v_encode.restype = ctypes.c_int
+    lib.qadamw_v_encode.argtypes = [vp, i64, i64, u64, i32, vp, P(QTensorC), vp, sz, vp]
+    lib.qadamw_v_decode.restype = ctypes.c_int
+    lib.qadamw_v_decode.argtypes = [vp, P(QTensorC), i64, i64, u64, i32, vp, vp]
+    lib.nvfp4_status_string.restype = ctypes.c_char_p
+    lib.nvfp4_status_string.argtypes = [ctypes.c_int]
+    lib.nvfp4_abi_version.restype = ctypes.c_int
+    lib.nvfp4_abi_version.argtypes = []
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != 0:
+        msg = load_library().nvfp4_status_string(rc).decode()
+        raise Nvfp4Error(f"nvfp4 status {rc}: {msg}")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise Nvfp4Error("nvfp4 kernels take GPU tensors only (no CPU path)")
+
+
+@dataclass
+class QTensor:
+    """One quantized copy on the GPU: codes [n][k/2] u8, scales [n][k/16] u8, gscale [1] f32."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    gscale: torch.Tensor
+
+    @property
+    def shape(self):
+        return self.codes.shape[0], self.codes.shape[1] * 2
+
+    def c(self):
+        return QTensorC(self.codes.data_ptr(), self.scales.data_ptr(), self.gscale.data_ptr())
+
+    @staticmethod
+    def empty(n, k, device):
+        return QTensor(torch.empty((n, k // 2), dtype=torch.uint8, device=device),
+                       torch.empty((n, k // 16), dtype=torch.uint8, device=device),
+                       torch.empty((1,), dtype=torch.float32, device=device))
+
+
+def quant_params(rowwise=True, colwise=False, block2d=False, round_row=NVFP4_RNE,
+                 round_col=NVFP4_RNE, rht_row=False, rht_col=False, seed=0):
+    return QuantParams(int(rowwise), int(colwise), NVFP4_BLOCK_2D if block2d else NVFP4_BLOCK_1D,
+                       int(round_row), int(round_col), int(rht_row), int(rht_col),
+                       int(seed) & 0xFFFFFFFFFFFFFFFF)
+
+
+def nvfp4_quantize_workspace_bytes(rows, cols, params):
+    return int(load_library().nvfp4_quantize_workspace_bytes(rows, cols, ctypes.byref(params)))
+
+
+def nvfp4_quantize(x, params, row_out=None, col_out=None, workspace=None):
+    """Quantize a 2-D bf16/fp32 CUDA tensor (row stride may exceed its width).
+
+    Returns (row_copy, col_copy); a copy not requested is None.  Output buffers and the
+    workspace are allocated with torch unless passed in."""
+    lib = load_library()
+    _require_cuda(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise Nvfp4Error("x must be a 2-D tensor with unit column stride")
+    if x.dtype == torch.bfloat16:
+        dt = NVFP4_BF16
+    elif x.dtype == torch.float32:
+        dt = NVFP4_F32
+    else:
+        raise Nvfp4Error(f"unsupported dtype {x.dtype}")
+    R, C = x.shape
+    dev = x.device
+    if params.rowwise and row_out is None:
+        row_out = QTensor.empty(R, C, dev)
+    if params.colwise and col_out is None:
+        col_out = QTensor.empty(C, R, dev)
+    need = nvfp4_quantize_workspace_bytes(R, C, params)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    rc_ = row_out.c() if params.rowwise else None
+    cc_ = col_out.c() if params.colwise else None
+    rc = lib.nvfp4_quantize(_ptr(x), dt, R, C, x.stride(0), ctypes.byref(params),
+                            ctypes.byref(rc_) if rc_ is not None else None,
+                            ctypes.byref(cc_) if cc_ is not None else None,
+                            _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(rc)
+    return (row_out if params.rowwise else None), (col_out if params.colwise else None)
+
+
+def nvfp4_dequantize(q, out_dtype=torch.float32, out=None):
+    lib = load_library()
+    _require_cuda(q.codes)
+    n, k = q.shape
+    if out is None:
+        out = torch.empty((n, k), dtype=out_dtype, device=q.codes.device)
+    dt = NVFP4_BF16 if out.dtype == torch.bfloat16 else NVFP4_F32
+    qc = q.c()
+    _check(lib.nvfp4_dequantize(ctypes.byref(qc), n, k, dt, _ptr(out), out.stride(0),
+                                _stream(out.device)))
+    return out
+
+
+def nvfp4_gemm(a, b, out=None):
+    """C = A B^T (A: M x K copy, B: N x K copy), FP32."""
+    lib = load_library()
+    _require_cuda(a.codes, b.codes)
+    M, K = a.shape
+    N, K2 = b.shape
+    if K != K2:
+        raise Nvfp4Error(f"K mismatch {K} vs {K2}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.codes.device)
+    ac, bc = a.c(), b.c()
+    _check(lib.nvfp4_gemm(ctypes.byref(ac), ctypes.byref(bc), M, N, K, _ptr(out), out.stride(0),
+                          _stream(out.device)))
+    return out
+
+
+def qadamw_v_workspace_bytes(rows, cols):
+    return int(load_library().qadamw_v_workspace_bytes(rows, cols))
+
+
+def qadamw_v_encode(v, seed=0, use_signs=True, mu=None, q=None, workspace=None):
+    lib = load_library()
+    _require_cuda(v)
+    if v.dtype != torch.float32 or v.dim() != 2 or not v.is_contiguous():
+        raise Nvfp4Error("v must be a contiguous 2-D float32 tensor")
+    R, C = v.shape
+    dev = v.device
+    if mu is None:
+        mu = torch.empty((R // 16, C // 16), dtype=torch.int16, device=dev)
+    if q is None:
+        q = QTensor.empty(R, C, dev)
+    need = qadamw_v_workspace_bytes(R, C)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    qc = q.c()
+    _check(lib.qadamw_v_encode(_ptr(v), R, C, int(seed) & 0xFFFFFFFFFFFFFFFF, int(use_signs),
+                               _ptr(mu), ctypes.byref(qc), _ptr(workspace), workspace.numel(),
+                               _stream(dev)))
+    return mu, q
+
+
+def qadamw_v_decode(mu, q, seed=0, use_signs=True, out=None):
+    lib = load_library()
+    _require_cuda(mu, q.codes)
+    R, C = q.shape
+    if out is None:
+        out = torch.empty((R, C), dtype=torch.float32, device=q.codes.device)
+    qc = q.c()
+    _check(lib.qadamw_v_decode(_ptr(mu), ctypes.byref(qc), R, C, int(seed) & 0xFFFFFFFFFFFFFFFF,
+                               int(use_signs), _ptr(out), _stream(out.device)))
+    return out
+
+
+def abi_version():
+    return load_library().nvfp4_abi_version()

@@ -1,0 +1,251 @@
+// qadamw.hip -- quantized-state AdamW second moment (encode / decode) for gfx950.
+//
+// Method: Full-Stack FP4 sec. 3.3 -- (1) y = sqrt(v), (2) subtract the tile-wise mean,
+// (3) fast Hadamard transform of the residual, (4) NVFP4 quantization; reconstruction
+// v ~ ((s_g s v_hat) H16 + mu)^2.  The gist.science summary (sec. 2.2) stores the tile
+// mean in BF16.  Tiles are 16x16, NVFP4 blocks 1x16 along rows, the residual is taken
+// against the stored BF16 mean, and the Hadamard is the random one (signs from the seed)
+// or the plain normalised H16.
+//
+// Work decomposition: one lane owns one row of one 16x16 tile, i.e. exactly one 1x16
+// NVFP4 block (64 bytes of v: four 16-byte loads).  The 16 lanes of a tile are lanes
+// 16k .. 16k+15 of a wave, so the tile sum is an in-register pairwise tree over the
+// row followed by xor-shuffles 1, 2, 4, 8 over the 16 row sums -- the same adjacent-
+// pair tree in the same order.  A workgroup (4 waves) covers 16 rows x 256 columns.
+// Encoding needs the amax of the whole transformed residual first, so it is two
+// kernels like the quantizer (per-workgroup partial maxima, reduced in every
+// workgroup of the second pass).
+#include "nvfp4.h"
+#include "device_common.h"
+
+namespace nvfp4 {
+
+constexpr int QVThreads = 256;
+constexpr int QVCols = 256;  // columns per workgroup (16 tiles)
+
+struct QVArgs {
+    const float* v;
+    int64_t rows, cols;
+    uint32_t k0, k1;
+    int use_signs;
+    uint16_t* mu;
+    uint8_t* codes;
+    uint8_t* scales;
+    float* sg;
+    float* partial;
+    int tiles_c;   // workgroups along columns
+    int nblocks;   // workgroups
+};
+
+__device__ __forceinline__ float tree16_row(const float y[16]) {
+    float t[8], u[4], w[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = y[2 * i] + y[2 * i + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = t[2 * i] + t[2 * i + 1];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) w[i] = u[2 * i] + u[2 * i + 1];
+    return w[0] + w[1];
+}
+
+// Square roots of one 1x16 row segment, the tile mean (bf16 bits), and the transformed
+// residual.  All 64 lanes must call it (cross-lane shuffles).
+__device__ __forceinline__ uint32_t residual_block(const QVArgs& a, int64_t r, int64_t c,
+                                                   bool valid, uint32_t signs, float e[16]) {
+    float y[16];
+    if (valid) {
+        const float4* p = (const float4*)(a.v + r * a.cols + c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float4 f = p[q];
+            y[4 * q] = f.x; y[4 * q + 1] = f.y; y[4 * q + 2] = f.z; y[4 * q + 3] = f.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] = 0.0f;
+    }
+    // sqrtf lowers to the correctly rounded square root on gfx950 (checked against IEEE
+    // sqrt on 4M log-normal and subnormal inputs); __fsqrt_rn is not, so it is avoided.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = sqrtf(y[i]);
+    float s = tree16_row(y);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) s = s + __shfl_xor(s, o, 64);
+    const uint32_t mu = f32_to_bf16_rne(s * 0.00390625f);
+    const float muf = bf16_to_f32(mu);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) e[i] = y[i] - muf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) e[i] = apply_sign(e[i], signs, i);
+    wht16(e);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) e[i] = e[i] * 0.25f;
+    return mu;
+}
+
+__device__ __forceinline__ void qv_coords(const QVArgs& a, int64_t& r, int64_t& c, bool& valid) {
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int br = blockIdx.x / a.tiles_c, bc = blockIdx.x % a.tiles_c;
+    r = (int64_t)br * 16 + (lane & 15);
+    c = (int64_t)bc * QVCols + (wid * 4 + (lane >> 4)) * 16;
+    valid = r < a.rows && c < a.cols;
+}
+
+__device__ __forceinline__ float block_max1(float a, float* red) {
+    a = wave_max(a);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__global__ __launch_bounds__(QVThreads) void k_qv_pass1(QVArgs a) {
+    __shared__ float red[4];
+    int64_t r, c;
+    bool valid;
+    qv_coords(a, r, c, valid);
+    const uint32_t signs = a.use_signs ? rht_sign_bits(a.k0, a.k1) : 0u;
+    float e[16];
+    const uint32_t mu = residual_block(a, r, c, valid, signs, e);
+    float am = 0.0f;
+    if (valid) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(e[i]));
+        if ((threadIdx.x & 15) == 0) a.mu[(r / 16) * (a.cols / 16) + c / 16] = (uint16_t)mu;
+    }
+    am = block_max1(am, red);
+    if (threadIdx.x == 0) a.partial[blockIdx.x] = am;
+}
+
+__global__ __launch_bounds__(QVThreads) void k_qv_pass2(QVArgs a) {
+    __shared__ float red[4];
+    float am = 0.0f;
+    for (int i = threadIdx.x; i < a.nblocks; i += QVThreads) am = fmaxf(am, a.partial[i]);
+    am = block_max1(am, red);
+    float sg = __fdiv_rn(am, 2688.0f);
+    if (sg == 0.0f) sg = 1.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.sg = sg;
+
+    int64_t r, c;
+    bool valid;
+    qv_coords(a, r, c, valid);
+    const uint32_t signs = a.use_signs ? rht_sign_bits(a.k0, a.k1) : 0u;
+    float e[16];
+    residual_block(a, r, c, valid, signs, e);
+    float bm = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(e[i]));
+    const uint32_t scode = e4m3_encode(__fdiv_rn(__fdiv_rn(bm, 6.0f), sg));
+    const float d = e4m3_value(scode) * sg;
+    const float rcp = scode ? __fdiv_rn(1.0f, d) : 0.0f;
+    uint32_t lo = 0, hi = 0;
+    lo = cvt_fp4x2<0>(lo, e[0] * rcp, e[1] * rcp);
+    lo = cvt_fp4x2<1>(lo, e[2] * rcp, e[3] * rcp);
+    lo = cvt_fp4x2<2>(lo, e[4] * rcp, e[5] * rcp);
+    lo = cvt_fp4x2<3>(lo, e[6] * rcp, e[7] * rcp);
+    hi = cvt_fp4x2<0>(hi, e[8] * rcp, e[9] * rcp);
+    hi = cvt_fp4x2<1>(hi, e[10] * rcp, e[11] * rcp);
+    hi = cvt_fp4x2<2>(hi, e[12] * rcp, e[13] * rcp);
+    hi = cvt_fp4x2<3>(hi, e[14] * rcp, e[15] * rcp);
+    if (valid) {
+        *(uint2*)(a.codes + r * (a.cols / 2) + c / 2) = make_uint2(lo, hi);
+        a.scales[r * (a.cols / 16) + c / 16] = (uint8_t)scode;
+    }
+}
+
+__global__ __launch_bounds__(QVThreads) void k_qv_decode(const uint16_t* mu, const uint8_t* codes,
+                                                         const uint8_t* scales, const float* gs,
+                                                         int64_t rows, int64_t cols, uint32_t k0,
+                                                         uint32_t k1, int use_signs, float* out) {
+    const int64_t kb = cols / 16;
+    const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (blk >= rows * kb) return;
+    const int64_t r = blk / kb, b = blk % kb;
+    const uint2 cw = *(const uint2*)(codes + r * (cols / 2) + b * 8);
+    const float s = e4m3_value(scales[r * kb + b]);
+    const float sg = *gs;
+    const float muf = bf16_to_f32(mu[(r / 16) * kb + b]);
+    const uint32_t signs = use_signs ? rht_sign_bits(k0, k1) : 0u;
+    float w[16];
+    uint32_t w2[2] = {cw.x, cw.y};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float2v p0 = fp4x2_to_f32<0>(w2[h]);
+        float2v p1 = fp4x2_to_f32<1>(w2[h]);
+        float2v p2 = fp4x2_to_f32<2>(w2[h]);
+        float2v p3 = fp4x2_to_f32<3>(w2[h]);
+        w[8 * h + 0] = p0.x; w[8 * h + 1] = p0.y; w[8 * h + 2] = p1.x; w[8 * h + 3] = p1.y;
+        w[8 * h + 4] = p2.x; w[8 * h + 5] = p2.y; w[8 * h + 6] = p3.x; w[8 * h + 7] = p3.y;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = (w[i] * s) * sg;
+    wht16(w);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = apply_sign(w[i] * 0.25f, signs, i);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float z = w[i] + muf;
+        w[i] = z * z;
+    }
+    float4* p = (float4*)(out + r * cols + b * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p[q] = make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+static int64_t qv_blocks(int64_t rows, int64_t cols, int* tiles_c) {
+    const int64_t tc = (cols + QVCols - 1) / QVCols;
+    if (tiles_c) *tiles_c = (int)tc;
+    return (rows / 16) * tc;
+}
+
+extern "C" size_t qadamw_v_workspace_bytes(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return (size_t)qv_blocks(rows, cols, nullptr) * sizeof(float);
+}
+
+extern "C" int qadamw_v_encode(const float* v, int64_t rows, int64_t cols, uint64_t seed,
+                               int32_t use_signs, uint16_t* mu, const nvfp4_qtensor* q, void* ws,
+                               size_t ws_bytes, void* stream) {
+    if (!q) return NVFP4_ERR_NULL;
+    if (rows < 0 || cols < 0 || rows % 16 || cols % 16) return NVFP4_ERR_SHAPE;
+    hipStream_t st = (hipStream_t)stream;
+    if (rows == 0 || cols == 0) return NVFP4_OK;
+    if (!q->codes || !q->scales || !q->gscale) return NVFP4_ERR_NULL;
+    if (!v || !mu) return NVFP4_ERR_NULL;
+    if (((uintptr_t)v & 15) || ((uintptr_t)q->codes & 7) || ((uintptr_t)mu & 1) ||
+        ((uintptr_t)q->gscale & 3))
+        return NVFP4_ERR_ALIGN;
+    const size_t need = qadamw_v_workspace_bytes(rows, cols);
+    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if ((uintptr_t)ws & 15) return NVFP4_ERR_ALIGN;
+    QVArgs a;
+    a.v = v; a.rows = rows; a.cols = cols;
+    a.k0 = (uint32_t)seed; a.k1 = (uint32_t)(seed >> 32);
+    a.use_signs = use_signs != 0;
+    a.mu = mu; a.codes = q->codes; a.scales = q->scales; a.sg = q->gscale;
+    a.partial = (float*)ws;
+    a.nblocks = (int)qv_blocks(rows, cols, &a.tiles_c);
+    k_qv_pass1<<<a.nblocks, QVThreads, 0, st>>>(a);
+    k_qv_pass2<<<a.nblocks, QVThreads, 0, st>>>(a);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+extern "C" int qadamw_v_decode(const uint16_t* mu, const nvfp4_qtensor* q, int64_t rows,
+                               int64_t cols, uint64_t seed, int32_t use_signs, float* v_out,
+                               void* stream) {
+    if (!q) return NVFP4_ERR_NULL;
+    if (rows < 0 || cols < 0 || rows % 16 || cols % 16) return NVFP4_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return NVFP4_OK;
+    if (!q->codes || !q->scales || !q->gscale || !mu || !v_out) return NVFP4_ERR_NULL;
+    if (((uintptr_t)v_out & 15) || ((uintptr_t)q->codes & 7) || ((uintptr_t)mu & 1))
+        return NVFP4_ERR_ALIGN;
+    const int64_t blocks = rows * (cols / 16);
+    k_qv_decode<<<(unsigned)((blocks + 255) / 256), 256, 0, (hipStream_t)stream>>>(
+        mu, q->codes, q->scales, q->gscale, rows, cols, (uint32_t)seed, (uint32_t)(seed >> 32),
+        use_signs != 0, v_out);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}

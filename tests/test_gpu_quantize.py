@@ -1,0 +1,167 @@
+"""GPU parity of nvfp4_quantize / nvfp4_dequantize against the CPU oracle.
+
+Bar: bit-exact codes, scales and tensor scales for every copy, every option combination
+(1D/2D, RNE/SR, Hadamard per copy), both input dtypes, shapes that span several 256x128
+workgroup tiles with ragged tails, and the full-size activation, weight and gradient
+tensors of the 3B workloads.  Inputs are seeded and synthetic; expected values come from
+the oracle only.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import assert_copy_equal, dev, to_gpu_qtensor
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import nvfp4_block_scaled_quantize_amd as nv
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    nv.load_library()
+    return nv
+
+
+def make_input(shape, seed, dtype):
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    x = synthetic.spiky(shape, seed)
+    g = torch.Generator().manual_seed(seed + 7)
+    # rows of tiny values, an all-zero 16x16 tile, signed zeros
+    if shape[0] >= 32:
+        x[16:32] *= 1e-5
+    if shape[0] >= 16 and shape[1] >= 32:
+        x[:16, 16:32] = 0.0
+        x[0, 16] = -0.0
+    x[torch.rand(shape, generator=g) < 0.01] = -0.0
+    return x.to(dtype)
+
+
+MODES = {
+    "row": dict(rowwise=True),
+    "col": dict(rowwise=False, colwise=True),
+    "rowcol": dict(rowwise=True, colwise=True),
+    "2d": dict(rowwise=True, colwise=True, block2d=True),
+    "2d_col": dict(rowwise=False, colwise=True, block2d=True),
+    "sr": dict(rowwise=True, colwise=True, round_row=1, round_col=1),
+    "wgrad_dy": dict(rowwise=False, colwise=True, round_col=1, rht_col=True),
+    "wgrad_x": dict(rowwise=False, colwise=True, rht_col=True),
+    "rht_row": dict(rowwise=True, rht_row=True),
+    "dgrad_and_wgrad": dict(rowwise=True, colwise=True, round_row=1, round_col=1, rht_col=True),
+    "all": dict(rowwise=True, colwise=True, round_row=1, round_col=1, rht_row=True, rht_col=True),
+}
+SHAPES = [(16, 16), (48, 80), (128, 256), (272, 400), (528, 144)]
+
+
+def run_case(nv, oracle, x, mode, seed):
+    kw = MODES[mode]
+    p = nv.quant_params(seed=seed, **kw)
+    print(f"quantize case {tuple(x.shape)} {x.dtype} {mode} seed={seed:#x}", flush=True)
+    gr, gc = nv.nvfp4_quantize(x.to(dev()), p)
+    torch.cuda.synchronize()
+    orow, ocol = oracle.quantize(x.float().numpy(), rowwise=kw.get("rowwise", True),
+                                 colwise=kw.get("colwise", False),
+                                 block2d=kw.get("block2d", False),
+                                 round_row=kw.get("round_row", 0), round_col=kw.get("round_col", 0),
+                                 rht_row=kw.get("rht_row", False), rht_col=kw.get("rht_col", False),
+                                 seed=seed)
+    if orow is not None:
+        assert_copy_equal(gr, orow, f"{mode} rowwise")
+    if ocol is not None:
+        assert_copy_equal(gc, ocol, f"{mode} colwise")
+    return gr, gc, orow, ocol
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("mode", list(MODES))
+def test_quantize_matches_oracle(nv, oracle, dtype, shape, mode):
+    seed = 0x1234 + shape[0] * 7 + shape[1]
+    x = make_input(shape, seed, dtype)
+    run_case(nv, oracle, x, mode, 0x5EED0000 + seed)
+
+
+def test_rne_ties_and_neighbours(nv, oracle):
+    # s_g = 1 (one block holds 6*448) and block amax 6 give s = 1, so the scaled values
+    # are the inputs themselves: every E2M1 tie, its float32 neighbours and their negatives.
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 2.0, 3.0, 4.0, 6.0]
+    vals = []
+    for t in ties:
+        a = np.float32(t)
+        vals += [a, np.nextafter(a, np.float32(0)), np.nextafter(a, np.float32(9))]
+    vals = np.array(vals + [-v for v in vals], dtype=np.float32)
+    nblk = (len(vals) + 14) // 15
+    x = np.zeros((16, 16 * (nblk + 1)), dtype=np.float32)
+    for b in range(nblk):
+        chunk = vals[15 * b:15 * b + 15]
+        x[:, 16 * b] = 6.0
+        x[:, 16 * b + 1:16 * b + 1 + len(chunk)] = chunk
+    x[0, -16] = 2688.0
+    xt = torch.from_numpy(x)
+    for mode in ["rowcol", "sr"]:
+        run_case(nv, oracle, xt, mode, 99)
+
+
+def test_leading_dimension_and_determinism(nv, oracle):
+    x = make_input((96, 160), 5, torch.bfloat16)
+    big = torch.zeros((96, 256), dtype=torch.bfloat16)
+    big[:, :160] = x
+    xb = big.to(dev())[:, :160]
+    p = nv.quant_params(rowwise=True, colwise=True, round_col=1, rht_col=True, seed=3)
+    r1, c1 = nv.nvfp4_quantize(xb, p)
+    r2, c2 = nv.nvfp4_quantize(x.to(dev()), p)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        r3, c3 = nv.nvfp4_quantize(xb, p)
+    torch.cuda.synchronize()
+    for a, b in [(r1, r2), (c1, c2), (r1, r3), (c1, c3)]:
+        assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+        assert torch.equal(a.gscale, b.gscale)
+    orow, ocol = oracle.quantize(x.float().numpy(), colwise=True, round_col=1, rht_col=True, seed=3)
+    assert_copy_equal(r1, orow, "ld rowwise")
+    assert_copy_equal(c1, ocol, "ld colwise")
+
+
+def test_empty_and_zero_tensors(nv, oracle):
+    p = nv.quant_params(rowwise=True, colwise=True)
+    e = torch.zeros((0, 32), dtype=torch.bfloat16, device=dev())
+    r, c = nv.nvfp4_quantize(e, p)
+    torch.cuda.synchronize()
+    assert r.gscale.item() == 1.0 and c.gscale.item() == 1.0
+    z = torch.zeros((32, 48), dtype=torch.float32)
+    run_case(nv, oracle, z, "rowcol", 1)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_dequantize_matches_oracle(nv, oracle, out_dtype):
+    x = make_input((272, 400), 11, torch.float32).numpy()
+    orow, _ = oracle.quantize(x, round_row=1, seed=4)
+    gq = to_gpu_qtensor(nv, orow)
+    out = nv.nvfp4_dequantize(gq, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref = torch.from_numpy(oracle.dequantize(orow))
+    if out_dtype == torch.bfloat16:
+        ref = ref.to(torch.bfloat16)          # torch's nearest-even rounding
+    assert torch.equal(out.cpu().view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32),
+                       ref.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32))
+
+
+# ------------------------------------------------------------------ full-size tensors
+def test_full_size_activation_rowcol(nv, oracle):
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    x = synthetic.ffn()["X"]                    # 8192 x 3072 bf16, outlier channels
+    run_case(nv, oracle, x, "rowcol", 0)
+
+
+def test_full_size_weight_2d(nv, oracle):
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    w = synthetic.normal((9216, 3072), synthetic.DATA_SEEDS["ffn"] + 1000, 0.02).to(torch.bfloat16)
+    run_case(nv, oracle, w, "2d", 0)
+
+
+def test_full_size_wgrad_operands(nv, oracle):
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    t = synthetic.wgrad()
+    run_case(nv, oracle, t["dY"], "wgrad_dy", synthetic.RHT_SEED_WGRAD)
+    run_case(nv, oracle, t["X"], "wgrad_x", synthetic.RHT_SEED_WGRAD)
