@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 quantized-linear hot path on one MI355X.
+
+A step is one pass of the whole path over the 3B model's FFN at 8192 tokens (hidden 3072,
+FFN 9216), the workload the headline metric is quoted on:
+  forward   Q(X) rowwise RNE + columnwise RHT16 copy, Q(W_up) 16x16 2D (both copies),
+            GEMM Y_up = X W_up^T (8192x9216x3072), Q(H) rowwise, Q(W_down) 2D,
+            GEMM Y_down = H W_down^T (8192x3072x9216)
+  backward  Q(dY) rowwise SR + columnwise RHT16 SR, dgrad GEMM dX = dY W_up
+            (8192x3072x9216), wgrad GEMM dW = dY^T X on the rotated copies (9216x3072x8192)
+  optimizer Q-AdamW second moment v (9216x3072) encode + decode
+  decode    dequantize of the W_up rowwise copy to FP32
+All inputs are seeded synthetic tensors resident in HBM before timing starts.
+
+Output: one JSON line.  value = total GEMM FLOPs of a step / step time (TFLOP/s, all
+quantization, optimizer-state and decode kernels included).  Per-kernel times come from
+HIP events recorded on the stream the kernels are launched on.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 quantize GB/s + W4A4 GEMM TFLOP/s at 8192×3072×9216 (% of roofline)"
+PEAK_HBM_GBPS = 8000.0
+PEAK_F16_TFLOPS = 2500.0   # dense f16/bf16 MFMA, MI355X
+TOKENS, HIDDEN, FFN = 8192, 3072, 9216
+SEED_WGRAD, SEED_QADAMW = 0x5EED4, 0x5EED5
+
+
+def qbytes(n, k):
+    """Bytes of one NVFP4 copy of an n x k matrix: codes, E4M3 scales, tensor scale."""
+    return n * k // 2 + n * k // 16 + 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=4096,
+                    help="rows of X for the oracle's bounded CPU sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def counters_for(kernel_file, key):
+    """HBM traffic per launch from a committed rocprofv3 counter summary, or None if the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    src = os.path.join(ROOT, "nvfp4_block_scaled_quantize_amd", "csrc", kernel_file)
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for line in open(path):
+        t = line.split()
+        if len(t) >= 4 and not line.startswith("#") and t[0] == key and t[1] == digest:
+            return float(t[2]) + float(t[3])
+    return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU path is a design note, not part of this build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import nvfp4_block_scaled_quantize_amd as nv
+    from nvfp4_block_scaled_quantize_amd import synthetic
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    nv.load_library()
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 256 << 20, "launches": 5}))
+        return
+
+    # ------------------------------------------------------------ inputs (seeded, in HBM)
+    ffn = synthetic.ffn()
+    wg = synthetic.wgrad()
+    X = ffn["X"].to(dev)
+    W_up = ffn["W_up"].to(dev)
+    W_down = ffn["W_down"].to(dev)
+    H = ffn["H"].to(dev)
+    dY = wg["dY"].to(dev)
+    v = synthetic.qadamw()["v"].to(dev)
+
+    P = nv.quant_params
+    p_x = P(rowwise=True, colwise=True, rht_col=True, seed=SEED_WGRAD)
+    p_w = P(rowwise=True, colwise=True, block2d=True)
+    p_h = P(rowwise=True)
+    p_wd = P(rowwise=True, block2d=True)
+    p_dy = P(rowwise=True, colwise=True, round_row=nv.NVFP4_SR, round_col=nv.NVFP4_SR,
+             rht_col=True, seed=SEED_WGRAD)
+
+    def alloc(R, C, params):
+        row = nv.QTensor.empty(R, C, dev) if params.rowwise else None
+        col = nv.QTensor.empty(C, R, dev) if params.colwise else None
+        ws = torch.empty(max(nv.nvfp4_quantize_workspace_bytes(R, C, params), 16),
+                         dtype=torch.uint8, device=dev)
+        return row, col, ws
+
+    qx = alloc(TOKENS, HIDDEN, p_x)
+    qw = alloc(FFN, HIDDEN, p_w)
+    qh = alloc(TOKENS, FFN, p_h)
+    qwd = alloc(HIDDEN, FFN, p_wd)
+    qdy = alloc(TOKENS, FFN, p_dy)
+    Y_up = torch.empty((TOKENS, FFN), dtype=torch.float32, device=dev)
+    Y_down = torch.empty((TOKENS, HIDDEN), dtype=torch.float32, device=dev)
+    dX = torch.empty((TOKENS, HIDDEN), dtype=torch.float32, device=dev)
+    dW = torch.empty((FFN, HIDDEN), dtype=torch.float32, device=dev)
+    mu = torch.empty((FFN // 16, HIDDEN // 16), dtype=torch.int16, device=dev)
+    qv = nv.QTensor.empty(FFN, HIDDEN, dev)
+    ws_v = torch.empty(max(nv.qadamw_v_workspace_bytes(FFN, HIDDEN), 16), dtype=torch.uint8,
+                       device=dev)
+    v_out = torch.empty_like(v)
+    w_dec = torch.empty((FFN, HIDDEN), dtype=torch.float32, device=dev)
+
+    # name -> (kind, algorithmic bytes, flops)
+    work = {
+        "quant_X_row+colRHT": ("quant", 2 * TOKENS * HIDDEN + 2 * qbytes(TOKENS, HIDDEN), 0),
+        "quant_Wup_2d": ("quant", 2 * FFN * HIDDEN + 2 * qbytes(FFN, HIDDEN), 0),
+        "gemm_ffn_up": ("gemm", qbytes(TOKENS, HIDDEN) + qbytes(FFN, HIDDEN) + 4 * TOKENS * FFN,
+                        2 * TOKENS * FFN * HIDDEN),
+        "quant_H_row": ("quant", 2 * TOKENS * FFN + qbytes(TOKENS, FFN), 0),
+        "quant_Wdown_2d": ("quant", 2 * HIDDEN * FFN + qbytes(HIDDEN, FFN), 0),
+        "gemm_ffn_down": ("gemm", qbytes(TOKENS, FFN) + qbytes(HIDDEN, FFN) + 4 * TOKENS * HIDDEN,
+                          2 * TOKENS * HIDDEN * FFN),
+        "quant_dY_rowSR+colRHTSR": ("quant", 2 * TOKENS * FFN + 2 * qbytes(TOKENS, FFN), 0),
+        "gemm_dgrad": ("gemm", qbytes(TOKENS, FFN) + qbytes(HIDDEN, FFN) + 4 * TOKENS * HIDDEN,
+                       2 * TOKENS * HIDDEN * FFN),
+        "gemm_wgrad": ("gemm", qbytes(FFN, TOKENS) + qbytes(HIDDEN, TOKENS) + 4 * FFN * HIDDEN,
+                       2 * FFN * HIDDEN * TOKENS),
+        "qadamw_encode": ("quant", 4 * FFN * HIDDEN + qbytes(FFN, HIDDEN) + FFN * HIDDEN // 128, 0),
+        "qadamw_decode": ("quant", qbytes(FFN, HIDDEN) + FFN * HIDDEN // 128 + 4 * FFN * HIDDEN, 0),
+        "dequant_Wup": ("quant", qbytes(FFN, HIDDEN) + 4 * FFN * HIDDEN, 0),
+    }
+
+    def calls():
+        yield "quant_X_row+colRHT", lambda: nv.nvfp4_quantize(X, p_x, qx[0], qx[1], qx[2])
+        yield "quant_Wup_2d", lambda: nv.nvfp4_quantize(W_up, p_w, qw[0], qw[1], qw[2])
+        yield "gemm_ffn_up", lambda: nv.nvfp4_gemm(qx[0], qw[0], out=Y_up)
+        yield "quant_H_row", lambda: nv.nvfp4_quantize(H, p_h, qh[0], None, qh[2])
+        yield "quant_Wdown_2d", lambda: nv.nvfp4_quantize(W_down, p_wd, qwd[0], None, qwd[2])
+        yield "gemm_ffn_down", lambda: nv.nvfp4_gemm(qh[0], qwd[0], out=Y_down)
+        yield "quant_dY_rowSR+colRHTSR", lambda: nv.nvfp4_quantize(dY, p_dy, qdy[0], qdy[1], qdy[2])
+        yield "gemm_dgrad", lambda: nv.nvfp4_gemm(qdy[0], qw[1], out=dX)
+        yield "gemm_wgrad", lambda: nv.nvfp4_gemm(qdy[1], qx[1], out=dW)
+        yield "qadamw_encode", lambda: nv.qadamw_v_encode(v, SEED_QADAMW, True, mu, qv, ws_v)
+        yield "qadamw_decode", lambda: nv.qadamw_v_decode(mu, qv, SEED_QADAMW, True, out=v_out)
+        yield "dequant_Wup", lambda: nv.nvfp4_dequantize(qw[0], out=w_dec)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(record):
+        for name, fn in calls():
+            if record is None:
+                fn()
+            else:
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record(stream)
+                fn()
+                e.record(stream)
+                record.append((name, s, e))
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    per = {}
+    for name, s, e in events:
+        per.setdefault(name, []).append(s.elapsed_time(e))
+    kernels = {}
+    for name, (kind, nbytes, flops) in work.items():
+        ms = sum(per[name]) / len(per[name])
+        d = {"ms": round(ms, 5)}
+        if kind == "gemm":
+            d["TFLOP/s"] = round(flops / ms / 1e9, 1)
+            d["frac_f16_peak"] = round(flops / ms / 1e9 / PEAK_F16_TFLOPS, 4)
+        d["GB/s"] = round(nbytes / ms / 1e6, 1)
+        if kind == "quant":
+            d["frac_hbm_peak"] = round(nbytes / ms / 1e6 / PEAK_HBM_GBPS, 4)
+        kernels[name] = d
+
+    gemm_flops = sum(f for k, b, f in work.values())
+    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+    q_names = [n for n, (k, b, f) in work.items() if k == "quant"]
+    q_bytes = sum(work[n][1] for n in q_names)
+    q_ms = sum(kernels[n]["ms"] for n in q_names)
+    up = kernels["gemm_ffn_up"]
+    up_flops = work["gemm_ffn_up"][2]
+    roofline = {"bound": "mfma", "kernel": "k_gemm (FFN-up 8192x9216x3072)",
+                "achieved": up["TFLOP/s"], "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(up["TFLOP/s"] / PEAK_F16_TFLOPS, 4),
+                "traffic": counters_for("gemm.hip", "gemm_ffn_up")}
+    xq = kernels["quant_X_row+colRHT"]
+    roofline_quant = {"bound": "hbm", "kernel": "k_amax+k_encode (X 8192x3072 bf16, row + col RHT)",
+                      "achieved": xq["GB/s"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                      "frac": round(xq["GB/s"] / PEAK_HBM_GBPS, 4),
+                      "traffic": counters_for("quantize.hip", "quant_X_row+colRHT")}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "3B FFN linear hot path: 8192 tokens, hidden 3072, FFN 9216; "
+                               "fwd up+down, bwd up (dgrad, wgrad with RHT16+SR), "
+                               "Q-AdamW v 9216x3072 encode+decode, W_up dequantize",
+                   "tokens": TOKENS, "hidden": HIDDEN, "ffn": FFN,
+                   "gemm_shapes_MxNxK": ["8192x9216x3072", "8192x3072x9216", "8192x3072x9216",
+                                         "9216x3072x8192"],
+                   "parallelism": "single GPU"},
+        "headline": {"gemm_ffn_up_TFLOP/s": up["TFLOP/s"],
+                     "quantize_X_GB/s": xq["GB/s"],
+                     "quantize_all_GB/s": round(q_bytes / q_ms / 1e6, 1)},
+        "roofline": roofline,
+        "roofline_quantize": roofline_quant,
+        "kernels": kernels,
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, synthetic, ffn)
+    print(json.dumps(out))
+
+
+def cpu_baseline(args, synthetic, ffn):
+    """The oracle, as it stands, on a bounded sample of the same workload: quantize the
+    first rows of X and all of W_up, then the binary64 GEMM of those rows against W_up."""
+    import numpy as np
+    import oracle
+    rows = args.cpu_sample_rows
+    x = ffn["X"][:rows].float().numpy()
+    w = ffn["W_up"].float().numpy()
+    t0 = time.perf_counter()
+    qa, _ = oracle.quantize(x)
+    qb, _ = oracle.quantize(w, block2d=True)
+    t1 = time.perf_counter()
+    oracle.gemm_f64(qa, qb)
+    t2 = time.perf_counter()
+    flops = 2.0 * rows * FFN * HIDDEN
+    qbytes_ = 2 * (rows + FFN) * HIDDEN + qbytes(rows, HIDDEN) + qbytes(FFN, HIDDEN)
+    return {"value": round(flops / (t2 - t0) / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"FFN-up: quantize X[:{rows}] (1x16) and W_up 9216x3072 (16x16), then the "
+                      f"binary64 GEMM {rows}x9216x3072; TFLOP/s counts the GEMM flops over the "
+                      f"quantize+GEMM time",
+            "quantize_GB/s": round(qbytes_ / (t1 - t0) / 1e9, 3),
+            "gemm_TFLOP/s": round(flops / (t2 - t1) / 1e12, 6),
+            "seconds": round(t2 - t0, 2)}
+
+
+if __name__ == "__main__":
+    main()
