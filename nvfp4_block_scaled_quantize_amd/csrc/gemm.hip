@@ -14,12 +14,25 @@
 // Work decomposition.  One workgroup (4 waves) computes a 256x256 tile of C; wave
 // (wm, wn) owns a 128x128 sub-tile as 4x4 MFMA 32x32x16 accumulators.  Packed codes and
 // scale bytes (not decoded values) are staged through LDS, 128 K-elements (64 bytes per
-// row) per stage, double buffered: on gfx950 LDS writes run at about a third of the
-// read rate, so staging 4-bit codes instead of 16-bit values keeps LDS off the critical
-// path.  Each wave decodes its own MFMA operands right before use: the hardware
-// fp4 -> f16 conversion (exact; it issues at a quarter of the VALU rate) and a packed f16
-// multiply by the block scale.  Conversions and multiplies are interleaved between the
-// MFMAs of the previous slot so that the VALU work runs under the matrix cores.
+// row) per stage: on gfx950 LDS writes run at about a third of the read rate, so
+// staging 4-bit codes instead of 16-bit values keeps LDS off the critical path.  Each
+// wave decodes its own MFMA operands right before use: the hardware fp4 -> f16
+// conversion (exact; it issues at a quarter of the VALU rate) asked for v * 256 through
+// its power-of-two scale operand, and one packed f16 multiply by s / 256, which is the
+// E4M3 scale byte shifted into the binary16 fields.  Conversions and multiplies are
+// interleaved between the MFMAs of the previous slot so that the VALU work runs under
+// the matrix cores.
+//
+// Staging.  Two paths fill the LDS tiles.
+//  * Direct (K % 64 == 0, scale rows 4-byte aligned, each operand under 2 GiB): buffer
+//    loads with the LDS flag write global bytes straight into LDS, lane l of a load to
+//    LDS address base + 16 l (or 4 l), so neither VGPRs nor LDS store instructions are
+//    spent, and three stages are in flight.  A lane whose 16-byte chunk lies outside the
+//    operand (row past M or N, k past K) gets an offset past the end of its buffer, and
+//    the buffer range check turns its load into zeros.  The choice of which global
+//    chunk each lane fetches lays the tile out in the swizzled order below.
+//  * Generic (any K % 32 == 0): each thread loads its chunks into registers with bounds
+//    checks and stores them to LDS; two stages.
 //
 // K ordering.  An MFMA sums over 16 k-slots; lanes 0-31 supply slots 0-7 and lanes
 // 32-63 slots 8-15.  Lane (i, h) of both operands reads the 64 contiguous k of half h
@@ -35,7 +48,12 @@ constexpr int GThreads = 256;
 constexpr int kStageCodeBytes = GBM * 64;       // per operand
 constexpr int kStageScaleBytes = GBM * 8;       // per operand
 constexpr int kStageBytes = 2 * kStageCodeBytes + 2 * kStageScaleBytes;
-constexpr int kGemmLds = 2 * kStageBytes;
+constexpr int kRegStages = 2, kDmaStages = 3;
+constexpr int kGemmLds = kRegStages * kStageBytes;
+constexpr int kGemmDmaLds = kDmaStages * kStageBytes;
+// direct loads per wave and stage: 4 + 4 code chunks, 2 + 2 scale words
+constexpr int kDmaLoadsPerStage = 12;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // past the end of every direct-path buffer
 
 struct GArgs {
     const uint8_t* ac;
@@ -49,6 +67,151 @@ struct GArgs {
     int64_t ldc;
     int tiles_n;
 };
+
+// Packed tile layout: row r holds 64 bytes as four 16-byte chunks; chunk q sits at slot
+// q ^ (r/4 mod 4), which keeps both the staging stores (four lanes per row) and the
+// fragment reads (one chunk of sixteen consecutive rows per 16 lanes) on distinct banks.
+// Scale bytes: row r's eight bytes of the stage at offset 8 r of the operand's scale area.
+__device__ __forceinline__ int code_off(int row, int chunk) {
+    return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+// ---------------------------------------------------------------- one stage of MMA
+
+// {s/256, s/256} as a binary16 pair from byte B of w, an E4M3 scale code with the sign
+// bit clear: the code shifted left by 7 lands its exponent and mantissa in the binary16
+// fields, which reads as the scale / 256 for normal and subnormal codes alike.
+template <int B>
+__device__ __forceinline__ half2v scale_pair(uint32_t w) {
+    constexpr uint32_t sel = 0x000C000Cu | (B << 8) | (B << 24);   // bytes {0, b, 0, b}
+    return __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0u, w, sel) >> 1);
+}
+
+// 8 codes -> 8 binary16 values (v * 256) * (s / 256) = v * s (exact), in the order
+// (n0, n1), (n2, n3), (n4, n5), (n6, n7) of the word's nibbles.  The conversion reads
+// one VGPR per output pair; bit-manipulation decodes (byte-table v_perm and the like)
+// need fewer issue cycles but several VGPR operands per pair, and measured slower here
+// because the MFMAs running beside them compete for the same register-file ports.
+__device__ __forceinline__ half8v decode8(uint32_t w, half2v s2) {
+    const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * s2;
+    const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * s2;
+    const half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * s2;
+    const half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * s2;
+    half8v o = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+    return o;
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
+    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// Sched-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008;
+
+// This wave's packed operands of one stage: 32 code bytes and 4 scale bytes per sub-tile.
+struct Frags {
+    uint4 fa[4][2], fb[4][2];
+    uint32_t wsa[4], wsb[4];
+};
+
+__device__ __forceinline__ void read_frags(const uint8_t* cur, int wm, int wn, int h, int li,
+                                           Frags& f) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const int ra = wm * 128 + x * 32 + li, rb = wn * 128 + x * 32 + li;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+            f.fa[x][c2] = *(const uint4*)(cur + code_off(ra, 2 * h + c2));
+            f.fb[x][c2] = *(const uint4*)(cur + kStageCodeBytes + code_off(rb, 2 * h + c2));
+        }
+        f.wsa[x] = *(const uint32_t*)(cur + 2 * kStageCodeBytes + ra * 8 + 4 * h);
+        f.wsb[x] = *(const uint32_t*)(cur + 2 * kStageCodeBytes + kStageScaleBytes + rb * 8 + 4 * h);
+    }
+}
+
+__device__ __forceinline__ void mma_stage(const Frags& f, float16v (&acc)[4][4]) {
+    // scales of this lane's four blocks per sub-tile as binary16 pairs
+    half2v psa[4][4], psb[4][4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        psa[x][0] = scale_pair<0>(f.wsa[x]); psa[x][1] = scale_pair<1>(f.wsa[x]);
+        psa[x][2] = scale_pair<2>(f.wsa[x]); psa[x][3] = scale_pair<3>(f.wsa[x]);
+        psb[x][0] = scale_pair<0>(f.wsb[x]); psb[x][1] = scale_pair<1>(f.wsb[x]);
+        psb[x][2] = scale_pair<2>(f.wsb[x]); psb[x][3] = scale_pair<3>(f.wsb[x]);
+    }
+    half8v av[4], bv[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        av[x] = decode8(f.fa[x][0].x, psa[x][0]);
+        bv[x] = decode8(f.fb[x][0].x, psb[x][0]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+        half8v an[4], bn[4];
+        if (tt < 7) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                an[x] = decode8(dword_of(f.fa[x][(tt + 1) >> 2], (tt + 1) & 3), psa[x][(tt + 1) >> 1]);
+                bn[x] = decode8(dword_of(f.fb[x][(tt + 1) >> 2], (tt + 1) & 3), psb[x][(tt + 1) >> 1]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        // each MFMA followed by four decode instructions of the next slot
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVALU, 4, 0);
+        }
+        if (tt < 7) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) { av[x] = an[x]; bv[x] = bn[x]; }
+        }
+    }
+}
+
+// D register r of lane l is row 8(r/4) + 4(l/32) + r%4, column l%32 of its 32x32 block.
+__device__ __forceinline__ void store_tile(const GArgs& g, const float16v (&acc)[4][4], int64_t m0,
+                                           int64_t n0, int wm, int wn, int h, int li) {
+    const float scale = *g.asg * *g.bsg;
+    const int64_t rbase = m0 + wm * 128 + 4 * h, cbase = n0 + wn * 128 + li;
+    if (m0 + GBM <= g.M && n0 + GBN <= g.N) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float* rowp = g.c + (rbase + i * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc + cbase;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) rowp[j * 32] = acc[i][j][r] * scale;
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t col = cbase + j * 32;
+                    if (row < g.M && col < g.N) g.c[row * g.ldc + col] = acc[i][j][r] * scale;
+                }
+            }
+    }
+}
+
+__device__ __forceinline__ void zero_acc(float16v (&acc)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+}
+
+// ---------------------------------------------------------------- generic staging path
 
 struct StageRegs {
     uint4 a[4], b[4];
@@ -87,13 +250,6 @@ __device__ __forceinline__ void load_stage(const GArgs& g, int64_t m0, int64_t n
     r.sb = load_scales8(g.bs, n0 + t, g.N, kb0, kblocks);
 }
 
-// Packed tile layout: row r holds 64 bytes as four 16-byte chunks; chunk q sits at slot
-// q ^ (r/4 mod 4), which keeps both the staging stores (four lanes per row) and the
-// fragment reads (one chunk of sixteen consecutive rows per 16 lanes) on distinct banks.
-__device__ __forceinline__ int code_off(int row, int chunk) {
-    return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
-}
-
 __device__ __forceinline__ void store_stage(uint8_t* buf, const StageRegs& r) {
     const int t = threadIdx.x;
     uint8_t* ac = buf;
@@ -110,145 +266,139 @@ __device__ __forceinline__ void store_stage(uint8_t* buf, const StageRegs& r) {
     *(uint2*)(bs + t * 8) = r.sb;
 }
 
-// E4M3 code -> binary16 without branches: the E4M3 bits shifted into the binary16
-// exponent/mantissa fields give value / 256 (both formats put their subnormals at the
-// same offset), so one exact multiply by 256 restores it.
-__device__ __forceinline__ _Float16 scale_f16(uint32_t code) {
-    const uint16_t bits = (uint16_t)((code & 0x7Fu) << 7);
-    return __builtin_bit_cast(_Float16, bits) * (_Float16)256.0f;
-}
-
-__device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
-    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-
-// 8 codes -> 8 binary16 values v * s (exact).
-__device__ __forceinline__ half8v decode8(uint32_t w, half2v s2) {
-    const half2v p0 = fp4x2_to_f16<0>(w) * s2;
-    const half2v p1 = fp4x2_to_f16<1>(w) * s2;
-    const half2v p2 = fp4x2_to_f16<2>(w) * s2;
-    const half2v p3 = fp4x2_to_f16<3>(w) * s2;
-    half8v o = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-    return o;
-}
-
-// Sched-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008;
-
 __global__ __launch_bounds__(GThreads, 1) void k_gemm(GArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6, wm = wid >> 1, wn = wid & 1;
     const int tm = blockIdx.x / g.tiles_n, tn = blockIdx.x % g.tiles_n;
     const int64_t m0 = (int64_t)tm * GBM, n0 = (int64_t)tn * GBN;
     const int h = lane >> 5, li = lane & 31;
-    const float scale = *g.asg * *g.bsg;
-    uint8_t* stages = lds;
 
     float16v acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
+    zero_acc(acc);
     const int nst = (int)((g.K + GBK - 1) / GBK);
     StageRegs regs;
     if (nst > 0) {
         load_stage(g, m0, n0, 0, regs);
-        store_stage(stages, regs);
+        store_stage(lds, regs);
     }
     __syncthreads();
-
     for (int s = 0; s < nst; ++s) {
-        const uint8_t* cur = stages + (s & 1) * kStageBytes;
+        const uint8_t* cur = lds + (s & 1) * kStageBytes;
         if (s + 1 < nst) load_stage(g, m0, n0, s + 1, regs);
-
-        // this wave's packed fragments: 32 bytes of codes and 4 scale bytes per sub-tile
-        uint4 fa[4][2], fb[4][2];
-        uint32_t wsa[4], wsb[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int ra = wm * 128 + x * 32 + li, rb = wn * 128 + x * 32 + li;
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                fa[x][c2] = *(const uint4*)(cur + code_off(ra, 2 * h + c2));
-                fb[x][c2] = *(const uint4*)(cur + kStageCodeBytes + code_off(rb, 2 * h + c2));
-            }
-            wsa[x] = *(const uint32_t*)(cur + 2 * kStageCodeBytes + ra * 8 + 4 * h);
-            wsb[x] = *(const uint32_t*)(cur + 2 * kStageCodeBytes + kStageScaleBytes + rb * 8 + 4 * h);
-        }
-        // scales of this lane's four blocks per sub-tile as binary16 pairs
-        half2v psa[4][4], psb[4][4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const _Float16 sa = scale_f16((wsa[x] >> (8 * b)) & 0xFFu);
-                const _Float16 sb = scale_f16((wsb[x] >> (8 * b)) & 0xFFu);
-                psa[x][b] = half2v{sa, sa};
-                psb[x][b] = half2v{sb, sb};
-            }
-        half8v av[4], bv[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            av[x] = decode8(fa[x][0].x, psa[x][0]);
-            bv[x] = decode8(fb[x][0].x, psb[x][0]);
-        }
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-            half8v an[4], bn[4];
-            if (tt < 7) {
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    an[x] = decode8(dword_of(fa[x][(tt + 1) >> 2], (tt + 1) & 3), psa[x][(tt + 1) >> 1]);
-                    bn[x] = decode8(dword_of(fb[x][(tt + 1) >> 2], (tt + 1) & 3), psb[x][(tt + 1) >> 1]);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-            // each MFMA followed by four decode instructions of the next slot
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(kSchedVALU, 4, 0);
-            }
-            if (tt < 7) {
-#pragma unroll
-                for (int x = 0; x < 4; ++x) { av[x] = an[x]; bv[x] = bn[x]; }
-            }
-        }
-        if (s + 1 < nst) store_stage(stages + ((s + 1) & 1) * kStageBytes, regs);
+        Frags f;
+        read_frags(cur, wm, wn, h, li, f);
+        mma_stage(f, acc);
+        if (s + 1 < nst) store_stage(lds + ((s + 1) & 1) * kStageBytes, regs);
         __syncthreads();
     }
+    store_tile(g, acc, m0, n0, wm, wn, h, li);
+}
 
-    // epilogue: D register r of lane l is row 8(r/4) + 4(l/32) + r%4, column l%32
-    const int64_t rbase = m0 + wm * 128 + 4 * h, cbase = n0 + wn * 128 + li;
-    if (m0 + GBM <= g.M && n0 + GBN <= g.N) {
+// ---------------------------------------------------------------- direct staging path
+
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor of a raw byte buffer: base, no stride, num_records bytes, the data
+// format word of untyped 32-bit buffer access.
+__device__ __forceinline__ int4v make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    return int4v{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+
+// Direct loads.  They are written as assembly so that the compiler does not track them:
+// its own bookkeeping would otherwise wait for every pending direct load before each LDS
+// read, which would serialise the three-stage pipeline.  The kernel waits for them
+// explicitly (dma_wait_barrier); it issues no other vector-memory loads in the loop, so
+// the compiler's own waits can only wait longer than needed, never shorter.
+__device__ __forceinline__ void dma16(int4v rsrc, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(int4v rsrc, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
+struct Rsrc4 {
+    int4v ac, as, bc, bs;
+};
+
+// Issue this wave's 12 direct loads of stage s into the LDS stage at byte address buf.
+// Load i of the codes covers LDS slots [256 i + 64 wid, +64) of the operand's tile; slot
+// p = row * 4 + q receives global chunk q ^ (row/4 mod 4) of the row, which is the layout
+// code_off describes.
+__device__ __forceinline__ void dma_stage(const GArgs& g, const Rsrc4& rs, uint32_t buf,
+                                          int64_t m0, int64_t n0, int s, int t, int wid,
+                                          uint32_t kbytes, uint32_t kblocks) {
+    const uint32_t k0b = (uint32_t)s * 64;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float* rowp = g.c + (rbase + i * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc + cbase;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) rowp[j * 32] = acc[i][j][r] * scale;
-            }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int64_t col = cbase + j * 32;
-                    if (row < g.M && col < g.N) g.c[row * g.ldc + col] = acc[i][j][r] * scale;
-                }
-            }
+    for (int i = 0; i < 4; ++i) {
+        const int p = i * 256 + t, row = p >> 2, q = p & 3;
+        const uint32_t off = k0b + (uint32_t)((q ^ ((row >> 2) & 3)) << 4);
+        const bool kin = off < kbytes;
+        const uint32_t va = (kin && m0 + row < g.M) ? (uint32_t)(m0 + row) * kbytes + off : kOutOfRange;
+        const uint32_t vb = (kin && n0 + row < g.N) ? (uint32_t)(n0 + row) * kbytes + off : kOutOfRange;
+        const uint32_t dst = buf + (uint32_t)(i * 256 + wid * 64) * 16;
+        dma16(rs.ac, dst, va);
+        dma16(rs.bc, dst + kStageCodeBytes, vb);
     }
+    const uint32_t kb0 = (uint32_t)s * 8;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int j = i * 256 + t, row = j >> 1;
+        const uint32_t kb = kb0 + 4 * (j & 1);
+        const bool kin = kb < kblocks;
+        const uint32_t va = (kin && m0 + row < g.M) ? (uint32_t)(m0 + row) * kblocks + kb : kOutOfRange;
+        const uint32_t vb = (kin && n0 + row < g.N) ? (uint32_t)(n0 + row) * kblocks + kb : kOutOfRange;
+        const uint32_t dst = buf + 2 * kStageCodeBytes + (uint32_t)(i * 256 + wid * 64) * 4;
+        dma4(rs.as, dst, va);
+        dma4(rs.bs, dst + kStageScaleBytes, vb);
+    }
+}
+
+// Wait until at most N of this wave's direct loads are outstanding (they complete in
+// issue order), then meet the other waves: after it every wave's loads of the awaited
+// stage are in LDS and every wave has finished reading the buffer about to be refilled.
+template <int N>
+__device__ __forceinline__ void dma_wait_barrier() {
+    if constexpr (N == 0)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+__global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(t >> 6), wm = wid >> 1, wn = wid & 1;
+    const int tm = blockIdx.x / g.tiles_n, tn = blockIdx.x % g.tiles_n;
+    const int64_t m0 = (int64_t)tm * GBM, n0 = (int64_t)tn * GBN;
+    const int h = lane >> 5, li = lane & 31;
+    const uint32_t kbytes = (uint32_t)(g.K / 2), kblocks = (uint32_t)(g.K / 16);
+    Rsrc4 rs;
+    rs.ac = make_rsrc(g.ac, (uint32_t)(g.M * kbytes));
+    rs.bc = make_rsrc(g.bc, (uint32_t)(g.N * kbytes));
+    rs.as = make_rsrc(g.as, (uint32_t)(g.M * kblocks));
+    rs.bs = make_rsrc(g.bs, (uint32_t)(g.N * kblocks));
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+
+    float16v acc[4][4];
+    zero_acc(acc);
+    const int nst = (int)((g.K + GBK - 1) / GBK);
+    if (nst > 0) dma_stage(g, rs, lds0, m0, n0, 0, t, wid, kbytes, kblocks);
+    if (nst > 1) dma_stage(g, rs, lds0 + kStageBytes, m0, n0, 1, t, wid, kbytes, kblocks);
+    int cb = 0, nb = 2;   // LDS buffer of stage s and of stage s + 2
+    for (int s = 0; s < nst; ++s) {
+        if (s + 1 < nst) dma_wait_barrier<kDmaLoadsPerStage>();
+        else dma_wait_barrier<0>();
+        Frags f;
+        read_frags(lds + cb * kStageBytes, wm, wn, h, li, f);
+        if (s + 2 < nst) dma_stage(g, rs, lds0 + nb * kStageBytes, m0, n0, s + 2, t, wid, kbytes, kblocks);
+        mma_stage(f, acc);
+        cb = cb == kDmaStages - 1 ? 0 : cb + 1;
+        nb = nb == kDmaStages - 1 ? 0 : nb + 1;
+    }
+    store_tile(g, acc, m0, n0, wm, wn, h, li);
 }
 
 }  // namespace nvfp4
@@ -271,10 +421,22 @@ extern "C" int nvfp4_gemm(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_
     g.M = M; g.N = N; g.K = K; g.c = c; g.ldc = ldc;
     const int64_t tiles_m = (M + GBM - 1) / GBM, tiles_n = (N + GBN - 1) / GBN;
     g.tiles_n = (int)tiles_n;
-    static_assert(kGemmLds <= 160 * 1024, "LDS budget");
-    if (hipFuncSetAttribute((const void*)k_gemm, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kGemmLds) != hipSuccess)
-        return NVFP4_ERR_HIP;
-    k_gemm<<<(unsigned)(tiles_m * tiles_n), GThreads, kGemmLds, (hipStream_t)stream>>>(g);
+    const unsigned grid = (unsigned)(tiles_m * tiles_n);
+    static_assert(kGemmDmaLds <= 160 * 1024 && kGemmLds <= 160 * 1024, "LDS budget");
+    // direct path: whole 4-byte scale words per row and stage, 32-bit buffer offsets
+    const int64_t kbytes = K / 2, limit = (int64_t)kOutOfRange;
+    const bool direct = K > 0 && K % 64 == 0 && ((uintptr_t)a->scales & 3) == 0 &&
+                        ((uintptr_t)b->scales & 3) == 0 && M * kbytes < limit && N * kbytes < limit;
+    if (direct) {
+        if (hipFuncSetAttribute((const void*)k_gemm_dma, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kGemmDmaLds) != hipSuccess)
+            return NVFP4_ERR_HIP;
+        k_gemm_dma<<<grid, GThreads, kGemmDmaLds, (hipStream_t)stream>>>(g);
+    } else {
+        if (hipFuncSetAttribute((const void*)k_gemm, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kGemmLds) != hipSuccess)
+            return NVFP4_ERR_HIP;
+        k_gemm<<<grid, GThreads, kGemmLds, (hipStream_t)stream>>>(g);
+    }
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
