@@ -65,7 +65,7 @@ struct GArgs {
     int64_t M, N, K;
     float* c;
     int64_t ldc;
-    int tiles_n;
+    int tiles_m, tiles_n;
 };
 
 // Packed tile layout: row r holds 64 bytes as four 16-byte chunks; chunk q sits at slot
@@ -174,32 +174,45 @@ __device__ __forceinline__ void mma_stage(const Frags& f, float16v (&acc)[4][4])
 }
 
 // D register r of lane l is row 8(r/4) + 4(l/32) + r%4, column l%32 of its 32x32 block.
+// One 32x32 block at a time, with scheduling fences between blocks so that the compiler
+// does not pull all 256 accumulators into VGPRs at once.
 __device__ __forceinline__ void store_tile(const GArgs& g, const float16v (&acc)[4][4], int64_t m0,
                                            int64_t n0, int wm, int wn, int h, int li) {
     const float scale = *g.asg * *g.bsg;
     const int64_t rbase = m0 + wm * 128 + 4 * h, cbase = n0 + wn * 128 + li;
-    if (m0 + GBM <= g.M && n0 + GBN <= g.N) {
+    const bool full = m0 + GBM <= g.M && n0 + GBN <= g.N;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float* rowp = g.c + (rbase + i * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc + cbase;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) rowp[j * 32] = acc[i][j][r] * scale;
-            }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) {
+            const int64_t col = cbase + j * 32;
+            const bool col_ok = full || col < g.N;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int64_t col = cbase + j * 32;
-                    if (row < g.M && col < g.N) g.c[row * g.ldc + col] = acc[i][j][r] * scale;
-                }
+                if (col_ok && (full || row < g.M)) g.c[row * g.ldc + col] = acc[i][j][r] * scale;
             }
-    }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+}
+
+// Tile of workgroup `bid`.  Workgroups are dealt to the eight XCDs round-robin (bid mod 8)
+// and each XCD has its own L2, so XCD x is given the contiguous range of tile ids
+// [x T/8, (x+1) T/8) (remainder spread over the first XCDs), and tile ids walk down
+// groups of 8 tile rows column by column: the 32 workgroups an XCD runs at once then share
+// A rows of 8 tile rows and B rows of about 4 tile columns in that XCD's L2.
+constexpr int kXcds = 8, kGroupRows = 8;
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int total = tiles_m * tiles_n;
+    const int q = total / kXcds, r = total % kXcds;
+    const int x = bid % kXcds, k = bid / kXcds;
+    const int id = x * q + (x < r ? x : r) + k;
+    const int group = id / (kGroupRows * tiles_n);
+    const int first = group * kGroupRows;
+    const int rows = tiles_m - first < kGroupRows ? tiles_m - first : kGroupRows;
+    const int in = id - group * kGroupRows * tiles_n;
+    tm = first + in % rows;
+    tn = in / rows;
 }
 
 __device__ __forceinline__ void zero_acc(float16v (&acc)[4][4]) {
@@ -269,7 +282,8 @@ __device__ __forceinline__ void store_stage(uint8_t* buf, const StageRegs& r) {
 __global__ __launch_bounds__(GThreads, 1) void k_gemm(GArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6, wm = wid >> 1, wn = wid & 1;
-    const int tm = blockIdx.x / g.tiles_n, tn = blockIdx.x % g.tiles_n;
+    int tm, tn;
+    tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * GBM, n0 = (int64_t)tn * GBN;
     const int h = lane >> 5, li = lane & 31;
 
@@ -371,7 +385,8 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int t = threadIdx.x, lane = t & 63;
     const int wid = __builtin_amdgcn_readfirstlane(t >> 6), wm = wid >> 1, wn = wid & 1;
-    const int tm = blockIdx.x / g.tiles_n, tn = blockIdx.x % g.tiles_n;
+    int tm, tn;
+    tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * GBM, n0 = (int64_t)tn * GBN;
     const int h = lane >> 5, li = lane & 31;
     const uint32_t kbytes = (uint32_t)(g.K / 2), kblocks = (uint32_t)(g.K / 16);
@@ -420,6 +435,7 @@ extern "C" int nvfp4_gemm(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_
     g.bc = b->codes; g.bs = b->scales; g.bsg = b->gscale;
     g.M = M; g.N = N; g.K = K; g.c = c; g.ldc = ldc;
     const int64_t tiles_m = (M + GBM - 1) / GBM, tiles_n = (N + GBN - 1) / GBN;
+    g.tiles_m = (int)tiles_m;
     g.tiles_n = (int)tiles_n;
     const unsigned grid = (unsigned)(tiles_m * tiles_n);
     static_assert(kGemmDmaLds <= 160 * 1024 && kGemmLds <= 160 * 1024, "LDS budget");
