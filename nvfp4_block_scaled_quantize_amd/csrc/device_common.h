@@ -66,16 +66,16 @@ __device__ __forceinline__ float apply_sign(float v, uint32_t bits, int i) {
 }
 
 // ---------------------------------------------------------------- E4M3 block scale
-// Nearest-even with saturation at 448 for s >= 0.
+// Nearest-even with saturation at 448 for s >= 0 (NaN -> 0), without branches: the
+// subnormal candidate (step 2^-9) and the normal one (mantissa rounded to 3 bits, ties
+// to even, exponent rebiased 127 -> 7) are both formed and one is selected.
 __device__ __forceinline__ uint32_t e4m3_encode(float s) {
-    if (s >= 448.0f) return 0x7Eu;
-    if (!(s == s)) return 0u;
-    if (s < 0.015625f) {                       // below 2^-6: subnormal step 2^-9
-        return (uint32_t)rintf(s * 512.0f);   // exact scaling, nearest-even; 8 = 2^-6
-    }
+    const uint32_t sub = (uint32_t)rintf(fminf(s, 1.0f) * 512.0f);   // exact scaling
     uint32_t b = __float_as_uint(s);
-    b = b + 0x7FFFFu + ((b >> 20) & 1u);      // round the mantissa to 3 bits, ties to even
-    return (b >> 20) - 960u;                   // rebias exponent 127 -> 7
+    b = b + 0x7FFFFu + ((b >> 20) & 1u);
+    uint32_t c = s < 0.015625f ? sub : (b >> 20) - 960u;              // 2^-6: smallest normal
+    c = s >= 448.0f ? 0x7Eu : c;
+    return s == s ? c : 0u;
 }
 
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
@@ -93,22 +93,21 @@ __device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b) {
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
 }
 
-// Stochastic rounding of a magnitude u >= 0 with 16 random bits: up iff
-// frac + r/2^16 >= 1, where frac = (u - c_k) / Delta_k.  Every step is exact.
-__device__ __forceinline__ uint32_t sr_mag(float u, uint32_t r16) {
-    if (!(u < 6.0f)) return 7u;
-    uint32_t k = (uint32_t)(u >= 0.5f) + (uint32_t)(u >= 1.0f) + (uint32_t)(u >= 1.5f) +
-                 (uint32_t)(u >= 2.0f) + (uint32_t)(u >= 3.0f) + (uint32_t)(u >= 4.0f);
-    float lo = k < 4 ? 0.5f * (float)k : (k == 4 ? 2.0f : (k == 5 ? 3.0f : 4.0f));
-    float inv_delta = k < 4 ? 2.0f : (k < 6 ? 1.0f : 0.5f);
-    float frac = (u - lo) * inv_delta;
-    float need = 1.0f - (float)r16 * (1.0f / 65536.0f);
-    return k + (frac >= need ? 1u : 0u);
-}
-
+// Stochastic rounding of x * rcp to an E2M1 code with 16 random bits r16: the magnitude
+// u = |x| rcp goes to its upper grid neighbour iff frac + r16 / 2^16 >= 1, frac being u's
+// position between its two neighbours (saturating at 6).  Only the 16 bits of u just
+// below the grid spacing can change that decision, so it is taken exactly on integers:
+//   u >= 1: the grid keeps one mantissa bit, and rounding up is the carry of
+//           bits(u) + (r16 << 6) out of the 22 dropped mantissa bits; the kept exponent
+//           and mantissa bit then read as code + 252 (clamped to 7 = 6.0);
+//   u <  1: the spacing is 1/2, and floor(u * 2^17) + r16 carries into bit 16 exactly
+//           when 2u's fraction plus r16 / 2^16 reaches 1; the quotient is the code (0..2).
+// No branches: both candidates are formed and one is selected.
 __device__ __forceinline__ uint32_t sr_code(float x, float rcp, uint32_t r16) {
-    float u = fabsf(x) * rcp;
-    return ((__float_as_uint(x) >> 28) & 8u) | sr_mag(u, r16);
+    const float u = fabsf(x) * rcp;
+    const uint32_t ca = min(((__float_as_uint(u) + (r16 << 6)) >> 22) - 252u, 7u);
+    const uint32_t cb = ((uint32_t)(fminf(u, 1.0f) * 131072.0f) + r16) >> 16;
+    return (u < 1.0f ? cb : ca) | ((__float_as_uint(x) >> 28) & 8u);
 }
 
 // Decode the two E2M1 codes in byte SEL of w to binary32 (exact).
