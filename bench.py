@@ -48,17 +48,108 @@ def parse():
                     help="rows of X for the oracle's bounded CPU sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (HBM counter calibration)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="write profiles/ffn3b_step_kernel_stats.txt from a rocprofv3 "
+                         "--kernel-trace --stats folder of one bench run")
+    ap.add_argument("--counter-summary", nargs=4, metavar="DIR",
+                    help="write profiles/hbm_counters.txt from rocprofv3 --pmc folders: "
+                         "FETCH_SIZE and WRITE_SIZE of one bench step, then of --copy-calibration")
     return ap.parse_args()
 
 
-def counters_for(kernel_file, key):
-    """HBM traffic per launch from a committed rocprofv3 counter summary, or None if the
-    kernel source changed since the counters were taken."""
+# Source files that define each kernel family, hashed together so that a counter entry is
+# used only while none of them has changed.
+CSRC = os.path.join(ROOT, "nvfp4_block_scaled_quantize_amd", "csrc")
+SOURCES = {
+    "gemm": ["gemm.hip", "device_common.h"],
+    "quant": ["quantize.hip", "quantize_kernels.h", "quantize_launch_bf16_lo.hip",
+              "quantize_launch_bf16_hi.hip", "quantize_launch_f32_lo.hip",
+              "quantize_launch_f32_hi.hip", "device_common.h"],
+    "qadamw": ["qadamw.hip", "device_common.h"],
+}
+FAMILY = {"gemm": "gemm", "quant": "quant", "qadamw_encode": "qadamw", "qadamw_decode": "qadamw",
+          "dequant": "quant"}
+# kernels each call of the step launches, in order (name prefixes; '?' marks optional)
+CALL_KERNELS = {"quant": ["?k_amax", "k_encode|k_quant"], "gemm": ["k_gemm"],
+                "qadamw_encode": ["k_qv_pass1", "k_qv_pass2"], "qadamw_decode": ["k_qv_decode"],
+                "dequant": ["k_dequant"]}
+
+
+STEP_ORDER = [("quant_X_row+colRHT", "quant"), ("quant_Wup_2d", "quant"), ("gemm_ffn_up", "gemm"),
+              ("quant_H_row", "quant"), ("quant_Wdown_2d", "quant"), ("gemm_ffn_down", "gemm"),
+              ("quant_dY_rowSR+colRHTSR", "quant"), ("gemm_dgrad", "gemm"), ("gemm_wgrad", "gemm"),
+              ("qadamw_encode", "qadamw_encode"), ("qadamw_decode", "qadamw_decode"),
+              ("dequant_Wup", "dequant")]
+
+
+def split_step(names):
+    """Assign a step's dispatch names (our kernels only, in order) to the step's calls;
+    returns [(key, [dispatch indices])] per call, repeated for as many steps as present."""
+    out, i = [], 0
+    while i < len(names):
+        for key, kind in STEP_ORDER:
+            idx = []
+            for pat in CALL_KERNELS[kind]:
+                alts = pat.lstrip("?").split("|")
+                if i < len(names) and any(a in names[i] for a in alts):
+                    idx.append(i)
+                    i += 1
+                elif not pat.startswith("?"):
+                    raise SystemExit(f"dispatch {i} ({names[i] if i < len(names) else 'none'}) "
+                                     f"does not match {pat} for {key}")
+            out.append((key, idx))
+    return out
+
+
+def trace_summary(d):
+    """Write profiles/ffn3b_step_kernel_stats.txt from a rocprofv3 --kernel-trace --stats
+    folder of `bench.py --steps 10 --warmup 2 --no-cpu-baseline`: the per-kernel statistics
+    and, from the dispatch trace, the average duration of each call of the step."""
+    import csv
+    import glob as _glob
+    stats = list(csv.DictReader(open(_glob.glob(os.path.join(d, "*kernel_stats.csv"))[0])))
+    trace = list(csv.DictReader(open(_glob.glob(os.path.join(d, "*kernel_trace.csv"))[0])))
+    trace = [r for r in trace if "nvfp4::" in r["Kernel_Name"]]
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace]
+    per = {}
+    for key, idx in split_step([r["Kernel_Name"] for r in trace]):
+        per.setdefault(key, []).append(sum(dur[i] for i in idx))
+    lines = ["# rocprofv3 kernel-trace summary: 3B FFN linear hot-path step (bench.py workload)",
+             "# commands (from the repository root on one MI355X; cd /tmp && TMPDIR=/tmp first):",
+             "#   rocprofv3 --kernel-trace --stats --output-format csv -d <kt> -o bench \\",
+             "#       -- python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+             "#   python3 bench.py --trace-summary <kt>",
+             "# per kernel (all steps, warm-up included):",
+             f"# {'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'share%':>7s}"]
+    for r in stats:
+        lines.append(f"{r['Name'][:62]:62s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                     f"{int(r['MinNs']) / 1e3:9.2f} {int(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):7.2f}")
+    lines.append("# per call of the step (sum of its kernels' durations), from the dispatch trace:")
+    lines.append(f"# {'call':28s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}")
+    for key, _ in STEP_ORDER:
+        v = per.get(key, [])
+        if v:
+            lines.append(f"{key:30s} {len(v):6d} {sum(v) / len(v):9.2f} {min(v):9.2f} {max(v):9.2f}")
+    out = os.path.join(ROOT, "profiles", "ffn3b_step_kernel_stats.txt")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def source_digest(family):
+    h = hashlib.sha256()
+    for f in SOURCES[family]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def counters_for(key, kind):
+    """HBM bytes per launch (fetch + write) from the committed rocprofv3 counter summary, or
+    None if a source of that kernel changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_counters.txt")
     if not os.path.exists(path):
         return None
-    src = os.path.join(ROOT, "nvfp4_block_scaled_quantize_amd", "csrc", kernel_file)
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    digest = source_digest(FAMILY[kind])
     for line in open(path):
         t = line.split()
         if len(t) >= 4 and not line.startswith("#") and t[0] == key and t[1] == digest:
@@ -66,8 +157,59 @@ def counters_for(kernel_file, key):
     return None
 
 
+def counter_summary(dirs):
+    """Write profiles/hbm_counters.txt from four rocprofv3 --pmc output folders: FETCH_SIZE and
+    WRITE_SIZE of `bench.py --steps 1 --warmup 0 --no-cpu-baseline`, then of
+    `bench.py --copy-calibration`.  Counters are KiB per dispatch (summed over the L2
+    instances); each is scaled by (bytes a plain 256 MiB device copy moves) / (what the same
+    counter reads for that copy)."""
+    import csv
+    import glob as _glob
+
+    def per_dispatch(d):
+        f = _glob.glob(os.path.join(d, "*counter_collection.csv"))[0]
+        agg, name = {}, {}
+        for r in csv.DictReader(open(f)):
+            k = int(r["Dispatch_Id"])
+            agg[k] = agg.get(k, 0.0) + float(r["Counter_Value"])
+            name[k] = r["Kernel_Name"]
+        return [(name[k], agg[k] * 1024.0) for k in sorted(agg)]
+
+    fetch, write, cfetch, cwrite = (per_dispatch(d) for d in dirs)
+    copy_bytes = 256 << 20
+    fc = [v for n, v in cfetch if "copyBuffer" in n or "copy" in n.lower()]
+    wc = [v for n, v in cwrite if "copyBuffer" in n or "copy" in n.lower()]
+    f_scale = copy_bytes / (sum(fc[-5:]) / 5)
+    w_scale = copy_bytes / (sum(wc[-5:]) / 5)
+    ours = [(n, fv, wv) for (n, fv), (_, wv) in zip(fetch, write) if "nvfp4::" in n]
+    order = STEP_ORDER
+    lines = ["# HBM traffic per launch from rocprofv3 --pmc (TCC FETCH_SIZE, WRITE_SIZE; one pass each)",
+             "# commands (from the repository root, cd /tmp && TMPDIR=/tmp first):",
+             "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <f> -o bench -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
+             "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <w> -o bench -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
+             "#   rocprofv3 --pmc FETCH_SIZE ... -d <cf> -o copy -- python3 bench.py --copy-calibration   (and WRITE_SIZE -> <cw>)",
+             "#   python3 bench.py --counter-summary <f> <w> <cf> <cw>",
+             f"# calibration: a 256 MiB device copy reads {sum(fc[-5:]) / 5 / 2**20:.1f} MiB FETCH_SIZE and "
+             f"{sum(wc[-5:]) / 5 / 2**20:.1f} MiB WRITE_SIZE -> scale fetch x{f_scale:.3f}, write x{w_scale:.3f}",
+             "# key  source-digest  fetch_bytes  write_bytes  (per launch, calibrated)"]
+    kinds = dict(order)
+    for key, idx in split_step([n for n, _, _ in ours])[:len(order)]:
+        fb = sum(ours[i][1] for i in idx)
+        wb = sum(ours[i][2] for i in idx)
+        lines.append(f"{key} {source_digest(FAMILY[kinds[key]])} {fb * f_scale:.0f} {wb * w_scale:.0f}")
+    out = os.path.join(ROOT, "profiles", "hbm_counters.txt")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU path is a design note, not part of this build)", file=sys.stderr)
@@ -212,15 +354,15 @@ def main():
     q_ms = sum(kernels[n]["ms"] for n in q_names)
     up = kernels["gemm_ffn_up"]
     up_flops = work["gemm_ffn_up"][2]
-    roofline = {"bound": "mfma", "kernel": "k_gemm (FFN-up 8192x9216x3072)",
+    roofline = {"bound": "mfma", "kernel": "k_gemm_dma (FFN-up 8192x9216x3072)",
                 "achieved": up["TFLOP/s"], "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(up["TFLOP/s"] / PEAK_F16_TFLOPS, 4),
-                "traffic": counters_for("gemm.hip", "gemm_ffn_up")}
+                "traffic": counters_for("gemm_ffn_up", "gemm")}
     xq = kernels["quant_X_row+colRHT"]
     roofline_quant = {"bound": "hbm", "kernel": "k_amax+k_encode (X 8192x3072 bf16, row + col RHT)",
                       "achieved": xq["GB/s"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                       "frac": round(xq["GB/s"] / PEAK_HBM_GBPS, 4),
-                      "traffic": counters_for("quantize.hip", "quant_X_row+colRHT")}
+                      "traffic": counters_for("quant_X_row+colRHT", "quant")}
 
     out = {
         "metric": METRIC,
