@@ -56,7 +56,7 @@ def _load():
         "or_rht16_forward": (None, [P, P]),
         "or_rht16_inverse": (None, [P, P]),
         "or_quantize_rows": (ctypes.c_int, [P, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                            u64, u32, P, P, P]),
+                                            ctypes.c_int, u64, u32, P, P, P]),
         "or_dequantize": (ctypes.c_int, [P, P, f32, i64, i64, P]),
         "or_gemm_f64": (ctypes.c_int, [P, P, f32, P, P, f32, i64, i64, i64, P, P]),
         "or_gemm_f64_entries": (ctypes.c_int, [P, P, f32, P, P, f32, i64, i64, i64, P, P, i64,
@@ -170,32 +170,32 @@ class QTensor:
         return self.codes.shape[0], self.codes.shape[1] * 2
 
 
-def quantize_rows(x, block2d=False, rounding=RNE, rht=False, seed=0, copy_id=0):
+def quantize_rows(x, block2d=False, rounding=RNE, rht=False, seed=0, copy_id=0, scale46=False):
     """Quantize x[n][k] along its rows (blocks of 16 consecutive row elements, or
-    16x16 tiles)."""
+    16x16 tiles); scale46 selects 4/6 adaptive block scaling (1x16 blocks only)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     n, k = x.shape
     codes = np.zeros((n, k // 2), dtype=np.uint8)
     scales = np.zeros((n, k // 16), dtype=np.uint8)
     sg = ctypes.c_float(0.0)
     rc = _load().or_quantize_rows(_ptr(x), n, k, int(block2d), int(rounding), int(rht),
-                                  int(seed), int(copy_id), _ptr(codes), _ptr(scales),
-                                  ctypes.byref(sg))
+                                  int(scale46), int(seed), int(copy_id), _ptr(codes),
+                                  _ptr(scales), ctypes.byref(sg))
     _check(rc, "quantize_rows")
     return QTensor(codes, scales, sg.value)
 
 
 def quantize(x, rowwise=True, colwise=False, block2d=False, round_row=RNE, round_col=RNE,
-             rht_row=False, rht_col=False, seed=0):
+             rht_row=False, rht_col=False, seed=0, scale46=False):
     """Rowwise copy = quantization of x along rows; columnwise copy = the same
     quantization applied to x transposed (blocks of 16 consecutive rows of x)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     row = col = None
     if rowwise:
-        row = quantize_rows(x, block2d, round_row, rht_row, seed, copy_id=0)
+        row = quantize_rows(x, block2d, round_row, rht_row, seed, copy_id=0, scale46=scale46)
     if colwise:
         col = quantize_rows(np.ascontiguousarray(x.T), block2d, round_col, rht_col, seed,
-                            copy_id=1)
+                            copy_id=1, scale46=scale46)
     return row, col
 
 

@@ -242,9 +242,36 @@ static int all_finite(const float* x, int64_t count)
     return 1;
 }
 
+/* 4/6 adaptive block scaling.  [FS4] sec. 3 (and the introduction's list of
+ * primitives) applies "4/6 scaling" to every NVFP4 quantization and the related-work
+ * paragraph describes it as MSE-optimal adaptive block scaling; the rule itself is not
+ * given.  Reading (listed in the design doc): each 1x16 block has two candidate E4M3 scales,
+ * the usual one mapping the block amax to 6 and one mapping it to 4, both formed by the
+ * same nearest-even saturating encode with the tensor scale unchanged; the block keeps
+ * the candidate whose nearest-even quantization has the smaller squared error, 6 on a
+ * tie.  The squared error is taken in binary32 in a fixed order: per element
+ * e = fma(-(v s), s_g, y) with v the signed decoded code, accumulated as
+ * (fma chain over elements 0..7) + (fma chain over elements 8..15).  With stochastic
+ * rounding the choice is the same (made on nearest-even errors) and the elements are
+ * then rounded stochastically with the chosen scale. */
+static float block_sse_rne(const float* y, uint8_t scode, float sg)
+{
+    float part[2] = {0.0f, 0.0f};
+    float s = (float)or_e4m3_value(scode);
+    float rcp = scode ? 1.0f / (s * sg) : 0.0f;
+    for (int i = 0; i < 16; ++i) {
+        int mag = scode ? or_e2m1_rne(fabsf(y[i]) * rcp) : 0;
+        float v = (float)or_e2m1_value(mag);
+        if (signbit(y[i])) v = -v;
+        float e = fmaf(-(v * s), sg, y[i]);
+        part[i / 8] = fmaf(e, e, part[i / 8]);
+    }
+    return part[0] + part[1];
+}
+
 /* Quantize already-transformed values y[n][k]. */
 static void quantize_core(const float* y, int64_t n, int64_t k, int block2d, int rounding,
-                          uint64_t seed, uint32_t copy_id,
+                          int scale46, uint64_t seed, uint32_t copy_id,
                           uint8_t* codes, uint8_t* scales, float* sg_out)
 {
     float amax_t = 0.0f;
@@ -269,8 +296,14 @@ static void quantize_core(const float* y, int64_t n, int64_t k, int block2d, int
                     float a = fabsf(y[rr * k + c]);
                     if (a > amax_b) amax_b = a;
                 }
-            float s = (amax_b / 6.0f) / sg;
-            scales[r * kb + b] = or_e4m3_encode(s);
+            uint8_t scode = or_e4m3_encode((amax_b / 6.0f) / sg);
+            if (scale46 && !block2d) {
+                uint8_t scode4 = or_e4m3_encode((amax_b / 4.0f) / sg);
+                const float* blk = &y[r * k + b * 16];
+                if (block_sse_rne(blk, scode4, sg) < block_sse_rne(blk, scode, sg))
+                    scode = scode4;
+            }
+            scales[r * kb + b] = scode;
         }
     }
     /* elements */
@@ -302,11 +335,12 @@ static void quantize_core(const float* y, int64_t n, int64_t k, int block2d, int
 }
 
 int or_quantize_rows(const float* x, int64_t n, int64_t k, int block2d, int rounding,
-                     int rht, uint64_t seed, uint32_t copy_id,
+                     int rht, int scale46, uint64_t seed, uint32_t copy_id,
                      uint8_t* codes, uint8_t* scales, float* sg)
 {
     if (n < 0 || k < 0 || k % 16 != 0 || (block2d && n % 16 != 0)) return -2;
     if (rounding != 0 && rounding != 1) return -5;
+    if (scale46 && block2d) return -5;              /* 4/6 is defined for 1D blocks */
     if (!all_finite(x, n * k)) return -8;
     float* y = (float*)malloc(sizeof(float) * (size_t)(n * k > 0 ? n * k : 1));
     if (!y) return -9;
@@ -319,7 +353,7 @@ int or_quantize_rows(const float* x, int64_t n, int64_t k, int block2d, int roun
                 or_rht16_forward(&y[r * k + c], sgn);
     }
     memset(codes, 0, (size_t)(n * (k / 2)));
-    quantize_core(y, n, k, block2d, rounding, seed, copy_id, codes, scales, sg);
+    quantize_core(y, n, k, block2d, rounding, scale46, seed, copy_id, codes, scales, sg);
     free(y);
     return 0;
 }
@@ -465,7 +499,7 @@ int or_qadamw_v_encode(const float* v, int64_t R, int64_t C, uint64_t seed, int 
         for (int64_t c = 0; c < C; c += 16)
             or_rht16_forward(&y[r * C + c], sgn);
     memset(codes, 0, (size_t)(R * (C / 2)));                          /* step 4 */
-    quantize_core(y, R, C, 0, 0, seed, 0, codes, scales, sg);
+    quantize_core(y, R, C, 0, 0, 0, seed, 0, codes, scales, sg);
     free(y);
     return 0;
 }

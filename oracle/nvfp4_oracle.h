@@ -75,7 +75,7 @@ void or_rht16_inverse(float v[16], const float sgn[16]);
  * Outputs: codes[n][k/2] (element 2i in the low nibble), scales[n][k/16] (E4M3
  * codes; 16x16 tiles stored expanded, one byte per row of the tile), *sg. */
 int or_quantize_rows(const float* x, int64_t n, int64_t k, int block2d, int rounding,
-                     int rht, uint64_t seed, uint32_t copy_id,
+                     int rht, int scale46, uint64_t seed, uint32_t copy_id,
                      uint8_t* codes, uint8_t* scales, float* sg);
 
 /* Decode codes[n][k/2], scales[n][k/16], sg into binary32 out[n][k]:
