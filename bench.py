@@ -392,9 +392,58 @@ def main():
         "kernels": kernels,
     }
 
+    out["extras"] = extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, synthetic, ffn)
     print(json.dumps(out))
+
+
+def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, stream, iters=20):
+    """Measurements outside the step, same method (HIP events on the launch stream):
+    the X and dY quantizes with 4/6 adaptive block scaling, the QKV-projection GEMM of the
+    3B model, and a plain device copy for the box's achievable HBM bandwidth."""
+    qkv = synthetic.qkv()
+    Xq, Wqkv = qkv["X"].to(dev), qkv["W"].to(dev)
+    p46x = nv.quant_params(rowwise=True, colwise=True, rht_col=True, seed=SEED_WGRAD, scale46=True)
+    p46dy = nv.quant_params(rowwise=True, colwise=True, round_row=nv.NVFP4_SR,
+                            round_col=nv.NVFP4_SR, rht_col=True, seed=SEED_WGRAD, scale46=True)
+    pq = nv.quant_params(rowwise=True)
+    qa, _ = nv.nvfp4_quantize(Xq, pq)
+    qb, _ = nv.nvfp4_quantize(Wqkv, pq)
+    C = torch.empty((Xq.shape[0], Wqkv.shape[0]), dtype=torch.float32, device=dev)
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    M, K = Xq.shape
+    N = Wqkv.shape[0]
+    cases = {
+        "quant_X_row+colRHT_4/6": (lambda: nv.nvfp4_quantize(X, p46x, qx[0], qx[1], qx[2]),
+                                   2 * TOKENS * HIDDEN + 2 * qbytes(TOKENS, HIDDEN), 0),
+        "quant_dY_rowSR+colRHTSR_4/6": (lambda: nv.nvfp4_quantize(dY, p46dy, qdy[0], qdy[1], qdy[2]),
+                                        2 * TOKENS * FFN + 2 * qbytes(TOKENS, FFN), 0),
+        "gemm_qkv_8192x6144x3072": (lambda: nv.nvfp4_gemm(qa, qb, out=C),
+                                    qbytes(M, K) + qbytes(N, K) + 4 * M * N, 2 * M * N * K),
+        "hbm_copy_256MiB": (lambda: dst.copy_(src), 2 * (256 << 20), 0),
+    }
+    res = {}
+    for name, (fn, nbytes, flops) in cases.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(iters):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / iters
+        d = {"ms": round(ms, 5), "GB/s": round(nbytes / ms / 1e6, 1)}
+        if flops:
+            d["TFLOP/s"] = round(flops / ms / 1e9, 1)
+            d["frac_f16_peak"] = round(flops / ms / 1e9 / PEAK_F16_TFLOPS, 4)
+        else:
+            d["frac_hbm_peak"] = round(nbytes / ms / 1e6 / PEAK_HBM_GBPS, 4)
+        res[name] = d
+    return res
 
 
 def cpu_baseline(args, synthetic, ffn):

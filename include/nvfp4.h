@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 
 enum nvfp4_status {
     NVFP4_OK = 0,
@@ -84,12 +84,21 @@ enum nvfp4_block { NVFP4_BLOCK_1D = 0, NVFP4_BLOCK_2D = 1 };
  *                      random sign vector per call derived from `seed` (Full-Stack FP4
  *                      sec. 3.2: one random 16x16 Hadamard matrix per backward pass; both
  *                      Wgrad operands must use the same seed so the transforms cancel)
+ *   scale46            0/1: 4/6 adaptive block scaling (Full-Stack FP4 sec. 3 and its
+ *                      introduction name it for every NVFP4 quantization; the related-work
+ *                      paragraph calls it MSE-optimal adaptive block scaling).  Each 1x16
+ *                      block keeps, of the two E4M3 scales mapping its amax to 6 and to 4,
+ *                      the one whose nearest-even quantization has the smaller squared
+ *                      error (binary32: e = fma(-(v s), s_g, x), summed as two fma chains
+ *                      over elements 0..7 and 8..15, then added); 6 on a tie.  Stochastic
+ *                      rounding uses the scale so chosen.  Not defined for 16x16 blocks.
  *   seed               key of the Philox4x32-10 generator behind D and the SR draws */
 typedef struct {
     int32_t rowwise, colwise;
     int32_t block;
     int32_t round_row, round_col;
     int32_t rht_row, rht_col;
+    int32_t scale46;
     uint64_t seed;
 } nvfp4_quant_params;
 

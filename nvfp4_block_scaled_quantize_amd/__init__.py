@@ -40,7 +40,8 @@ class QuantParams(ctypes.Structure):
     _fields_ = [("rowwise", ctypes.c_int32), ("colwise", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("round_row", ctypes.c_int32),
                 ("round_col", ctypes.c_int32), ("rht_row", ctypes.c_int32),
-                ("rht_col", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("rht_col", ctypes.c_int32), ("scale46", ctypes.c_int32),
+                ("seed", ctypes.c_uint64)]
 
 
 class QTensorC(ctypes.Structure):
@@ -49,6 +50,7 @@ class QTensorC(ctypes.Structure):
 
 
 _lib = None
+ABI_VERSION = 2   # NVFP4_ABI_VERSION of include/nvfp4.h this binding matches
 
 
 def load_library(path: Optional[str] = None):
@@ -82,6 +84,9 @@ def load_library(path: Optional[str] = None):
     lib.nvfp4_status_string.argtypes = [ctypes.c_int]
     lib.nvfp4_abi_version.restype = ctypes.c_int
     lib.nvfp4_abi_version.argtypes = []
+    if lib.nvfp4_abi_version() != ABI_VERSION:
+        raise Nvfp4Error(f"{p} has ABI version {lib.nvfp4_abi_version()}, this binding expects "
+                         f"{ABI_VERSION}: rebuild the HIP library (__graft_entry__.build())")
     if path is None:
         _lib = lib
     return lib
@@ -129,9 +134,9 @@ class QTensor:
 
 
 def quant_params(rowwise=True, colwise=False, block2d=False, round_row=NVFP4_RNE,
-                 round_col=NVFP4_RNE, rht_row=False, rht_col=False, seed=0):
+                 round_col=NVFP4_RNE, rht_row=False, rht_col=False, seed=0, scale46=False):
     return QuantParams(int(rowwise), int(colwise), NVFP4_BLOCK_2D if block2d else NVFP4_BLOCK_1D,
-                       int(round_row), int(round_col), int(rht_row), int(rht_col),
+                       int(round_row), int(round_col), int(rht_row), int(rht_col), int(scale46),
                        int(seed) & 0xFFFFFFFFFFFFFFFF)
 
 

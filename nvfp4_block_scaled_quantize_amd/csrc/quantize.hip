@@ -92,6 +92,8 @@ extern "C" int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t co
         ((p->rowwise && (p->round_row != NVFP4_RNE || p->rht_row)) ||
          (p->colwise && (p->round_col != NVFP4_RNE || p->rht_col))))
         return NVFP4_ERR_MODE;
+    if ((p->scale46 != 0 && p->scale46 != 1) || (p->scale46 && p->block == NVFP4_BLOCK_2D))
+        return NVFP4_ERR_MODE;
     hipStream_t st = (hipStream_t)stream;
     if (rows == 0 || cols == 0) {  // nothing to encode; the tensor scale is 1
         if ((p->rowwise && (!row_out || !row_out->gscale)) ||
@@ -124,6 +126,7 @@ extern "C" int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t co
     a.sr_col = a.colwise && p->round_col == NVFP4_SR;
     a.rht_row = a.rowwise && p->rht_row != 0;
     a.rht_col = a.colwise && p->rht_col != 0;
+    a.scale46 = p->scale46 != 0;
     a.k0 = (uint32_t)p->seed;
     a.k1 = (uint32_t)(p->seed >> 32);
     a.rcodes = a.rowwise ? row_out->codes : nullptr;

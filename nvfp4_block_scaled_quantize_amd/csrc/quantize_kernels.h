@@ -35,6 +35,7 @@ struct QArgs {
     int is_bf16;
     int rowwise, colwise, block2d;
     int sr_row, sr_col, rht_row, rht_col;
+    int scale46;
     uint32_t k0, k1;
     uint8_t* rcodes;
     uint8_t* rscales;
@@ -204,6 +205,25 @@ __device__ __forceinline__ uint32_t encode8_sr(const float w[8], float rcp, cons
     return r;
 }
 
+// 4/6 adaptive block scaling: squared error of 8 values quantized nearest-even with scale
+// code sc, as the fma chain over the values in order of e_i^2, e_i = fma(-(v_i s), s_g, w_i)
+// (v_i the signed decoded code; v_i s is exact).  Also returns the 8 codes.
+__device__ __forceinline__ float sse8_rne(const float w[8], uint32_t sc, float sg, uint32_t& codes) {
+    const float s = e4m3_value(sc);
+    const float rcp = sc ? __fdiv_rn(1.0f, s * sg) : 0.0f;
+    codes = encode8_rne(w, rcp);
+    const float2v p[4] = {fp4x2_to_f32<0>(codes), fp4x2_to_f32<1>(codes), fp4x2_to_f32<2>(codes),
+                          fp4x2_to_f32<3>(codes)};
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float v = (i & 1) ? p[i >> 1].y : p[i >> 1].x;
+        const float e = __builtin_fmaf(-(v * s), sg, w[i]);
+        acc = __builtin_fmaf(e, e, acc);
+    }
+    return acc;
+}
+
 __device__ __forceinline__ float sg_from_amax(float amax) {
     float sg = __fdiv_rn(amax, 2688.0f);
     return sg == 0.0f ? 1.0f : sg;
@@ -259,7 +279,8 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) w[i] = v[i][j];
             if (RHT_COL) rht_col16(w, signs);
-            uint32_t scode;
+            uint32_t scode, rlo = 0, rhi = 0;
+            bool have = false;   // nearest-even codes already formed by the 4/6 choice
             if (a.block2d) {
                 scode = scode2d;
             } else {
@@ -267,13 +288,24 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(w[i]));
                 scode = e4m3_encode(__fdiv_rn(__fdiv_rn(am, 6.0f), sg_c));
+                if (a.scale46) {
+                    const uint32_t sc4 = e4m3_encode(__fdiv_rn(__fdiv_rn(am, 4.0f), sg_c));
+                    uint32_t l6, h6, l4, h4;
+                    const float e6 = sse8_rne(&w[0], scode, sg_c, l6) + sse8_rne(&w[8], scode, sg_c, h6);
+                    const float e4 = sse8_rne(&w[0], sc4, sg_c, l4) + sse8_rne(&w[8], sc4, sg_c, h4);
+                    const bool use4 = e4 < e6;
+                    scode = use4 ? sc4 : scode;
+                    rlo = use4 ? l4 : l6;
+                    rhi = use4 ? h4 : h6;
+                    have = true;
+                }
             }
             const float d = e4m3_value(scode) * sg_c;
             const float rcp = scode ? __fdiv_rn(1.0f, d) : 0.0f;
             uint32_t lo, hi;
             if (!SR_COL) {
-                lo = encode8_rne(&w[0], rcp);
-                hi = encode8_rne(&w[8], rcp);
+                lo = have ? rlo : encode8_rne(&w[0], rcp);
+                hi = have ? rhi : encode8_rne(&w[8], rcp);
             } else {
                 const uint64_t g = ((uint64_t)(c0 + j) * (uint64_t)a.rows + (uint64_t)r0) >> 3;
                 lo = encode8_sr(&w[0], rcp, sr_words(g, 1u, a.k0, a.k1));
@@ -293,7 +325,8 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) w[e] = v[i][e];
             if (RHT_ROW) rht_pair8(w, signs, pc & 1);
-            uint32_t scode;
+            uint32_t scode, rcodes = 0;
+            bool have = false;   // nearest-even codes already formed by the 4/6 choice
             if (a.block2d) {
                 scode = scode2d;
             } else {
@@ -302,12 +335,26 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
                 for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(w[e]));
                 am = fmaxf(am, __shfl_xor(am, 1, 64));
                 scode = e4m3_encode(__fdiv_rn(__fdiv_rn(am, 6.0f), sg_r));
+                if (a.scale46) {
+                    // the block's halves sit in this lane and lane ^ 1; a + b == b + a, so
+                    // both lanes form the same (elements 0..7) + (elements 8..15) sum
+                    const uint32_t sc4 = e4m3_encode(__fdiv_rn(__fdiv_rn(am, 4.0f), sg_r));
+                    uint32_t c6, c4;
+                    float e6 = sse8_rne(w, scode, sg_r, c6);
+                    float e4 = sse8_rne(w, sc4, sg_r, c4);
+                    e6 += __shfl_xor(e6, 1, 64);
+                    e4 += __shfl_xor(e4, 1, 64);
+                    const bool use4 = e4 < e6;
+                    scode = use4 ? sc4 : scode;
+                    rcodes = use4 ? c4 : c6;
+                    have = true;
+                }
             }
             const float d = e4m3_value(scode) * sg_r;
             const float rcp = scode ? __fdiv_rn(1.0f, d) : 0.0f;
             uint32_t codes;
             if (!SR_ROW) {
-                codes = encode8_rne(w, rcp);
+                codes = have ? rcodes : encode8_rne(w, rcp);
             } else {
                 const uint64_t g = ((uint64_t)(r0 + i) * (uint64_t)a.cols + (uint64_t)c0) >> 3;
                 codes = encode8_sr(w, rcp, sr_words(g, 0u, a.k0, a.k1));

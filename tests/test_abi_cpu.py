@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(nv):
 
 def test_version_and_status_strings(nv):
     lib = nv.load_library()
-    assert lib.nvfp4_abi_version() == 1
+    assert lib.nvfp4_abi_version() == nv.ABI_VERSION == 2
     assert lib.nvfp4_status_string(0) == b"ok"
     for code in range(-7, 0):
         s = lib.nvfp4_status_string(code)
@@ -92,8 +92,10 @@ def test_quantize_argument_errors(nv):
     assert need > 0
     assert call(x, 1, 32, 32, 32, ctypes.byref(p), ctypes.byref(q), None, ws, need - 1, None) == -6
     assert call(x, 1, 32, 32, 32, ctypes.byref(p), ctypes.byref(q), None, None, need, None) == -6
-    # modes: no copy, bad enums, 2D with SR or RHT
+    # modes: no copy, bad enums, 2D with SR, RHT or 4/6 scaling
     for bad in [nv.quant_params(rowwise=False, colwise=False),
+                nv.QuantParams(1, 0, 0, 0, 0, 0, 0, 2),
+                nv.quant_params(block2d=True, scale46=True),
                 nv.QuantParams(1, 0, 5, 0, 0, 0, 0, 0),
                 nv.QuantParams(1, 0, 0, 3, 0, 0, 0, 0),
                 nv.quant_params(block2d=True, round_row=nv.NVFP4_SR),

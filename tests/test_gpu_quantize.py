@@ -50,6 +50,13 @@ MODES = {
     "rht_row": dict(rowwise=True, rht_row=True),
     "dgrad_and_wgrad": dict(rowwise=True, colwise=True, round_row=1, round_col=1, rht_col=True),
     "all": dict(rowwise=True, colwise=True, round_row=1, round_col=1, rht_row=True, rht_col=True),
+    # 4/6 adaptive block scaling (1x16 blocks)
+    "46_row": dict(rowwise=True, scale46=True),
+    "46_rowcol": dict(rowwise=True, colwise=True, scale46=True),
+    "46_sr_rhtcol": dict(rowwise=True, colwise=True, round_row=1, round_col=1, rht_col=True,
+                         scale46=True),
+    "46_all": dict(rowwise=True, colwise=True, round_row=1, round_col=1, rht_row=True,
+                   rht_col=True, scale46=True),
 }
 SHAPES = [(16, 16), (48, 80), (128, 256), (272, 400), (528, 144)]
 
@@ -65,7 +72,7 @@ def run_case(nv, oracle, x, mode, seed):
                                  block2d=kw.get("block2d", False),
                                  round_row=kw.get("round_row", 0), round_col=kw.get("round_col", 0),
                                  rht_row=kw.get("rht_row", False), rht_col=kw.get("rht_col", False),
-                                 seed=seed)
+                                 seed=seed, scale46=kw.get("scale46", False))
     if orow is not None:
         assert_copy_equal(gr, orow, f"{mode} rowwise")
     if ocol is not None:
@@ -152,6 +159,26 @@ def test_full_size_activation_rowcol(nv, oracle):
     from nvfp4_block_scaled_quantize_amd import synthetic
     x = synthetic.ffn()["X"]                    # 8192 x 3072 bf16, outlier channels
     run_case(nv, oracle, x, "rowcol", 0)
+
+
+def test_full_size_activation_scale46(nv, oracle):
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    x = synthetic.ffn()["X"]                    # 8192 x 3072 bf16, outlier channels
+    gr, _, orow, _ = run_case(nv, oracle, x, "46_rowcol", 0)
+    s46 = (orow.scales != oracle.quantize(x.float().numpy())[0].scales).mean()
+    assert 0.05 < s46 < 0.95                    # both candidates occur at full size
+
+
+def test_full_size_gradient_scale46_sr(nv, oracle):
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    t = synthetic.wgrad()                       # dY 8192 x 9216, Student-t entries
+    run_case(nv, oracle, t["dY"], "46_sr_rhtcol", synthetic.RHT_SEED_WGRAD)
+
+
+def test_scale46_refused_with_2d_blocks(nv):
+    x = torch.zeros((32, 32), dtype=torch.bfloat16, device=dev())
+    with pytest.raises(nv.Nvfp4Error):
+        nv.nvfp4_quantize(x, nv.quant_params(block2d=True, scale46=True))
 
 
 def test_full_size_weight_2d(nv, oracle):
