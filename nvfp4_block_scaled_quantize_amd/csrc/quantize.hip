@@ -137,6 +137,14 @@ extern "C" int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t co
     a.csg = a.colwise ? col_out->gscale : nullptr;
     a.partial = (float*)ws;
     a.ntiles = (int)quant_tiles(rows, cols, &a.tiles_c);
+    {   // k_amax: one wave per 16 x 512 wave tile, four per workgroup, at most about one
+        // round of resident workgroups (each then loops), never more than ntiles
+        const int64_t wtiles = (rows / 16) * ((cols + kAmaxWaveCols - 1) / kAmaxWaveCols);
+        int64_t np = (wtiles + 3) / 4;
+        if (np > 768) np = 768;
+        if (np > a.ntiles) np = a.ntiles;
+        a.npart = (int)(np > 0 ? np : 1);
+    }
     const int f = a.sr_row | (a.sr_col << 1) | (a.rht_row << 2) | (a.rht_col << 3);
     if (a.is_bf16)
         (f < 8 ? launch_quant_bf16_lo : launch_quant_bf16_hi)(f, a, st);

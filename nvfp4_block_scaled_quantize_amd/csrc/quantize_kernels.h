@@ -43,9 +43,10 @@ struct QArgs {
     uint8_t* ccodes;
     uint8_t* cscales;
     float* csg;
-    float* partial;  // [2][ntiles]: rowwise-copy and columnwise-copy amax per tile
+    float* partial;  // [2][npart]: rowwise-copy and columnwise-copy amax per k_amax workgroup
     int tiles_c;
     int ntiles;
+    int npart;       // k_amax workgroups (<= ntiles)
 };
 
 template <bool BF16>
@@ -130,21 +131,12 @@ __device__ __forceinline__ void block_max2(float& a, float& b, float* red) {
     b = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
 }
 
-// Specialised on the input dtype and the Hadamard flags (bit 0: rowwise copy, bit 1:
-// columnwise copy) so that each variant keeps its 16x8 patch in registers.
-template <bool BF16, int H>
-__global__ __launch_bounds__(kThreads) void k_amax(QArgs a) {
-    constexpr bool RHT_ROW = H & 1, RHT_COL = (H >> 1) & 1;
-    __shared__ float red[8];
-    const int t = threadIdx.x, pc = t & 15, pr = t >> 4;
-    const int tile_r = blockIdx.x / a.tiles_c, tile_c = blockIdx.x % a.tiles_c;
-    const int64_t r0 = (int64_t)tile_r * kTileRows + pr * 16;
-    const int64_t c0 = (int64_t)tile_c * kTileCols + pc * 8;
-    const bool valid = r0 < a.rows && c0 < a.cols;
-    float v[16][8];
-    load_patch<BF16>(a, r0, c0, valid, v);
-    const uint32_t signs = (RHT_ROW || RHT_COL) ? rht_sign_bits(a.k0, a.k1) : 0u;
-
+// Amax of one 16x8 patch for the rowwise and the columnwise copy (each plain or after its
+// Hadamard transform).  The rowwise transform pairs this lane with lane ^ 1 (positions 8..15
+// of the 16-chunk when this lane's column is a multiple of 16).
+template <bool RHT_ROW, bool RHT_COL>
+__device__ __forceinline__ void patch_amax(const QArgs& a, float v[16][8], uint32_t signs, int half,
+                                           float& mr, float& mc) {
     float plain = 0.0f, arow = 0.0f, acol = 0.0f;
     if ((a.rowwise && !RHT_ROW) || (a.colwise && !RHT_COL)) {
 #pragma unroll
@@ -158,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(QArgs a) {
             float w[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) w[e] = v[i][e];
-            rht_pair8(w, signs, pc & 1);
+            rht_pair8(w, signs, half);
 #pragma unroll
             for (int e = 0; e < 8; ++e) arow = fmaxf(arow, fabsf(w[e]));
         }
@@ -174,12 +166,34 @@ __global__ __launch_bounds__(kThreads) void k_amax(QArgs a) {
             for (int i = 0; i < 16; ++i) acol = fmaxf(acol, fabsf(w[i]));
         }
     }
-    float mr = RHT_ROW ? arow : plain;
-    float mc = RHT_COL ? acol : plain;
+    mr = fmaxf(mr, RHT_ROW ? arow : plain);
+    mc = fmaxf(mc, RHT_COL ? acol : plain);
+}
+
+constexpr int kAmaxWaveCols = 512;   // columns of a k_amax wave tile (64 lanes x 8)
+
+// Specialised on the input dtype and the Hadamard flags (bit 0: rowwise copy, bit 1:
+// columnwise copy) so that each variant keeps its 16x8 patch in registers.
+template <bool BF16, int H>
+__global__ __launch_bounds__(kThreads) void k_amax(QArgs a) {
+    constexpr bool RHT_ROW = H & 1, RHT_COL = (H >> 1) & 1;
+    __shared__ float red[8];
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const uint32_t signs = (RHT_ROW || RHT_COL) ? rht_sign_bits(a.k0, a.k1) : 0u;
+    const int64_t wcols = (a.cols + kAmaxWaveCols - 1) / kAmaxWaveCols;
+    const int64_t nwt = (a.rows / 16) * wcols;
+    float mr = 0.0f, mc = 0.0f;
+    for (int64_t w = (int64_t)blockIdx.x * 4 + wid; w < nwt; w += (int64_t)gridDim.x * 4) {
+        const int64_t r0 = (w / wcols) * 16;
+        const int64_t c0 = (w % wcols) * kAmaxWaveCols + lane * 8;
+        float v[16][8];
+        load_patch<BF16>(a, r0, c0, c0 < a.cols, v);
+        patch_amax<RHT_ROW, RHT_COL>(a, v, signs, lane & 1, mr, mc);
+    }
     block_max2(mr, mc, red);
     if (t == 0) {
         a.partial[blockIdx.x] = mr;
-        a.partial[a.ntiles + blockIdx.x] = mc;
+        a.partial[a.npart + blockIdx.x] = mc;
     }
 }
 
@@ -246,9 +260,9 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
 
     // tensor scales from the per-tile partial maxima
     float mr = 0.0f, mc = 0.0f;
-    for (int i = t; i < a.ntiles; i += kThreads) {
+    for (int i = t; i < a.npart; i += kThreads) {
         mr = fmaxf(mr, a.partial[i]);
-        mc = fmaxf(mc, a.partial[a.ntiles + i]);
+        mc = fmaxf(mc, a.partial[a.npart + i]);
     }
     block_max2(mr, mc, red);
     const float sg_r = sg_from_amax(mr), sg_c = sg_from_amax(mc);
@@ -384,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
 
 template <bool BF16, int F>
 void launch_quant(const QArgs& a, hipStream_t st) {
-    k_amax<BF16, (F >> 2)><<<a.ntiles, kThreads, 0, st>>>(a);
+    k_amax<BF16, (F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
     k_encode<BF16, F><<<a.ntiles, kThreads, 0, st>>>(a);
 }
 
