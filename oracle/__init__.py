@@ -64,6 +64,8 @@ def _load():
         "or_qadamw_v_encode": (ctypes.c_int, [P, i64, i64, u64, ctypes.c_int, P, P, P, P]),
         "or_qadamw_v_decode": (ctypes.c_int, [P, P, P, f32, i64, i64, u64, ctypes.c_int, P]),
         "or_num_threads": (ctypes.c_int, []),
+        "or_qadamw_step": (ctypes.c_int, [P, P, i64, i64, P, P, f32, P, P, P, f32, P, u64, u64, u64,
+                                          ctypes.c_int, P, P, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -264,3 +266,32 @@ def unpack_codes(codes):
     lo = codes & 0x0F
     hi = codes >> 4
     return np.stack([lo, hi], axis=-1).reshape(codes.shape[0], codes.shape[1] * 2)
+
+
+def qadamw_step(w, g, m, mu, v, hp, m_rht_seed, m_sr_seed, v_seed, v_use_signs=True):
+    """One quantized-state AdamW step (see or_qadamw_step).  w, g: float32 [R][C]; m: the
+    moment state (QTensor of the rotated first moment); mu, v: the second-moment state.
+    hp = dict(lr, beta1, beta2, eps, weight_decay, grad_coef, bias1, bias2).
+    Returns (w_new, m_state, mu_new, v_state, m_new_f32, v_new_f32)."""
+    w = np.array(w, dtype=np.float32, copy=True)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    R, C = w.shape
+    h = np.array([hp[k] for k in ("lr", "beta1", "beta2", "eps", "weight_decay", "grad_coef",
+                                  "bias1", "bias2")], dtype=np.float32)
+    mc = np.zeros((R, C // 2), dtype=np.uint8)
+    ms = np.zeros((R, C // 16), dtype=np.uint8)
+    vc = np.zeros((R, C // 2), dtype=np.uint8)
+    vs = np.zeros((R, C // 16), dtype=np.uint8)
+    mu_out = np.zeros((R // 16, C // 16), dtype=np.uint16)
+    msg, vsg = ctypes.c_float(0.0), ctypes.c_float(0.0)
+    m_new = np.zeros((R, C), dtype=np.float32)
+    v_new = np.zeros((R, C), dtype=np.float32)
+    rc = _load().or_qadamw_step(_ptr(w), _ptr(g), R, C,
+                                _ptr(np.ascontiguousarray(m.codes)), _ptr(np.ascontiguousarray(m.scales)), m.sg,
+                                _ptr(np.ascontiguousarray(mu, dtype=np.uint16)),
+                                _ptr(np.ascontiguousarray(v.codes)), _ptr(np.ascontiguousarray(v.scales)), v.sg,
+                                _ptr(h), int(m_rht_seed), int(m_sr_seed), int(v_seed), int(v_use_signs),
+                                _ptr(mc), _ptr(ms), ctypes.byref(msg), _ptr(mu_out), _ptr(vc), _ptr(vs),
+                                ctypes.byref(vsg), _ptr(m_new), _ptr(v_new))
+    _check(rc, "qadamw_step")
+    return w, QTensor(mc, ms, msg.value), mu_out, QTensor(vc, vs, vsg.value), m_new, v_new

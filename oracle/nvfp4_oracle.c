@@ -528,6 +528,71 @@ int or_qadamw_v_decode(const uint16_t* mu, const uint8_t* codes, const uint8_t* 
     return 0;
 }
 
+/* ------------------------------------------------------------------------- */
+/* Quantized-state AdamW step.  [FS4] sec. 2 (preliminaries) gives the moments  */
+/* m_t = beta1 m_{t-1} + g_t and v_t = beta2 v_{t-1} + (1 - beta2) g_t^2; sec.   */
+/* 3.3 stores m_t through a Hadamard rotation, stochastic rounding and 4/6       */
+/* scaling, and v_t through the sqrt / tile-mean / Hadamard / NVFP4 pipeline.   */
+/* The update itself is not printed.  Readings: the gradient        */
+/* coefficient of m is a parameter (1 in the pages' form, 1 - beta1 in the      */
+/* common one); the update is decoupled AdamW with caller-supplied bias          */
+/* multipliers, w <- w - lr (bias1 m / (sqrt(bias2 v) + eps) + wd w); the m      */
+/* rotation uses random signs from a seed that stays with the state, and the    */
+/* stochastic rounding a fresh seed per step.  Every elementwise operation is   */
+/* one binary32 rounding in the order written below.                           */
+/* hp = {lr, beta1, beta2, eps, weight_decay, grad_coef, bias1, bias2}.          */
+/* ------------------------------------------------------------------------- */
+int or_qadamw_step(float* w, const float* g, int64_t R, int64_t C,
+                   const uint8_t* m_codes, const uint8_t* m_scales, float m_sg,
+                   const uint16_t* mu, const uint8_t* v_codes, const uint8_t* v_scales, float v_sg,
+                   const float* hp, uint64_t m_rht_seed, uint64_t m_sr_seed, uint64_t v_seed,
+                   int v_use_signs,
+                   uint8_t* m_codes_out, uint8_t* m_scales_out, float* m_sg_out,
+                   uint16_t* mu_out, uint8_t* v_codes_out, uint8_t* v_scales_out, float* v_sg_out,
+                   float* m_new_out, float* v_new_out)
+{
+    if (R < 0 || C < 0 || R % 16 != 0 || C % 16 != 0) return -2;
+    size_t n = (size_t)(R * C > 0 ? R * C : 1);
+    float* mp = (float*)malloc(sizeof(float) * n);
+    float* vp = (float*)malloc(sizeof(float) * n);
+    float* y = (float*)malloc(sizeof(float) * n);
+    if (!mp || !vp || !y) { free(mp); free(vp); free(y); return -9; }
+    int rc = or_dequantize(m_codes, m_scales, m_sg, R, C, mp);
+    if (!rc) rc = or_qadamw_v_decode(mu, v_codes, v_scales, v_sg, R, C, v_seed, v_use_signs, vp);
+    if (rc) { free(mp); free(vp); free(y); return rc; }
+    float sgn[16];
+    or_rht_signs(m_rht_seed, sgn);
+    for (int64_t i = 0; i < R * C; i += 16) or_rht16_inverse(&mp[i], sgn);
+
+    const float lr = hp[0], b1 = hp[1], b2 = hp[2], eps = hp[3], wd = hp[4], cg = hp[5];
+    const float bias1 = hp[6], bias2 = hp[7];
+    const float omb2 = 1.0f - b2;
+    for (int64_t i = 0; i < R * C; ++i) {
+        const float gi = g[i];
+        const float m = b1 * mp[i] + cg * gi;
+        const float v = b2 * vp[i] + omb2 * (gi * gi);
+        const float den = sqrtf(bias2 * v) + eps;
+        const float upd = (bias1 * m) / den + wd * w[i];
+        w[i] = w[i] - lr * upd;
+        mp[i] = m;
+        vp[i] = v;
+    }
+    if (m_new_out) memcpy(m_new_out, mp, sizeof(float) * (size_t)(R * C));
+    if (v_new_out) memcpy(v_new_out, vp, sizeof(float) * (size_t)(R * C));
+    /* m: rotate each 1x16 chunk, then NVFP4 1x16 with 4/6 scaling and stochastic rounding */
+    memcpy(y, mp, sizeof(float) * (size_t)(R * C));
+    for (int64_t i = 0; i < R * C; i += 16) or_rht16_forward(&y[i], sgn);
+    memset(m_codes_out, 0, (size_t)(R * (C / 2)));
+    quantize_core(y, R, C, 0, 1, 1, m_sr_seed, 0, m_codes_out, m_scales_out, m_sg_out);
+    /* v: the Q-AdamW second-moment pipeline */
+    rc = or_qadamw_v_encode(vp, R, C, v_seed, v_use_signs, mu_out, v_codes_out, v_scales_out,
+                            v_sg_out);
+    free(mp);
+    free(vp);
+    free(y);
+    return rc;
+}
+
 int or_num_threads(void)
 {
 #ifdef _OPENMP

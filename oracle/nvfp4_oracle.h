@@ -105,6 +105,20 @@ int or_qadamw_v_decode(const uint16_t* mu, const uint8_t* codes, const uint8_t* 
                        float* v_out);
 
 /* Number of OpenMP threads the oracle runs with (1 without OpenMP). */
+/* Quantized-state AdamW step (reading in nvfp4_oracle.c): decodes m (NVFP4 1x16 of the
+ * Hadamard-rotated moment) and v (second-moment pipeline), updates the moments and the
+ * FP32 weights w in place, re-encodes m (rotation, 4/6, stochastic rounding with
+ * m_sr_seed) and v.  hp = {lr, beta1, beta2, eps, weight_decay, grad_coef, bias1, bias2}.
+ * m_new_out / v_new_out (may be NULL) receive the updated moments before encoding. */
+int or_qadamw_step(float* w, const float* g, int64_t R, int64_t C,
+                   const uint8_t* m_codes, const uint8_t* m_scales, float m_sg,
+                   const uint16_t* mu, const uint8_t* v_codes, const uint8_t* v_scales, float v_sg,
+                   const float* hp, uint64_t m_rht_seed, uint64_t m_sr_seed, uint64_t v_seed,
+                   int v_use_signs,
+                   uint8_t* m_codes_out, uint8_t* m_scales_out, float* m_sg_out,
+                   uint16_t* mu_out, uint8_t* v_codes_out, uint8_t* v_scales_out, float* v_sg_out,
+                   float* m_new_out, float* v_new_out);
+
 int or_num_threads(void);
 
 #ifdef __cplusplus
