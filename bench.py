@@ -65,13 +65,14 @@ SOURCES = {
     "quant": ["quantize.hip", "quantize_kernels.h", "quantize_launch_bf16_lo.hip",
               "quantize_launch_bf16_hi.hip", "quantize_launch_f32_lo.hip",
               "quantize_launch_f32_hi.hip", "device_common.h"],
-    "qadamw": ["qadamw.hip", "device_common.h"],
+    "qadamw": ["qadamw.hip", "quantize_kernels.h", "device_common.h"],
 }
 FAMILY = {"gemm": "gemm", "quant": "quant", "qadamw_encode": "qadamw", "qadamw_decode": "qadamw",
-          "dequant": "quant"}
+          "qadamw_step": "qadamw", "dequant": "quant"}
 # kernels each call of the step launches, in order (name prefixes; '?' marks optional)
 CALL_KERNELS = {"quant": ["?k_amax", "k_encode|k_quant"], "gemm": ["k_gemm"],
                 "qadamw_encode": ["k_qv_pass1", "k_qv_pass2"], "qadamw_decode": ["k_qv_decode"],
+                "qadamw_step": ["k_qs_pass1", "k_qs_pass2"],
                 "dequant": ["k_dequant"]}
 
 
@@ -79,7 +80,7 @@ STEP_ORDER = [("quant_X_row+colRHT", "quant"), ("quant_Wup_2d", "quant"), ("gemm
               ("quant_H_row", "quant"), ("quant_Wdown_2d", "quant"), ("gemm_ffn_down", "gemm"),
               ("quant_dY_rowSR+colRHTSR", "quant"), ("gemm_dgrad", "gemm"), ("gemm_wgrad", "gemm"),
               ("qadamw_encode", "qadamw_encode"), ("qadamw_decode", "qadamw_decode"),
-              ("dequant_Wup", "dequant")]
+              ("qadamw_step_Wup", "qadamw_step"), ("dequant_Wup", "dequant")]
 
 
 def split_step(names):
@@ -273,6 +274,22 @@ def main():
                        device=dev)
     v_out = torch.empty_like(v)
     w_dec = torch.empty((FFN, HIDDEN), dtype=torch.float32, device=dev)
+    # full Q-AdamW step on W_up: fp32 master weights, bf16 gradient, states out of place
+    w_master = W_up.float()
+    g_up = synthetic.normal((FFN, HIDDEN), SEED_QADAMW + 1, 1e-3).to(torch.bfloat16).to(dev)
+    p_step = nv.qadamw_step_params(1.5e-4, 0.9, 0.95, 1e-8, 0.1, 1.0, 1 / (1 - 0.9 ** 10),
+                                   1 / (1 - 0.95 ** 10), m_rht_seed=SEED_WGRAD, m_sr_seed=SEED_WGRAD + 1,
+                                   v_seed=SEED_QADAMW, v_use_signs=True)
+    ws_step = torch.empty(max(nv.qadamw_step_workspace_bytes(FFN, HIDDEN), 16), dtype=torch.uint8,
+                          device=dev)
+    z = nv.QTensor(torch.zeros((FFN, HIDDEN // 2), dtype=torch.uint8, device=dev),
+                   torch.zeros((FFN, HIDDEN // 16), dtype=torch.uint8, device=dev),
+                   torch.ones((1,), device=dev))
+    zmu = torch.zeros((FFN // 16, HIDDEN // 16), dtype=torch.int16, device=dev)
+    # one step from the zero state gives the (non-trivial) states every timed step reads
+    st_m, st_mu, st_v = nv.qadamw_step(w_master, g_up, z, zmu, z, p_step, workspace=ws_step)
+    st_m2, st_mu2, st_v2 = (nv.QTensor.empty(FFN, HIDDEN, dev), torch.empty_like(zmu),
+                            nv.QTensor.empty(FFN, HIDDEN, dev))
 
     # name -> (kind, algorithmic bytes, flops)
     work = {
@@ -291,6 +308,9 @@ def main():
                        2 * FFN * HIDDEN * TOKENS),
         "qadamw_encode": ("quant", 4 * FFN * HIDDEN + qbytes(FFN, HIDDEN) + FFN * HIDDEN // 128, 0),
         "qadamw_decode": ("quant", qbytes(FFN, HIDDEN) + FFN * HIDDEN // 128 + 4 * FFN * HIDDEN, 0),
+        # g bf16 in, w f32 in and out, both states in and out
+        "qadamw_step_Wup": ("quant", 2 * FFN * HIDDEN + 8 * FFN * HIDDEN
+                            + 2 * (2 * qbytes(FFN, HIDDEN) + FFN * HIDDEN // 128), 0),
         "dequant_Wup": ("quant", qbytes(FFN, HIDDEN) + 4 * FFN * HIDDEN, 0),
     }
 
@@ -306,6 +326,8 @@ def main():
         yield "gemm_wgrad", lambda: nv.nvfp4_gemm(qdy[1], qx[1], out=dW)
         yield "qadamw_encode", lambda: nv.qadamw_v_encode(v, SEED_QADAMW, True, mu, qv, ws_v)
         yield "qadamw_decode", lambda: nv.qadamw_v_decode(mu, qv, SEED_QADAMW, True, out=v_out)
+        yield "qadamw_step_Wup", lambda: nv.qadamw_step(w_master, g_up, st_m, st_mu, st_v, p_step,
+                                                        st_m2, st_mu2, st_v2, ws_step)
         yield "dequant_Wup", lambda: nv.nvfp4_dequantize(qw[0], out=w_dec)
 
     stream = torch.cuda.current_stream(dev)

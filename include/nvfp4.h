@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 2
+#define NVFP4_ABI_VERSION 3
 
 enum nvfp4_status {
     NVFP4_OK = 0,
@@ -173,6 +173,42 @@ int qadamw_v_encode(const float* v, int64_t rows, int64_t cols, uint64_t seed, i
  * use_signs must match the encode call. */
 int qadamw_v_decode(const uint16_t* mu, const nvfp4_qtensor* q, int64_t rows, int64_t cols,
                     uint64_t seed, int32_t use_signs, float* v_out, void* stream);
+
+/* Quantized-state AdamW step (Full-Stack FP4 sec. 2: m = beta1 m + c g,
+ * v = beta2 v + (1 - beta2) g^2; sec. 3.3: m stored through a Hadamard rotation, 4/6
+ * scaling and stochastic rounding, v through the qadamw_v pipeline; the update, not printed
+ * there, is read as decoupled AdamW):
+ *   m = beta1 m_old + grad_coef g;  v = beta2 v_old + (1 - beta2) g^2;
+ *   w = w - lr (bias1 m / (sqrt(bias2 v) + eps) + weight_decay w)
+ * each operation one binary32 rounding in this order (the division correctly rounded).
+ *   grad_coef      1 in the pages' form of m, 1 - beta1 in the common one
+ *   bias1, bias2   bias-correction multipliers, e.g. 1/(1 - beta^t), or 1
+ *   m_rht_seed     signs of m's 1x16 Hadamard rotation; fixed for the life of the state
+ *   m_sr_seed      stochastic rounding of the new m; fresh each step
+ *   v_seed, v_use_signs   as qadamw_v_encode; fixed for the life of the state */
+typedef struct {
+    float lr, beta1, beta2, eps, weight_decay, grad_coef, bias1, bias2;
+    uint64_t m_rht_seed, m_sr_seed, v_seed;
+    int32_t v_use_signs;
+} qadamw_step_params;
+
+/* Device workspace (bytes) qadamw_step needs. */
+size_t qadamw_step_workspace_bytes(int64_t rows, int64_t cols);
+
+/* One step on a rows x cols parameter (multiples of 16).
+ *   w        f32 [rows][cols] master weights, updated in place, 16-byte aligned
+ *   g        gradient, f32 or bf16 per g_dtype, [rows][cols], 16-byte aligned
+ *   m_in     first-moment state: NVFP4 1x16 copy of the rotated m (codes, scales, s_g)
+ *   m_out    the new first-moment state (same layout); must not overlap m_in
+ *   mu_in, v_in    second-moment state as written by qadamw_v_encode
+ *   mu_out, v_out  the new second-moment state; must not overlap mu_in, v_in
+ *   ws       workspace of at least qadamw_step_workspace_bytes() bytes, 16-byte aligned
+ * A zero state (all codes and scales 0, tile means 0, any s_g) decodes to m = v = 0. */
+int qadamw_step(float* w, const void* g, int g_dtype, int64_t rows, int64_t cols,
+                const nvfp4_qtensor* m_in, const nvfp4_qtensor* m_out,
+                const uint16_t* mu_in, const nvfp4_qtensor* v_in, uint16_t* mu_out,
+                const nvfp4_qtensor* v_out, const qadamw_step_params* p, void* ws,
+                size_t ws_bytes, void* stream);
 
 /* Static string naming a status code. */
 const char* nvfp4_status_string(int status);

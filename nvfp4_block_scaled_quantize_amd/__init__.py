@@ -29,7 +29,8 @@ NVFP4_BLOCK_1D, NVFP4_BLOCK_2D = 0, 1
 
 EXPORTED = ["nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantize",
             "nvfp4_gemm", "qadamw_v_workspace_bytes", "qadamw_v_encode", "qadamw_v_decode",
-            "nvfp4_status_string", "nvfp4_abi_version"]
+            "nvfp4_status_string", "nvfp4_abi_version", "qadamw_step_workspace_bytes",
+            "qadamw_step"]
 
 
 class Nvfp4Error(RuntimeError):
@@ -44,13 +45,21 @@ class QuantParams(ctypes.Structure):
                 ("seed", ctypes.c_uint64)]
 
 
+class QAdamWStepParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("grad_coef", ctypes.c_float), ("bias1", ctypes.c_float), ("bias2", ctypes.c_float),
+                ("m_rht_seed", ctypes.c_uint64), ("m_sr_seed", ctypes.c_uint64),
+                ("v_seed", ctypes.c_uint64), ("v_use_signs", ctypes.c_int32)]
+
+
 class QTensorC(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("gscale", ctypes.c_void_p)]
 
 
 _lib = None
-ABI_VERSION = 2   # NVFP4_ABI_VERSION of include/nvfp4.h this binding matches
+ABI_VERSION = 3   # NVFP4_ABI_VERSION of include/nvfp4.h this binding matches
 
 
 def load_library(path: Optional[str] = None):
@@ -80,6 +89,11 @@ def load_library(path: Optional[str] = None):
     lib.qadamw_v_encode.argtypes = [vp, i64, i64, u64, i32, vp, P(QTensorC), vp, sz, vp]
     lib.qadamw_v_decode.restype = ctypes.c_int
     lib.qadamw_v_decode.argtypes = [vp, P(QTensorC), i64, i64, u64, i32, vp, vp]
+    lib.qadamw_step_workspace_bytes.restype = sz
+    lib.qadamw_step_workspace_bytes.argtypes = [i64, i64]
+    lib.qadamw_step.restype = ctypes.c_int
+    lib.qadamw_step.argtypes = [vp, vp, ctypes.c_int, i64, i64, P(QTensorC), P(QTensorC), vp,
+                                P(QTensorC), vp, P(QTensorC), P(QAdamWStepParams), vp, sz, vp]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     lib.nvfp4_status_string.argtypes = [ctypes.c_int]
     lib.nvfp4_abi_version.restype = ctypes.c_int
@@ -205,6 +219,38 @@ def nvfp4_gemm(a, b, out=None):
     _check(lib.nvfp4_gemm(ctypes.byref(ac), ctypes.byref(bc), M, N, K, _ptr(out), out.stride(0),
                           _stream(out.device)))
     return out
+
+
+def qadamw_step_params(lr, beta1, beta2, eps, weight_decay, grad_coef=1.0, bias1=1.0, bias2=1.0,
+                       m_rht_seed=0, m_sr_seed=0, v_seed=0, v_use_signs=True):
+    return QAdamWStepParams(lr, beta1, beta2, eps, weight_decay, grad_coef, bias1, bias2,
+                            int(m_rht_seed) & 0xFFFFFFFFFFFFFFFF, int(m_sr_seed) & 0xFFFFFFFFFFFFFFFF,
+                            int(v_seed) & 0xFFFFFFFFFFFFFFFF, int(v_use_signs))
+
+
+def qadamw_step(w, g, m, mu, v, params, m_out=None, mu_out=None, v_out=None, workspace=None):
+    """One quantized-state AdamW step: updates w (f32, in place) and returns the new states
+    (m_out, mu_out, v_out), allocated here unless passed (they must not alias the inputs)."""
+    lib = load_library()
+    _require_cuda(w, g)
+    if w.dtype != torch.float32 or not w.is_contiguous() or w.dim() != 2:
+        raise Nvfp4Error("w must be a contiguous 2-D float32 tensor")
+    if g.shape != w.shape or not g.is_contiguous() or g.dtype not in (torch.float32, torch.bfloat16):
+        raise Nvfp4Error("g must be a contiguous float32/bfloat16 tensor shaped like w")
+    R, C = w.shape
+    d = w.device
+    m_out = m_out if m_out is not None else QTensor.empty(R, C, d)
+    v_out = v_out if v_out is not None else QTensor.empty(R, C, d)
+    mu_out = mu_out if mu_out is not None else torch.empty((R // 16, C // 16), dtype=torch.int16, device=d)
+    if workspace is None:
+        workspace = torch.empty(max(int(lib.qadamw_step_workspace_bytes(R, C)), 16),
+                                dtype=torch.uint8, device=d)
+    dt = NVFP4_BF16 if g.dtype == torch.bfloat16 else NVFP4_F32
+    mi, mo, vi, vo = m.c(), m_out.c(), v.c(), v_out.c()
+    _check(lib.qadamw_step(_ptr(w), _ptr(g), dt, R, C, ctypes.byref(mi), ctypes.byref(mo), _ptr(mu),
+                           ctypes.byref(vi), _ptr(mu_out), ctypes.byref(vo), ctypes.byref(params),
+                           _ptr(workspace), workspace.numel(), _stream(d)))
+    return m_out, mu_out, v_out
 
 
 def qadamw_v_workspace_bytes(rows, cols):

@@ -17,6 +17,7 @@
 // workgroup of the second pass).
 #include "nvfp4.h"
 #include "device_common.h"
+#include "quantize_kernels.h"   // encode8_rne, encode8_sr, sse8_rne (the quantizer's block encoders)
 
 namespace nvfp4 {
 
@@ -48,22 +49,10 @@ __device__ __forceinline__ float tree16_row(const float y[16]) {
     return w[0] + w[1];
 }
 
-// Square roots of one 1x16 row segment, the tile mean (bf16 bits), and the transformed
-// residual.  All 64 lanes must call it (cross-lane shuffles).
-__device__ __forceinline__ uint32_t residual_block(const QVArgs& a, int64_t r, int64_t c,
-                                                   bool valid, uint32_t signs, float e[16]) {
-    float y[16];
-    if (valid) {
-        const float4* p = (const float4*)(a.v + r * a.cols + c);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            float4 f = p[q];
-            y[4 * q] = f.x; y[4 * q + 1] = f.y; y[4 * q + 2] = f.z; y[4 * q + 3] = f.w;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) y[i] = 0.0f;
-    }
+// Square roots of one 1x16 row segment y (in place), the tile mean (bf16 bits) and the
+// transformed residual e.  The 16 lanes 16k .. 16k+15 hold the rows of one 16x16 tile.
+// All 64 lanes must call it (cross-lane shuffles).
+__device__ __forceinline__ uint32_t residual_from(float y[16], uint32_t signs, float e[16]) {
     // sqrtf lowers to the correctly rounded square root on gfx950 (checked against IEEE
     // sqrt on 4M log-normal and subnormal inputs); __fsqrt_rn is not, so it is avoided.
 #pragma unroll
@@ -81,6 +70,23 @@ __device__ __forceinline__ uint32_t residual_block(const QVArgs& a, int64_t r, i
 #pragma unroll
     for (int i = 0; i < 16; ++i) e[i] = e[i] * 0.25f;
     return mu;
+}
+
+__device__ __forceinline__ uint32_t residual_block(const QVArgs& a, int64_t r, int64_t c,
+                                                   bool valid, uint32_t signs, float e[16]) {
+    float y[16];
+    if (valid) {
+        const float4* p = (const float4*)(a.v + r * a.cols + c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float4 f = p[q];
+            y[4 * q] = f.x; y[4 * q + 1] = f.y; y[4 * q + 2] = f.z; y[4 * q + 3] = f.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] = 0.0f;
+    }
+    return residual_from(y, signs, e);
 }
 
 __device__ __forceinline__ void qv_coords(const QVArgs& a, int64_t& r, int64_t& c, bool& valid) {
@@ -192,6 +198,215 @@ __global__ __launch_bounds__(QVThreads) void k_qv_decode(const uint16_t* mu, con
     for (int q = 0; q < 4; ++q) p[q] = make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
 }
 
+// ---------------------------------------------------------------- full AdamW step
+// Full-Stack FP4 sec. 2 (moments m = beta1 m + c g, v = beta2 v + (1 - beta2) g^2) and sec.
+// 3.3 (m stored through a Hadamard rotation, 4/6 scaling and stochastic rounding; v through
+// the pipeline above); decoupled AdamW update w -= lr (bias1 m / (sqrt(bias2 v) + eps) +
+// wd w).  Same lane layout as the v kernels (one lane = one 1x16 row block of a 16x16 tile).
+// The new s_g of m and of v need the amax of the whole new states, so it is two passes:
+// pass 1 forms the moments and their partial maxima (and writes the new tile means);
+// pass 2 forms them again, bit for bit, and encodes, and updates w.  The states are read
+// from m_in/v_in and written to m_out/v_out, which therefore must not alias.
+struct QSArgs {
+    float* w;
+    const void* g;
+    int g_bf16;
+    int64_t rows, cols;
+    const uint8_t* mc; const uint8_t* ms; const float* msg;     // m in
+    uint8_t* mco; uint8_t* mso; float* msgo;                     // m out
+    const uint16_t* mu; const uint8_t* vc; const uint8_t* vs; const float* vsg;  // v in
+    uint16_t* muo; uint8_t* vco; uint8_t* vso; float* vsgo;      // v out
+    float lr, b1, b2, eps, wd, cg, bias1, bias2;
+    uint32_t mk0, mk1, sk0, sk1, vk0, vk1;
+    int v_use_signs;
+    float* partial;   // [2][nblocks]: m and v residual maxima per workgroup
+    int tiles_c, nblocks;
+};
+
+// Decode 16 codes of a row block: (v s) s_g, then the inverse transform D (1/4 H16 x).
+__device__ __forceinline__ void decode_rot16(const uint8_t* codes, const uint8_t* scales, float sg,
+                                             int64_t r, int64_t c, int64_t cols, uint32_t signs,
+                                             float x[16]) {
+    const uint2 cw = *(const uint2*)(codes + r * (cols / 2) + c / 2);
+    const float s = e4m3_value(scales[r * (cols / 16) + c / 16]);
+    const uint32_t w2[2] = {cw.x, cw.y};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float2v p0 = fp4x2_to_f32<0>(w2[h]), p1 = fp4x2_to_f32<1>(w2[h]);
+        const float2v p2 = fp4x2_to_f32<2>(w2[h]), p3 = fp4x2_to_f32<3>(w2[h]);
+        x[8 * h + 0] = p0.x; x[8 * h + 1] = p0.y; x[8 * h + 2] = p1.x; x[8 * h + 3] = p1.y;
+        x[8 * h + 4] = p2.x; x[8 * h + 5] = p2.y; x[8 * h + 6] = p3.x; x[8 * h + 7] = p3.y;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = (x[i] * s) * sg;
+    wht16(x);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = apply_sign(x[i] * 0.25f, signs, i);
+}
+
+// New moments of one row block (zeros for lanes outside the tensor).
+__device__ __forceinline__ void qs_moments(const QSArgs& a, int64_t r, int64_t c, bool valid,
+                                           uint32_t msigns, uint32_t vsigns, float m[16], float v[16]) {
+    if (!valid) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { m[i] = 0.0f; v[i] = 0.0f; }
+        return;
+    }
+    float mp[16], vp[16], g[16];
+    decode_rot16(a.mc, a.ms, *a.msg, r, c, a.cols, msigns, mp);
+    decode_rot16(a.vc, a.vs, *a.vsg, r, c, a.cols, vsigns, vp);
+    const float muf = bf16_to_f32(a.mu[(r / 16) * (a.cols / 16) + c / 16]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float z = vp[i] + muf;
+        vp[i] = z * z;
+    }
+    if (a.g_bf16) {
+        const uint4* p = (const uint4*)((const uint16_t*)a.g + r * a.cols + c);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint4 u = p[q];
+            const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                g[8 * q + 2 * k] = __uint_as_float(ww[k] << 16);
+                g[8 * q + 2 * k + 1] = __uint_as_float(ww[k] & 0xFFFF0000u);
+            }
+        }
+    } else {
+        const float4* p = (const float4*)((const float*)a.g + r * a.cols + c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 f = p[q];
+            g[4 * q] = f.x; g[4 * q + 1] = f.y; g[4 * q + 2] = f.z; g[4 * q + 3] = f.w;
+        }
+    }
+    const float omb2 = 1.0f - a.b2;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        m[i] = a.b1 * mp[i] + a.cg * g[i];
+        v[i] = a.b2 * vp[i] + omb2 * (g[i] * g[i]);
+    }
+}
+
+// The rotated first moment y = 1/4 H16 (D m).
+__device__ __forceinline__ void rot16(const float m[16], uint32_t signs, float y[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = apply_sign(m[i], signs, i);
+    wht16(y);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = y[i] * 0.25f;
+}
+
+__device__ __forceinline__ void qs_coords(const QSArgs& a, int64_t& r, int64_t& c, bool& valid) {
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int br = blockIdx.x / a.tiles_c, bc = blockIdx.x % a.tiles_c;
+    r = (int64_t)br * 16 + (lane & 15);
+    c = (int64_t)bc * QVCols + (wid * 4 + (lane >> 4)) * 16;
+    valid = r < a.rows && c < a.cols;
+}
+
+__global__ __launch_bounds__(QVThreads) void k_qs_pass1(QSArgs a) {
+    __shared__ float red[8];
+    int64_t r, c;
+    bool valid;
+    qs_coords(a, r, c, valid);
+    const uint32_t msigns = rht_sign_bits(a.mk0, a.mk1);
+    const uint32_t vsigns = a.v_use_signs ? rht_sign_bits(a.vk0, a.vk1) : 0u;
+    float m[16], v[16], y[16], e[16];
+    qs_moments(a, r, c, valid, msigns, vsigns, m, v);
+    rot16(m, msigns, y);
+    const uint32_t mu = residual_from(v, vsigns, e);
+    float am = 0.0f, av = 0.0f;
+    if (valid) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { am = fmaxf(am, fabsf(y[i])); av = fmaxf(av, fabsf(e[i])); }
+        if ((threadIdx.x & 15) == 0) a.muo[(r / 16) * (a.cols / 16) + c / 16] = (uint16_t)mu;
+    }
+    block_max2(am, av, red);
+    if (threadIdx.x == 0) {
+        a.partial[blockIdx.x] = am;
+        a.partial[a.nblocks + blockIdx.x] = av;
+    }
+}
+
+__global__ __launch_bounds__(QVThreads) void k_qs_pass2(QSArgs a) {
+    __shared__ float red[8];
+    float am = 0.0f, av = 0.0f;
+    for (int i = threadIdx.x; i < a.nblocks; i += QVThreads) {
+        am = fmaxf(am, a.partial[i]);
+        av = fmaxf(av, a.partial[a.nblocks + i]);
+    }
+    block_max2(am, av, red);
+    const float sgm = sg_from_amax(am), sgv = sg_from_amax(av);
+    if (blockIdx.x == 0 && threadIdx.x == 0) { *a.msgo = sgm; *a.vsgo = sgv; }
+
+    int64_t r, c;
+    bool valid;
+    qs_coords(a, r, c, valid);
+    const uint32_t msigns = rht_sign_bits(a.mk0, a.mk1);
+    const uint32_t vsigns = a.v_use_signs ? rht_sign_bits(a.vk0, a.vk1) : 0u;
+    float m[16], v[16], y[16], e[16];
+    qs_moments(a, r, c, valid, msigns, vsigns, m, v);
+
+    // weights
+    if (valid) {
+        float4* pw = (float4*)(a.w + r * a.cols + c);
+        float w[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 f = pw[q];
+            w[4 * q] = f.x; w[4 * q + 1] = f.y; w[4 * q + 2] = f.z; w[4 * q + 3] = f.w;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float den = sqrtf(a.bias2 * v[i]) + a.eps;
+            const float upd = __fdiv_rn(a.bias1 * m[i], den) + a.wd * w[i];
+            w[i] = w[i] - a.lr * upd;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pw[q] = make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+    }
+
+    // m: rotated, 1x16 blocks with 4/6 scaling, stochastic rounding
+    rot16(m, msigns, y);
+    {
+        float bm = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(y[i]));
+        uint32_t sc = e4m3_encode(__fdiv_rn(__fdiv_rn(bm, 6.0f), sgm));
+        const uint32_t sc4 = e4m3_encode(__fdiv_rn(__fdiv_rn(bm, 4.0f), sgm));
+        uint32_t t0, t1, t2, t3;
+        const float e6 = sse8_rne(&y[0], sc, sgm, t0) + sse8_rne(&y[8], sc, sgm, t1);
+        const float e4 = sse8_rne(&y[0], sc4, sgm, t2) + sse8_rne(&y[8], sc4, sgm, t3);
+        sc = e4 < e6 ? sc4 : sc;
+        const float d = e4m3_value(sc) * sgm;
+        const float rcp = sc ? __fdiv_rn(1.0f, d) : 0.0f;
+        const uint64_t g0 = ((uint64_t)r * (uint64_t)a.cols + (uint64_t)c) >> 3;
+        const uint32_t lo = encode8_sr(&y[0], rcp, sr_words(g0, 0u, a.sk0, a.sk1));
+        const uint32_t hi = encode8_sr(&y[8], rcp, sr_words(g0 + 1, 0u, a.sk0, a.sk1));
+        if (valid) {
+            *(uint2*)(a.mco + r * (a.cols / 2) + c / 2) = make_uint2(lo, hi);
+            a.mso[r * (a.cols / 16) + c / 16] = (uint8_t)sc;
+        }
+    }
+    // v: the second-moment pipeline, nearest-even
+    residual_from(v, vsigns, e);
+    {
+        float bm = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(e[i]));
+        const uint32_t sc = e4m3_encode(__fdiv_rn(__fdiv_rn(bm, 6.0f), sgv));
+        const float d = e4m3_value(sc) * sgv;
+        const float rcp = sc ? __fdiv_rn(1.0f, d) : 0.0f;
+        const uint32_t lo = encode8_rne(&e[0], rcp), hi = encode8_rne(&e[8], rcp);
+        if (valid) {
+            *(uint2*)(a.vco + r * (a.cols / 2) + c / 2) = make_uint2(lo, hi);
+            a.vso[r * (a.cols / 16) + c / 16] = (uint8_t)sc;
+        }
+    }
+}
+
 }  // namespace nvfp4
 
 using namespace nvfp4;
@@ -247,5 +462,55 @@ extern "C" int qadamw_v_decode(const uint16_t* mu, const nvfp4_qtensor* q, int64
     k_qv_decode<<<(unsigned)((blocks + 255) / 256), 256, 0, (hipStream_t)stream>>>(
         mu, q->codes, q->scales, q->gscale, rows, cols, (uint32_t)seed, (uint32_t)(seed >> 32),
         use_signs != 0, v_out);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+extern "C" size_t qadamw_step_workspace_bytes(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return (size_t)qv_blocks(rows, cols, nullptr) * 2 * sizeof(float);
+}
+
+extern "C" int qadamw_step(float* w, const void* g, int g_dtype, int64_t rows, int64_t cols,
+                           const nvfp4_qtensor* m_in, const nvfp4_qtensor* m_out,
+                           const uint16_t* mu_in, const nvfp4_qtensor* v_in, uint16_t* mu_out,
+                           const nvfp4_qtensor* v_out, const qadamw_step_params* p, void* ws,
+                           size_t ws_bytes, void* stream) {
+    if (!p || !m_in || !m_out || !v_in || !v_out) return NVFP4_ERR_NULL;
+    if (g_dtype != NVFP4_F32 && g_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+    if (rows < 0 || cols < 0 || rows % 16 || cols % 16) return NVFP4_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return NVFP4_OK;
+    const nvfp4_qtensor* qs[4] = {m_in, m_out, v_in, v_out};
+    for (const nvfp4_qtensor* q : qs) {
+        if (!q->codes || !q->scales || !q->gscale) return NVFP4_ERR_NULL;
+        if (((uintptr_t)q->codes & 7) || ((uintptr_t)q->gscale & 3)) return NVFP4_ERR_ALIGN;
+    }
+    if (!w || !g || !mu_in || !mu_out) return NVFP4_ERR_NULL;
+    if (((uintptr_t)w & 15) || ((uintptr_t)g & 15) || ((uintptr_t)mu_in & 1) || ((uintptr_t)mu_out & 1))
+        return NVFP4_ERR_ALIGN;
+    // the states are read by both passes: outputs must not overlap the inputs
+    if (m_out->codes == m_in->codes || m_out->scales == m_in->scales || v_out->codes == v_in->codes ||
+        v_out->scales == v_in->scales || mu_out == mu_in || m_out->gscale == m_in->gscale ||
+        v_out->gscale == v_in->gscale)
+        return NVFP4_ERR_MODE;
+    const size_t need = qadamw_step_workspace_bytes(rows, cols);
+    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if ((uintptr_t)ws & 15) return NVFP4_ERR_ALIGN;
+    QSArgs a;
+    a.w = w; a.g = g; a.g_bf16 = g_dtype == NVFP4_BF16; a.rows = rows; a.cols = cols;
+    a.mc = m_in->codes; a.ms = m_in->scales; a.msg = m_in->gscale;
+    a.mco = m_out->codes; a.mso = m_out->scales; a.msgo = m_out->gscale;
+    a.mu = mu_in; a.vc = v_in->codes; a.vs = v_in->scales; a.vsg = v_in->gscale;
+    a.muo = mu_out; a.vco = v_out->codes; a.vso = v_out->scales; a.vsgo = v_out->gscale;
+    a.lr = p->lr; a.b1 = p->beta1; a.b2 = p->beta2; a.eps = p->eps; a.wd = p->weight_decay;
+    a.cg = p->grad_coef; a.bias1 = p->bias1; a.bias2 = p->bias2;
+    a.mk0 = (uint32_t)p->m_rht_seed; a.mk1 = (uint32_t)(p->m_rht_seed >> 32);
+    a.sk0 = (uint32_t)p->m_sr_seed; a.sk1 = (uint32_t)(p->m_sr_seed >> 32);
+    a.vk0 = (uint32_t)p->v_seed; a.vk1 = (uint32_t)(p->v_seed >> 32);
+    a.v_use_signs = p->v_use_signs != 0;
+    a.partial = (float*)ws;
+    a.nblocks = (int)qv_blocks(rows, cols, &a.tiles_c);
+    hipStream_t st = (hipStream_t)stream;
+    k_qs_pass1<<<a.nblocks, QVThreads, 0, st>>>(a);
+    k_qs_pass2<<<a.nblocks, QVThreads, 0, st>>>(a);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
