@@ -84,10 +84,11 @@ STEP_ORDER = [("quant_X_row+colRHT", "quant"), ("quant_Wup_2d", "quant"), ("gemm
 
 
 def split_step(names):
-    """Assign a step's dispatch names (our kernels only, in order) to the step's calls;
-    returns [(key, [dispatch indices])] per call, repeated for as many steps as present."""
-    out, i = [], 0
-    while i < len(names):
+    """Assign dispatch names (our kernels only, in order) to the step's calls; returns
+    [(key, [dispatch indices])] per call, for every whole step present.  Set-up launches
+    before the first step and the extra measurements after the last are skipped."""
+    def one_step(i):
+        got = []
         for key, kind in STEP_ORDER:
             idx = []
             for pat in CALL_KERNELS[kind]:
@@ -96,9 +97,22 @@ def split_step(names):
                     idx.append(i)
                     i += 1
                 elif not pat.startswith("?"):
-                    raise SystemExit(f"dispatch {i} ({names[i] if i < len(names) else 'none'}) "
-                                     f"does not match {pat} for {key}")
-            out.append((key, idx))
+                    return None, i
+            got.append((key, idx))
+        return got, i
+
+    out, i = [], 0
+    while i < len(names):
+        got, j = one_step(i)
+        if got is None:
+            if out:
+                break
+            i += 1
+            continue
+        out += got
+        i = j
+    if not out:
+        raise SystemExit("no whole step found in the dispatch list")
     return out
 
 

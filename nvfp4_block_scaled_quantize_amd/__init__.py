@@ -228,6 +228,10 @@ def qadamw_step_params(lr, beta1, beta2, eps, weight_decay, grad_coef=1.0, bias1
                             int(v_seed) & 0xFFFFFFFFFFFFFFFF, int(v_use_signs))
 
 
+def qadamw_step_workspace_bytes(rows, cols):
+    return int(load_library().qadamw_step_workspace_bytes(rows, cols))
+
+
 def qadamw_step(w, g, m, mu, v, params, m_out=None, mu_out=None, v_out=None, workspace=None):
     """One quantized-state AdamW step: updates w (f32, in place) and returns the new states
     (m_out, mu_out, v_out), allocated here unless passed (they must not alias the inputs)."""
@@ -243,7 +247,7 @@ def qadamw_step(w, g, m, mu, v, params, m_out=None, mu_out=None, v_out=None, wor
     v_out = v_out if v_out is not None else QTensor.empty(R, C, d)
     mu_out = mu_out if mu_out is not None else torch.empty((R // 16, C // 16), dtype=torch.int16, device=d)
     if workspace is None:
-        workspace = torch.empty(max(int(lib.qadamw_step_workspace_bytes(R, C)), 16),
+        workspace = torch.empty(max(qadamw_step_workspace_bytes(R, C), 16),
                                 dtype=torch.uint8, device=d)
     dt = NVFP4_BF16 if g.dtype == torch.bfloat16 else NVFP4_F32
     mi, mo, vi, vo = m.c(), m_out.c(), v.c(), v_out.c()

@@ -157,6 +157,22 @@ __device__ __forceinline__ void static_for(Fn&& f) {
     }
 }
 
+// The value held by lane ^ 1 (a DPP quad permutation [1,0,3,2]: no LDS traffic).
+__device__ __forceinline__ float xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+// Correctly rounded a / b from r_b = RN(1 / b) (Markstein's correction: q = RN(a r_b) is
+// within one ulp, the residual a - q b is exact in one fma, and RN(q + residual * r_b) is
+// the correctly rounded quotient while no operand, quotient or residual is subnormal).
+// Checked on the host: over every positive binary32 a for b = 6 and b = 4 (all normal
+// quotients agree), and over 10^9 random pairs with b >= 2^-92 and a / b in [2^-12, 2^10].
+__device__ __forceinline__ float div_rn_by(float a, float b, float rb) {
+    const float q = a * rb;
+    const float r = __builtin_fmaf(-q, b, a);
+    return __builtin_fmaf(r, rb, q);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -49,41 +49,74 @@ struct QArgs {
     int npart;       // k_amax workgroups (<= ntiles)
 };
 
-template <bool BF16>
-__device__ __forceinline__ void load_patch(const QArgs& a, int64_t r0, int64_t c0, bool valid,
-                                           float v[16][8]) {
-    if (!valid) {
+// One thread's 16-row x 8-column input patch.  bfloat16 stays packed two to a register
+// (64 VGPRs rather than 128) and is widened where it is used: a bfloat16 is the upper
+// half of the binary32 with the same value.
+template <bool BF16> struct Patch;
+
+template <> struct Patch<true> {
+    uint32_t p[16][4];
+    __device__ __forceinline__ void load(const void* x, int64_t ld, int64_t r0, int64_t c0, bool valid) {
+        if (!valid) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+#pragma unroll
+                for (int h = 0; h < 4; ++h) p[i][h] = 0u;
+            return;
+        }
+        const uint16_t* src = (const uint16_t*)x + r0 * ld + c0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint4 q = *(const uint4*)(src + (int64_t)i * ld);
+            p[i][0] = q.x; p[i][1] = q.y; p[i][2] = q.z; p[i][3] = q.w;
+        }
+    }
+    __device__ __forceinline__ float at(int i, int e) const {
+        return __uint_as_float((e & 1) ? (p[i][e >> 1] & 0xFFFF0000u) : (p[i][e >> 1] << 16));
+    }
+    // max |x| over the patch: on the packed bits with the signs cleared, two at a time
+    // (sign-magnitude bit patterns order like the magnitudes)
+    __device__ __forceinline__ float amax() const {
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+        u16x2 m = {0, 0};
 #pragma unroll
         for (int i = 0; i < 16; ++i)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
-        return;
+            for (int h = 0; h < 4; ++h)
+                m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, p[i][h] & 0x7FFF7FFFu));
+        return fmaxf(__uint_as_float((uint32_t)m.x << 16), __uint_as_float((uint32_t)m.y << 16));
     }
-    if (BF16) {
-        const uint16_t* p = (const uint16_t*)a.x + r0 * a.ld + c0;
-        uint4 q[16];
+};
+
+template <> struct Patch<false> {
+    float p[16][8];
+    __device__ __forceinline__ void load(const void* x, int64_t ld, int64_t r0, int64_t c0, bool valid) {
+        if (!valid) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) q[i] = *(const uint4*)(p + (int64_t)i * a.ld);
+            for (int i = 0; i < 16; ++i)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) p[i][e] = 0.0f;
+            return;
+        }
+        const float* src = (const float*)x + r0 * ld + c0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            uint32_t w[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                v[i][2 * h] = __uint_as_float(w[h] << 16);
-                v[i][2 * h + 1] = __uint_as_float(w[h] & 0xFFFF0000u);
-            }
-        }
-    } else {
-        const float* p = (const float*)a.x + r0 * a.ld + c0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float4 q0 = *(const float4*)(p + (int64_t)i * a.ld);
-            float4 q1 = *(const float4*)(p + (int64_t)i * a.ld + 4);
-            v[i][0] = q0.x; v[i][1] = q0.y; v[i][2] = q0.z; v[i][3] = q0.w;
-            v[i][4] = q1.x; v[i][5] = q1.y; v[i][6] = q1.z; v[i][7] = q1.w;
+            const float4 q0 = *(const float4*)(src + (int64_t)i * ld);
+            const float4 q1 = *(const float4*)(src + (int64_t)i * ld + 4);
+            p[i][0] = q0.x; p[i][1] = q0.y; p[i][2] = q0.z; p[i][3] = q0.w;
+            p[i][4] = q1.x; p[i][5] = q1.y; p[i][6] = q1.z; p[i][7] = q1.w;
         }
     }
-}
+    __device__ __forceinline__ float at(int i, int e) const { return p[i][e]; }
+    __device__ __forceinline__ float amax() const {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(p[i][e]));
+        return m;
+    }
+};
 
 // Random Hadamard transform of one 16-chunk held as 8 values per lane in a lane pair
 // (lane with half = 0 holds positions 0..7, its neighbour positions 8..15).  Stages 1,
@@ -104,7 +137,7 @@ __device__ __forceinline__ void rht_pair8(float w[8], uint32_t signs, int half) 
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        float p = __shfl_xor(w[e], 1, 64);
+        float p = xor1(w[e]);
         w[e] = half ? (p - w[e]) : (w[e] + p);
     }
 #pragma unroll
@@ -134,22 +167,17 @@ __device__ __forceinline__ void block_max2(float& a, float& b, float* red) {
 // Amax of one 16x8 patch for the rowwise and the columnwise copy (each plain or after its
 // Hadamard transform).  The rowwise transform pairs this lane with lane ^ 1 (positions 8..15
 // of the 16-chunk when this lane's column is a multiple of 16).
-template <bool RHT_ROW, bool RHT_COL>
-__device__ __forceinline__ void patch_amax(const QArgs& a, float v[16][8], uint32_t signs, int half,
-                                           float& mr, float& mc) {
+template <bool BF16, bool RHT_ROW, bool RHT_COL>
+__device__ __forceinline__ void patch_amax(const QArgs& a, const Patch<BF16>& P, uint32_t signs,
+                                           int half, float& mr, float& mc) {
     float plain = 0.0f, arow = 0.0f, acol = 0.0f;
-    if ((a.rowwise && !RHT_ROW) || (a.colwise && !RHT_COL)) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) plain = fmaxf(plain, fabsf(v[i][e]));
-    }
+    if ((a.rowwise && !RHT_ROW) || (a.colwise && !RHT_COL)) plain = P.amax();
     if (RHT_ROW) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             float w[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] = v[i][e];
+            for (int e = 0; e < 8; ++e) w[e] = P.at(i, e);
             rht_pair8(w, signs, half);
 #pragma unroll
             for (int e = 0; e < 8; ++e) arow = fmaxf(arow, fabsf(w[e]));
@@ -160,7 +188,7 @@ __device__ __forceinline__ void patch_amax(const QArgs& a, float v[16][8], uint3
         for (int j = 0; j < 8; ++j) {
             float w[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) w[i] = v[i][j];
+            for (int i = 0; i < 16; ++i) w[i] = P.at(i, j);
             rht_col16(w, signs);
 #pragma unroll
             for (int i = 0; i < 16; ++i) acol = fmaxf(acol, fabsf(w[i]));
@@ -186,9 +214,9 @@ __global__ __launch_bounds__(kThreads) void k_amax(QArgs a) {
     for (int64_t w = (int64_t)blockIdx.x * 4 + wid; w < nwt; w += (int64_t)gridDim.x * 4) {
         const int64_t r0 = (w / wcols) * 16;
         const int64_t c0 = (w % wcols) * kAmaxWaveCols + lane * 8;
-        float v[16][8];
-        load_patch<BF16>(a, r0, c0, c0 < a.cols, v);
-        patch_amax<RHT_ROW, RHT_COL>(a, v, signs, lane & 1, mr, mc);
+        Patch<BF16> P;
+        P.load(a.x, a.ld, r0, c0, c0 < a.cols);
+        patch_amax<BF16, RHT_ROW, RHT_COL>(a, P, signs, lane & 1, mr, mc);
     }
     block_max2(mr, mc, red);
     if (t == 0) {
@@ -219,12 +247,12 @@ __device__ __forceinline__ uint32_t encode8_sr(const float w[8], float rcp, cons
     return r;
 }
 
-// 4/6 adaptive block scaling: squared error of 8 values quantized nearest-even with scale
-// code sc, as the fma chain over the values in order of e_i^2, e_i = fma(-(v_i s), s_g, w_i)
-// (v_i the signed decoded code; v_i s is exact).  Also returns the 8 codes.
-__device__ __forceinline__ float sse8_rne(const float w[8], uint32_t sc, float sg, uint32_t& codes) {
-    const float s = e4m3_value(sc);
-    const float rcp = sc ? __fdiv_rn(1.0f, s * sg) : 0.0f;
+// 4/6 adaptive block scaling: squared error of 8 values quantized nearest-even with block
+// scale s (reciprocal rcp = RN(1 / fl(s s_g))), as the fma chain over the values in order of
+// e_i^2, e_i = fma(-(v_i s), s_g, w_i) (v_i the signed decoded code; v_i s is exact).  Also
+// returns the 8 codes.
+__device__ __forceinline__ float sse8_rne(const float w[8], float s, float rcp, float sg,
+                                          uint32_t& codes) {
     codes = encode8_rne(w, rcp);
     const float2v p[4] = {fp4x2_to_f32<0>(codes), fp4x2_to_f32<1>(codes), fp4x2_to_f32<2>(codes),
                           fp4x2_to_f32<3>(codes)};
@@ -238,9 +266,44 @@ __device__ __forceinline__ float sse8_rne(const float w[8], uint32_t sc, float s
     return acc;
 }
 
+// The same with the scale given as its E4M3 code.
+__device__ __forceinline__ float sse8_rne(const float w[8], uint32_t sc, float sg, uint32_t& codes) {
+    const float s = e4m3_value(sc);
+    return sse8_rne(w, s, sc ? __fdiv_rn(1.0f, s * sg) : 0.0f, sg, codes);
+}
+
 __device__ __forceinline__ float sg_from_amax(float amax) {
     float sg = __fdiv_rn(amax, 2688.0f);
     return sg == 0.0f ? 1.0f : sg;
+}
+
+constexpr float kRcp6 = 1.0f / 6.0f;     // RN(1/6)
+
+// Block-scale arithmetic of one copy for one call.  The code of a block with amax am is
+// E4M3(fl(fl(am / k) / s_g)) (k = 6, or 4 for the 4/6 candidate), its element reciprocal
+// RN(1 / fl(E4M3 value * s_g)), both exactly as the definitions read:
+//  * the two divisions go through div_rn_by when s_g >= 2^-92 (the tensor amax is at
+//    least about 2^-80.6).  Then every block whose code can be nonzero has normal
+//    operands and quotients, where the corrected division is exact; blocks with quotients
+//    below 2^-12 get code 0 either way.  Smaller tensor scales take the plain divisions;
+//  * the reciprocal of each of the 128 codes is computed once per workgroup into LDS.
+struct CopyScale {
+    float sg, rsg;
+    bool fast;
+    const float* rtab;
+    __device__ __forceinline__ uint32_t code(float am, float k, float rk) const {
+        float z;
+        if (fast)
+            z = div_rn_by(div_rn_by(am, k, rk), sg, rsg);
+        else
+            z = __fdiv_rn(__fdiv_rn(am, k), sg);
+        return e4m3_encode(z);
+    }
+    __device__ __forceinline__ float rcp(uint32_t c) const { return rtab[c]; }
+};
+
+__device__ __forceinline__ float uniform_f(float v) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
 
 // Specialised on the input dtype and on F: bit 0 rowwise SR, bit 1 columnwise SR,
@@ -251,12 +314,17 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
     constexpr bool RHT_ROW = (F >> 2) & 1, RHT_COL = (F >> 3) & 1;
     __shared__ uint2 ccodes_lds[kTileCols][16];           // [column][16-row slot], slot ^ (column/8)
     __shared__ uint8_t cscales_lds[kTileCols * 17];       // [column][slot], stride 17
+    __shared__ float rtab[2][128];                        // element reciprocal per scale code
     __shared__ float red[8];
     const int t = threadIdx.x, pc = t & 15, pr = t >> 4;
     const int tile_r = blockIdx.x / a.tiles_c, tile_c = blockIdx.x % a.tiles_c;
     const int64_t r0 = (int64_t)tile_r * kTileRows + pr * 16;
     const int64_t c0 = (int64_t)tile_c * kTileCols + pc * 8;
     const bool valid = r0 < a.rows && c0 < a.cols;
+
+    // the patch loads go out first and land while the tensor scales are formed
+    Patch<BF16> P;
+    P.load(a.x, a.ld, r0, c0, valid);
 
     // tensor scales from the per-tile partial maxima
     float mr = 0.0f, mc = 0.0f;
@@ -265,25 +333,26 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
         mc = fmaxf(mc, a.partial[a.npart + i]);
     }
     block_max2(mr, mc, red);
-    const float sg_r = sg_from_amax(mr), sg_c = sg_from_amax(mc);
+    const float sg_r = uniform_f(sg_from_amax(mr)), sg_c = uniform_f(sg_from_amax(mc));
     if (blockIdx.x == 0 && t == 0) {
         if (a.rowwise) *a.rsg = sg_r;
         if (a.colwise) *a.csg = sg_c;
     }
-
-    float v[16][8];
-    load_patch<BF16>(a, r0, c0, valid, v);
+    if (t < 128) {
+        const float s = e4m3_value(t);
+        rtab[0][t] = t ? __fdiv_rn(1.0f, s * sg_r) : 0.0f;
+        rtab[1][t] = t ? __fdiv_rn(1.0f, s * sg_c) : 0.0f;
+    }
+    __syncthreads();
+    const CopyScale rsc{sg_r, __fdiv_rn(1.0f, sg_r), sg_r >= 0x1p-92f, rtab[0]};
+    const CopyScale csc{sg_c, __fdiv_rn(1.0f, sg_c), sg_c >= 0x1p-92f, rtab[1]};
     const uint32_t signs = (RHT_ROW || RHT_COL) ? rht_sign_bits(a.k0, a.k1) : 0u;
 
     uint32_t scode2d = 0;
     if (a.block2d) {  // one scale per 16x16 tile = this patch and its neighbour's
-        float am = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(v[i][e]));
-        am = fmaxf(am, __shfl_xor(am, 1, 64));
-        scode2d = e4m3_encode(__fdiv_rn(__fdiv_rn(am, 6.0f), sg_r));
+        float am = P.amax();
+        am = fmaxf(am, xor1(am));
+        scode2d = rsc.code(am, 6.0f, kRcp6);
     }
 
     if (a.colwise) {
@@ -291,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
             constexpr int j = decltype(J)::value;
             float w[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) w[i] = v[i][j];
+            for (int i = 0; i < 16; ++i) w[i] = P.at(i, j);
             if (RHT_COL) rht_col16(w, signs);
             uint32_t scode, rlo = 0, rhi = 0;
             bool have = false;   // nearest-even codes already formed by the 4/6 choice
@@ -301,12 +370,14 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
                 float am = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(w[i]));
-                scode = e4m3_encode(__fdiv_rn(__fdiv_rn(am, 6.0f), sg_c));
+                scode = csc.code(am, 6.0f, kRcp6);
                 if (a.scale46) {
-                    const uint32_t sc4 = e4m3_encode(__fdiv_rn(__fdiv_rn(am, 4.0f), sg_c));
+                    const uint32_t sc4 = csc.code(am, 4.0f, 0.25f);
+                    const float s6 = e4m3_value(scode), s4 = e4m3_value(sc4);
+                    const float q6 = csc.rcp(scode), q4 = csc.rcp(sc4);
                     uint32_t l6, h6, l4, h4;
-                    const float e6 = sse8_rne(&w[0], scode, sg_c, l6) + sse8_rne(&w[8], scode, sg_c, h6);
-                    const float e4 = sse8_rne(&w[0], sc4, sg_c, l4) + sse8_rne(&w[8], sc4, sg_c, h4);
+                    const float e6 = sse8_rne(&w[0], s6, q6, sg_c, l6) + sse8_rne(&w[8], s6, q6, sg_c, h6);
+                    const float e4 = sse8_rne(&w[0], s4, q4, sg_c, l4) + sse8_rne(&w[8], s4, q4, sg_c, h4);
                     const bool use4 = e4 < e6;
                     scode = use4 ? sc4 : scode;
                     rlo = use4 ? l4 : l6;
@@ -314,8 +385,7 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
                     have = true;
                 }
             }
-            const float d = e4m3_value(scode) * sg_c;
-            const float rcp = scode ? __fdiv_rn(1.0f, d) : 0.0f;
+            const float rcp = csc.rcp(scode);
             uint32_t lo, hi;
             if (!SR_COL) {
                 lo = have ? rlo : encode8_rne(&w[0], rcp);
@@ -337,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
             constexpr int i = decltype(I)::value;
             float w[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] = v[i][e];
+            for (int e = 0; e < 8; ++e) w[e] = P.at(i, e);
             if (RHT_ROW) rht_pair8(w, signs, pc & 1);
             uint32_t scode, rcodes = 0;
             bool have = false;   // nearest-even codes already formed by the 4/6 choice
@@ -347,25 +417,24 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
                 float am = 0.0f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(w[e]));
-                am = fmaxf(am, __shfl_xor(am, 1, 64));
-                scode = e4m3_encode(__fdiv_rn(__fdiv_rn(am, 6.0f), sg_r));
+                am = fmaxf(am, xor1(am));
+                scode = rsc.code(am, 6.0f, kRcp6);
                 if (a.scale46) {
                     // the block's halves sit in this lane and lane ^ 1; a + b == b + a, so
                     // both lanes form the same (elements 0..7) + (elements 8..15) sum
-                    const uint32_t sc4 = e4m3_encode(__fdiv_rn(__fdiv_rn(am, 4.0f), sg_r));
+                    const uint32_t sc4 = rsc.code(am, 4.0f, 0.25f);
                     uint32_t c6, c4;
-                    float e6 = sse8_rne(w, scode, sg_r, c6);
-                    float e4 = sse8_rne(w, sc4, sg_r, c4);
-                    e6 += __shfl_xor(e6, 1, 64);
-                    e4 += __shfl_xor(e4, 1, 64);
+                    float e6 = sse8_rne(w, e4m3_value(scode), rsc.rcp(scode), sg_r, c6);
+                    float e4 = sse8_rne(w, e4m3_value(sc4), rsc.rcp(sc4), sg_r, c4);
+                    e6 += xor1(e6);
+                    e4 += xor1(e4);
                     const bool use4 = e4 < e6;
                     scode = use4 ? sc4 : scode;
                     rcodes = use4 ? c4 : c6;
                     have = true;
                 }
             }
-            const float d = e4m3_value(scode) * sg_r;
-            const float rcp = scode ? __fdiv_rn(1.0f, d) : 0.0f;
+            const float rcp = rsc.rcp(scode);
             uint32_t codes;
             if (!SR_ROW) {
                 codes = have ? rcodes : encode8_rne(w, rcp);
