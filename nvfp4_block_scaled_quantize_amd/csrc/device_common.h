@@ -66,16 +66,20 @@ __device__ __forceinline__ float apply_sign(float v, uint32_t bits, int i) {
 }
 
 // ---------------------------------------------------------------- E4M3 block scale
-// Nearest-even with saturation at 448 for s >= 0 (NaN -> 0), without branches: the
-// subnormal candidate (step 2^-9) and the normal one (mantissa rounded to 3 bits, ties
-// to even, exponent rebiased 127 -> 7) are both formed and one is selected.
+// Nearest-even E4M3 code with saturation at 448 for finite s >= 0: gfx950's OCP FP8
+// conversion of min(s, 448).  It equals nearest-even rounding to the E4M3 "fn" grid for
+// every non-negative finite binary32 (an exhaustive GPU test compares it with a plain
+// search over the grid).
 __device__ __forceinline__ uint32_t e4m3_encode(float s) {
-    const uint32_t sub = (uint32_t)rintf(fminf(s, 1.0f) * 512.0f);   // exact scaling
-    uint32_t b = __float_as_uint(s);
-    b = b + 0x7FFFFu + ((b >> 20) & 1u);
-    uint32_t c = s < 0.015625f ? sub : (b >> 20) - 960u;              // 2^-6: smallest normal
-    c = s >= 448.0f ? 0x7Eu : c;
-    return s == s ? c : 0u;
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(s, 448.0f), 0.0f, 0, false) & 0xFFu;
+}
+
+// The codes of two scales from one conversion.
+__device__ __forceinline__ void e4m3_encode2(float s0, float s1, uint32_t& c0, uint32_t& c1) {
+    const uint32_t w =
+        (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(s0, 448.0f), fminf(s1, 448.0f), 0, false);
+    c0 = w & 0xFFu;
+    c1 = (w >> 8) & 0xFFu;
 }
 
 __device__ __forceinline__ float e4m3_value(uint32_t c) {

@@ -74,6 +74,11 @@ template <> struct Patch<true> {
     __device__ __forceinline__ float at(int i, int e) const {
         return __uint_as_float((e & 1) ? (p[i][e >> 1] & 0xFFFF0000u) : (p[i][e >> 1] << 16));
     }
+    // negate element (i, 2h) where bit 15 of m is set and element (i, 2h + 1) where bit 31 is
+    __device__ __forceinline__ void flip(int i, int h, uint32_t m) { p[i][h] ^= m; }
+    static __device__ __forceinline__ uint32_t pair_mask(uint32_t b_even, uint32_t b_odd) {
+        return (b_even << 15) | (b_odd << 31);
+    }
     // max |x| over the patch: on the packed bits with the signs cleared, two at a time
     // (sign-magnitude bit patterns order like the magnitudes)
     __device__ __forceinline__ float amax() const {
@@ -108,6 +113,13 @@ template <> struct Patch<false> {
         }
     }
     __device__ __forceinline__ float at(int i, int e) const { return p[i][e]; }
+    __device__ __forceinline__ void flip(int i, int h, uint32_t m) {   // m as for bfloat16
+        p[i][2 * h] = __uint_as_float(__float_as_uint(p[i][2 * h]) ^ (m << 16));
+        p[i][2 * h + 1] = __uint_as_float(__float_as_uint(p[i][2 * h + 1]) ^ (m & 0x80000000u));
+    }
+    static __device__ __forceinline__ uint32_t pair_mask(uint32_t b_even, uint32_t b_odd) {
+        return (b_even << 15) | (b_odd << 31);
+    }
     __device__ __forceinline__ float amax() const {
         float m = 0.0f;
 #pragma unroll
@@ -118,12 +130,15 @@ template <> struct Patch<false> {
     }
 };
 
-// Random Hadamard transform of one 16-chunk held as 8 values per lane in a lane pair
-// (lane with half = 0 holds positions 0..7, its neighbour positions 8..15).  Stages 1,
-// 2, 4 are in-register; stage 8 exchanges with lane ^ 1.
-__device__ __forceinline__ void rht_pair8(float w[8], uint32_t signs, int half) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = apply_sign(w[e], signs, half * 8 + e);
+// The random Hadamard transform of a 16-chunk is (1/4) H16 (D v): the sign flips D are
+// applied to the packed patch beforehand (flip_row_signs / flip_col_signs: one XOR per
+// packed pair), the butterflies here, and the factor 1/4 by the caller (an exact scaling,
+// folded into the element reciprocal where that is exact too).
+//
+// Butterflies of a 16-chunk held as 8 values per lane in a lane pair (the lane with
+// half = 0 holds positions 0..7, its neighbour positions 8..15): stages 1, 2, 4
+// in-register, stage 8 with lane ^ 1 as one fma with +-1 (w + p, or p - w).
+__device__ __forceinline__ void wht_pair8(float w[8], float sgn) {
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -136,20 +151,47 @@ __device__ __forceinline__ void rht_pair8(float w[8], uint32_t signs, int half) 
         }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float p = xor1(w[e]);
-        w[e] = half ? (p - w[e]) : (w[e] + p);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = w[e] * 0.25f;
+    for (int e = 0; e < 8; ++e) w[e] = __builtin_fmaf(w[e], sgn, xor1(w[e]));
 }
 
-__device__ __forceinline__ void rht_col16(float w[16], uint32_t signs) {
+// Row signs: element (i, e) of the lane's 8 columns sits at position half * 8 + e of its
+// 16-chunk.  Column signs: the patch's 16 rows are one 16-chunk of every column.
+template <bool BF16>
+__device__ __forceinline__ uint32_t row_sign_mask(uint32_t signs, int half, int h) {
+    const uint32_t s = signs >> (half * 8 + 2 * h);
+    return Patch<BF16>::pair_mask(s & 1u, (s >> 1) & 1u);
+}
+__device__ __forceinline__ uint32_t col_sign_mask(uint32_t signs, int i) {
+    const uint32_t b = (signs >> i) & 1u;
+    return (b << 15) | (b << 31);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void flip_signs(Patch<BF16>& P, uint32_t signs, int half, bool rows,
+                                           bool cols) {
+    uint32_t rm[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) w[i] = apply_sign(w[i], signs, i);
-    wht16(w);
+    for (int h = 0; h < 4; ++h) rm[h] = rows ? row_sign_mask<BF16>(signs, half, h) : 0u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) w[i] = w[i] * 0.25f;
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t cm = cols ? col_sign_mask(signs, i) : 0u;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) P.flip(i, h, rm[h] ^ cm);
+    }
+}
+
+// Largest magnitude of 8 (or 16) values, on the bit patterns (the values are |w|).
+__device__ __forceinline__ float amax8(const float w[8]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(w[e]));
+    return m;
+}
+// max with lane ^ 1 for a non-negative value (integer order of the bit patterns)
+__device__ __forceinline__ float pair_max(float v) {
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b, 0xB1, 0xF, 0xF, false);
+    return __uint_as_float(max(b, o));
 }
 
 // Workgroup max of two values; every thread gets the results.
@@ -166,33 +208,37 @@ __device__ __forceinline__ void block_max2(float& a, float& b, float* red) {
 
 // Amax of one 16x8 patch for the rowwise and the columnwise copy (each plain or after its
 // Hadamard transform).  The rowwise transform pairs this lane with lane ^ 1 (positions 8..15
-// of the 16-chunk when this lane's column is a multiple of 16).
+// of the 16-chunk when this lane's column is a multiple of 16).  The factor 1/4 is applied
+// to the maxima: x -> fl(x / 4) is monotone, so max fl(|w| / 4) = fl(max |w| / 4).
 template <bool BF16, bool RHT_ROW, bool RHT_COL>
-__device__ __forceinline__ void patch_amax(const QArgs& a, const Patch<BF16>& P, uint32_t signs,
+__device__ __forceinline__ void patch_amax(const QArgs& a, Patch<BF16>& P, uint32_t signs,
                                            int half, float& mr, float& mc) {
     float plain = 0.0f, arow = 0.0f, acol = 0.0f;
     if ((a.rowwise && !RHT_ROW) || (a.colwise && !RHT_COL)) plain = P.amax();
     if (RHT_ROW) {
+        flip_signs<BF16>(P, signs, half, true, false);
+        const float sgn = half ? -1.0f : 1.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             float w[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) w[e] = P.at(i, e);
-            rht_pair8(w, signs, half);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) arow = fmaxf(arow, fabsf(w[e]));
+            wht_pair8(w, sgn);
+            arow = fmaxf(arow, amax8(w));
         }
+        arow = arow * 0.25f;
     }
     if (RHT_COL) {
+        flip_signs<BF16>(P, signs, half, RHT_ROW, true);   // undo the row signs, apply the column signs
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             float w[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) w[i] = P.at(i, j);
-            rht_col16(w, signs);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acol = fmaxf(acol, fabsf(w[i]));
+            wht16(w);
+            acol = fmaxf(acol, fmaxf(amax8(&w[0]), amax8(&w[8])));
         }
+        acol = acol * 0.25f;
     }
     mr = fmaxf(mr, RHT_ROW ? arow : plain);
     mc = fmaxf(mc, RHT_COL ? acol : plain);
@@ -207,7 +253,8 @@ __global__ __launch_bounds__(kThreads) void k_amax(QArgs a) {
     constexpr bool RHT_ROW = H & 1, RHT_COL = (H >> 1) & 1;
     __shared__ float red[8];
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-    const uint32_t signs = (RHT_ROW || RHT_COL) ? rht_sign_bits(a.k0, a.k1) : 0u;
+    const uint32_t signs =
+        (RHT_ROW || RHT_COL) ? __builtin_amdgcn_readfirstlane(rht_sign_bits(a.k0, a.k1)) : 0u;
     const int64_t wcols = (a.cols + kAmaxWaveCols - 1) / kAmaxWaveCols;
     const int64_t nwt = (a.rows / 16) * wcols;
     float mr = 0.0f, mc = 0.0f;
@@ -308,6 +355,14 @@ __device__ __forceinline__ float uniform_f(float v) {
 
 // Specialised on the input dtype and on F: bit 0 rowwise SR, bit 1 columnwise SR,
 // bit 2 rowwise Hadamard, bit 3 columnwise Hadamard.
+//
+// The rowwise copy is encoded first, from the patch as loaded (with the row signs flipped in
+// place when it is rotated); the patch is then flipped to the column signs and the
+// columnwise copy encoded.  A rotated copy's factor 1/4 is folded into the block maximum and
+// the element reciprocal (fl(|w'| / 4) = |w'| / 4 and fl(r / 4) = r / 4 exactly) when that is
+// exact for every block whose codes can differ: no 4/6 scaling (its squared errors use the
+// rotated values themselves) and 2^-92 <= s_g <= 2^110 (no reciprocal is then subnormal,
+// and elements small enough to be rounded by the 1/4 quantize to 0 either way).
 template <bool BF16, int F>
 __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
     constexpr bool SR_ROW = F & 1, SR_COL = (F >> 1) & 1;
@@ -321,6 +376,7 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
     const int64_t r0 = (int64_t)tile_r * kTileRows + pr * 16;
     const int64_t c0 = (int64_t)tile_c * kTileCols + pc * 8;
     const bool valid = r0 < a.rows && c0 < a.cols;
+    const int half = pc & 1;
 
     // the patch loads go out first and land while the tensor scales are formed
     Patch<BF16> P;
@@ -346,78 +402,42 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
     __syncthreads();
     const CopyScale rsc{sg_r, __fdiv_rn(1.0f, sg_r), sg_r >= 0x1p-92f, rtab[0]};
     const CopyScale csc{sg_c, __fdiv_rn(1.0f, sg_c), sg_c >= 0x1p-92f, rtab[1]};
-    const uint32_t signs = (RHT_ROW || RHT_COL) ? rht_sign_bits(a.k0, a.k1) : 0u;
+    const bool fold_r = RHT_ROW && !a.scale46 && sg_r >= 0x1p-92f && sg_r <= 0x1p110f;
+    const bool fold_c = RHT_COL && !a.scale46 && sg_c >= 0x1p-92f && sg_c <= 0x1p110f;
+    const uint32_t signs =
+        (RHT_ROW || RHT_COL) ? __builtin_amdgcn_readfirstlane(rht_sign_bits(a.k0, a.k1)) : 0u;
 
     uint32_t scode2d = 0;
     if (a.block2d) {  // one scale per 16x16 tile = this patch and its neighbour's
-        float am = P.amax();
-        am = fmaxf(am, xor1(am));
-        scode2d = rsc.code(am, 6.0f, kRcp6);
-    }
-
-    if (a.colwise) {
-        static_for<0, 8>([&](auto J) {
-            constexpr int j = decltype(J)::value;
-            float w[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) w[i] = P.at(i, j);
-            if (RHT_COL) rht_col16(w, signs);
-            uint32_t scode, rlo = 0, rhi = 0;
-            bool have = false;   // nearest-even codes already formed by the 4/6 choice
-            if (a.block2d) {
-                scode = scode2d;
-            } else {
-                float am = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(w[i]));
-                scode = csc.code(am, 6.0f, kRcp6);
-                if (a.scale46) {
-                    const uint32_t sc4 = csc.code(am, 4.0f, 0.25f);
-                    const float s6 = e4m3_value(scode), s4 = e4m3_value(sc4);
-                    const float q6 = csc.rcp(scode), q4 = csc.rcp(sc4);
-                    uint32_t l6, h6, l4, h4;
-                    const float e6 = sse8_rne(&w[0], s6, q6, sg_c, l6) + sse8_rne(&w[8], s6, q6, sg_c, h6);
-                    const float e4 = sse8_rne(&w[0], s4, q4, sg_c, l4) + sse8_rne(&w[8], s4, q4, sg_c, h4);
-                    const bool use4 = e4 < e6;
-                    scode = use4 ? sc4 : scode;
-                    rlo = use4 ? l4 : l6;
-                    rhi = use4 ? h4 : h6;
-                    have = true;
-                }
-            }
-            const float rcp = csc.rcp(scode);
-            uint32_t lo, hi;
-            if (!SR_COL) {
-                lo = have ? rlo : encode8_rne(&w[0], rcp);
-                hi = have ? rhi : encode8_rne(&w[8], rcp);
-            } else {
-                const uint64_t g = ((uint64_t)(c0 + j) * (uint64_t)a.rows + (uint64_t)r0) >> 3;
-                lo = encode8_sr(&w[0], rcp, sr_words(g, 1u, a.k0, a.k1));
-                hi = encode8_sr(&w[8], rcp, sr_words(g + 1, 1u, a.k0, a.k1));
-            }
-            const int cl = pc * 8 + j;
-            ccodes_lds[cl][pr ^ pc] = make_uint2(lo, hi);
-            cscales_lds[cl * 17 + pr] = (uint8_t)scode;
-        });
+        scode2d = rsc.code(pair_max(P.amax()), 6.0f, kRcp6);
     }
 
     if (a.rowwise) {
+        if (RHT_ROW) flip_signs<BF16>(P, signs, half, true, false);
+        const float sgn = half ? -1.0f : 1.0f;
         const int64_t rpitch = a.cols / 2, spitch = a.cols / 16;
+        uint8_t* const cbase = a.rcodes + r0 * rpitch + c0 / 2;
+        uint8_t* const sbase = a.rscales + r0 * spitch + c0 / 16;
         static_for<0, 16>([&](auto I) {
             constexpr int i = decltype(I)::value;
             float w[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) w[e] = P.at(i, e);
-            if (RHT_ROW) rht_pair8(w, signs, pc & 1);
+            if (RHT_ROW) {
+                wht_pair8(w, sgn);
+                if (!fold_r) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[e] = w[e] * 0.25f;
+                }
+            }
             uint32_t scode, rcodes = 0;
             bool have = false;   // nearest-even codes already formed by the 4/6 choice
+            float rscale = 1.0f; // 1/4 when the rotation's factor is folded in
             if (a.block2d) {
                 scode = scode2d;
             } else {
-                float am = 0.0f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(w[e]));
-                am = fmaxf(am, xor1(am));
+                float am = pair_max(amax8(w));
+                if (RHT_ROW && fold_r) { am = am * 0.25f; rscale = 0.25f; }
                 scode = rsc.code(am, 6.0f, kRcp6);
                 if (a.scale46) {
                     // the block's halves sit in this lane and lane ^ 1; a + b == b + a, so
@@ -434,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
                     have = true;
                 }
             }
-            const float rcp = rsc.rcp(scode);
+            const float rcp = rsc.rcp(scode) * rscale;
             uint32_t codes;
             if (!SR_ROW) {
                 codes = have ? rcodes : encode8_rne(w, rcp);
@@ -443,13 +463,64 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
                 codes = encode8_sr(w, rcp, sr_words(g, 0u, a.k0, a.k1));
             }
             if (valid) {
-                *(uint32_t*)(a.rcodes + (r0 + i) * rpitch + c0 / 2) = codes;
-                if ((pc & 1) == 0) a.rscales[(r0 + i) * spitch + c0 / 16] = (uint8_t)scode;
+                *(uint32_t*)(cbase + i * rpitch) = codes;
+                if (half == 0) sbase[i * spitch] = (uint8_t)scode;
             }
         });
     }
 
     if (a.colwise) {
+        // from the loaded (or row-flipped) signs to the column signs
+        if (RHT_COL || RHT_ROW) flip_signs<BF16>(P, signs, half, RHT_ROW, RHT_COL);
+        static_for<0, 8>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            float w[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) w[i] = P.at(i, j);
+            if (RHT_COL) {
+                wht16(w);
+                if (!fold_c) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) w[i] = w[i] * 0.25f;
+                }
+            }
+            uint32_t scode, rlo = 0, rhi = 0;
+            bool have = false;   // nearest-even codes already formed by the 4/6 choice
+            float rscale = 1.0f;
+            if (a.block2d) {
+                scode = scode2d;
+            } else {
+                float am = fmaxf(amax8(&w[0]), amax8(&w[8]));
+                if (RHT_COL && fold_c) { am = am * 0.25f; rscale = 0.25f; }
+                scode = csc.code(am, 6.0f, kRcp6);
+                if (a.scale46) {
+                    const uint32_t sc4 = csc.code(am, 4.0f, 0.25f);
+                    const float s6 = e4m3_value(scode), s4 = e4m3_value(sc4);
+                    const float q6 = csc.rcp(scode), q4 = csc.rcp(sc4);
+                    uint32_t l6, h6, l4, h4;
+                    const float e6 = sse8_rne(&w[0], s6, q6, sg_c, l6) + sse8_rne(&w[8], s6, q6, sg_c, h6);
+                    const float e4 = sse8_rne(&w[0], s4, q4, sg_c, l4) + sse8_rne(&w[8], s4, q4, sg_c, h4);
+                    const bool use4 = e4 < e6;
+                    scode = use4 ? sc4 : scode;
+                    rlo = use4 ? l4 : l6;
+                    rhi = use4 ? h4 : h6;
+                    have = true;
+                }
+            }
+            const float rcp = csc.rcp(scode) * rscale;
+            uint32_t lo, hi;
+            if (!SR_COL) {
+                lo = have ? rlo : encode8_rne(&w[0], rcp);
+                hi = have ? rhi : encode8_rne(&w[8], rcp);
+            } else {
+                const uint64_t g = ((uint64_t)(c0 + j) * (uint64_t)a.rows + (uint64_t)r0) >> 3;
+                lo = encode8_sr(&w[0], rcp, sr_words(g, 1u, a.k0, a.k1));
+                hi = encode8_sr(&w[8], rcp, sr_words(g + 1, 1u, a.k0, a.k1));
+            }
+            const int cl = pc * 8 + j;
+            ccodes_lds[cl][pr ^ pc] = make_uint2(lo, hi);
+            cscales_lds[cl * 17 + pr] = (uint8_t)scode;
+        });
         __syncthreads();
         const int64_t cpitch = a.rows / 2, spitch = a.rows / 16;
         const int64_t gc0 = (int64_t)tile_c * kTileCols, gr0 = (int64_t)tile_r * kTileRows;
