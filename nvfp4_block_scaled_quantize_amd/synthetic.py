@@ -15,12 +15,14 @@ sotapapers summary's model description):
            H bf16 8192x9216 N(0,1) with 8 outlier channels x30
   wgrad    dY bf16 8192x9216, Student-t (nu = 3) rescaled to std 1e-3; X as qkv
   qadamw   v fp32 9216x3072 log-normal exp(-18 + 3 N(0,1))
+  lora     rank-64 factors of the FFN-up LoRA-SVD branch: L1 bf16 64x3072 N(0, 1/3072),
+           L2 bf16 9216x64 N(0,0.02^2), beta 0.5 (rank and beta are not on the pages)
 Real activations, weights, gradients and optimizer states of the pages' trained
 model are not available; these distributions stand in for them.
 """
 import torch
 
-DATA_SEEDS = {"tiny": 1, "qkv": 2, "ffn": 3, "wgrad": 4, "qadamw": 5}
+DATA_SEEDS = {"tiny": 1, "qkv": 2, "ffn": 3, "wgrad": 4, "qadamw": 5, "lora": 6}
 RHT_SEED_WGRAD = 0x5EED4
 RHT_SEED_QADAMW = 0x5EED5
 
@@ -98,3 +100,9 @@ def wgrad(tokens=8192, hidden=3072, ffn_dim=9216, seed=DATA_SEEDS["wgrad"]):
 
 def qadamw(rows=9216, cols=3072, seed=DATA_SEEDS["qadamw"]):
     return {"v": lognormal((rows, cols), seed)}
+
+
+def lora(rank=64, hidden=3072, ffn_dim=9216, seed=DATA_SEEDS["lora"]):
+    return {"L1": bf16(normal((rank, hidden), seed, hidden ** -0.5)),
+            "L2": bf16(normal((ffn_dim, rank), seed + 1000, 0.02)),
+            "beta": 0.5}

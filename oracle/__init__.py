@@ -64,6 +64,10 @@ def _load():
         "or_qadamw_v_encode": (ctypes.c_int, [P, i64, i64, u64, ctypes.c_int, P, P, P, P]),
         "or_qadamw_v_decode": (ctypes.c_int, [P, P, P, f32, i64, i64, u64, ctypes.c_int, P]),
         "or_num_threads": (ctypes.c_int, []),
+        "or_lora_down": (ctypes.c_int, [P, i64, i64, P, i64, f32, P, P, P]),
+        "or_gemm_lora_f64": (ctypes.c_int, [P, P, f32, P, P, f32, i64, i64, i64, P, P, i64, P, P]),
+        "or_gemm_lora_f64_entries": (ctypes.c_int, [P, P, f32, P, P, f32, i64, i64, i64, P, P, i64,
+                                                    P, P, i64, P, P]),
         "or_qadamw_step": (ctypes.c_int, [P, P, i64, i64, P, P, f32, P, P, P, f32, P, u64, u64, u64,
                                           ctypes.c_int, P, P, P, P, P, P, P, P, P]),
     }
@@ -233,6 +237,58 @@ def gemm_f64_entries(qa, qb, em, en):
                                      _ptr(qb.scales), qb.sg, M, N, K, _ptr(em), _ptr(en),
                                      em.shape[0], _ptr(out), _ptr(ad))
     _check(rc, "gemm_f64_entries")
+    return out, ad
+
+
+# ---------------------------------------------------------------- LoRA-SVD low-rank branch
+def lora_down(x, a, beta):
+    """Down-projection t = BF16(beta x a^T) of Full-Stack FP4 sec. 3.2 eq. (1): x [M][K]
+    (binary32), a [r][K] BF16 bits.  Returns (t [M][r] BF16 bits, binary64 value before
+    the rounding, |beta| sum |x a|)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    M, K = x.shape
+    r, K2 = a.shape
+    assert K == K2
+    t = np.zeros((M, r), dtype=np.uint16)
+    t64 = np.zeros((M, r), dtype=np.float64)
+    tabs = np.zeros((M, r), dtype=np.float64)
+    _check(_load().or_lora_down(_ptr(x), M, K, _ptr(a), r, float(beta), _ptr(t), _ptr(t64),
+                                _ptr(tabs)), "lora_down")
+    return t, t64, tabs
+
+
+def gemm_lora_f64(qa, qb, t, b):
+    """A B^T over the dequantized operands plus t b^T (t [M][r], b [N][r] BF16 bits),
+    binary64; returns (C, sum of |terms|)."""
+    M, K = qa.shape
+    N, _ = qb.shape
+    t = np.ascontiguousarray(t, dtype=np.uint16)
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    r = t.shape[1]
+    assert t.shape == (M, r) and b.shape == (N, r)
+    C = np.zeros((M, N), dtype=np.float64)
+    ad = np.zeros((M, N), dtype=np.float64)
+    _check(_load().or_gemm_lora_f64(_ptr(qa.codes), _ptr(qa.scales), qa.sg, _ptr(qb.codes),
+                                    _ptr(qb.scales), qb.sg, M, N, K, _ptr(t), _ptr(b), r, _ptr(C),
+                                    _ptr(ad)), "gemm_lora_f64")
+    return C, ad
+
+
+def gemm_lora_f64_entries(qa, qb, t, b, em, en):
+    M, K = qa.shape
+    N, _ = qb.shape
+    t = np.ascontiguousarray(t, dtype=np.uint16)
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    r = t.shape[1]
+    em = np.ascontiguousarray(em, dtype=np.int64)
+    en = np.ascontiguousarray(en, dtype=np.int64)
+    out = np.zeros(em.shape[0], dtype=np.float64)
+    ad = np.zeros(em.shape[0], dtype=np.float64)
+    _check(_load().or_gemm_lora_f64_entries(_ptr(qa.codes), _ptr(qa.scales), qa.sg,
+                                            _ptr(qb.codes), _ptr(qb.scales), qb.sg, M, N, K,
+                                            _ptr(t), _ptr(b), r, _ptr(em), _ptr(en), em.shape[0],
+                                            _ptr(out), _ptr(ad)), "gemm_lora_f64_entries")
     return out, ad
 
 

@@ -446,6 +446,112 @@ int or_gemm_f64_entries(const uint8_t* codesA, const uint8_t* scalesA, float sgA
 }
 
 /* ------------------------------------------------------------------------- */
+/* Low-rank branch of the LoRA-SVD linear.  [FS4] sec. 3.2 eq. (1): Y is the     */
+/* NVFP4 product Q(X) Q(W_res)^T plus beta (X L1^T) L2^T computed in BF16, and   */
+/* Appendix 9 fuses the down-projection X L1^T with the quantizer (same input)   */
+/* and the up-projection with the GEMM (same output).  Readings: the rank r and  */
+/* beta are parameters (the pages give neither); the down-projection output is   */
+/* one BF16 tensor T = BF16(beta X L1^T) (beta applied before that rounding, so  */
+/* the up-projection adds T L2^T); both factors are BF16.  The reference forms   */
+/* beta * sum_k x a in binary64 and rounds it once to BF16; the up-projection    */
+/* term is binary64 over the BF16 T and L2.                                      */
+/* ------------------------------------------------------------------------- */
+
+/* Nearest BF16 (8 significant bits, binary32 exponent range, ties to even) of a
+ * binary64 value, rounded once. */
+static uint16_t bf16_rne_f64(double v)
+{
+    if (v == 0.0) return signbit(v) ? 0x8000u : 0u;
+    const double a = fabs(v);
+    int e;
+    frexp(a, &e);                      /* a = f 2^e, f in [0.5, 1) */
+    int q = e - 8;                     /* weight of the last kept bit */
+    if (q < -133) q = -133;            /* BF16 subnormal spacing */
+    const double units = ldexp(a, -q); /* exact: a power-of-two scaling */
+    const double fl = floor(units), fr = units - fl;
+    double n = fl;
+    if (fr > 0.5 || (fr == 0.5 && fmod(fl, 2.0) != 0.0)) n = fl + 1.0;
+    const float f = (float)ldexp(n, q); /* at most 8 significant bits (or a power of two) */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    const uint16_t b = (uint16_t)(u >> 16);
+    return v < 0 ? (uint16_t)(b | 0x8000u) : b;
+}
+
+int or_lora_down(const float* x, int64_t M, int64_t K, const uint16_t* a, int64_t r, float beta,
+                 uint16_t* t, double* t64, double* tabs)
+{
+    if (M < 0 || K < 0 || r < 0) return -2;
+    for (int64_t i = 0; i < M * K; ++i)
+        if (!isfinite(x[i])) return -3;
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t j = 0; j < r; ++j) {
+            double s = 0.0, sa = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double p = (double)x[m * K + k] * (double)or_bf16_value(a[j * K + k]);
+                s += p;
+                sa += fabs(p);
+            }
+            const double v = (double)beta * s;
+            t[m * r + j] = bf16_rne_f64(v);
+            if (t64) t64[m * r + j] = v;
+            if (tabs) tabs[m * r + j] = fabs((double)beta) * sa;
+        }
+    return 0;
+}
+
+/* The low-rank term sum_j T[m][j] B[n][j] (binary64; the BF16 products are exact). */
+static double lora_term(const uint16_t* t, const uint16_t* b, int64_t r, int64_t m, int64_t n,
+                        double* abs_out)
+{
+    double s = 0.0, sa = 0.0;
+    for (int64_t j = 0; j < r; ++j) {
+        const double p = (double)or_bf16_value(t[m * r + j]) * (double)or_bf16_value(b[n * r + j]);
+        s += p;
+        sa += fabs(p);
+    }
+    *abs_out = sa;
+    return s;
+}
+
+int or_gemm_lora_f64(const uint8_t* codesA, const uint8_t* scalesA, float sgA,
+                     const uint8_t* codesB, const uint8_t* scalesB, float sgB,
+                     int64_t M, int64_t N, int64_t K, const uint16_t* t, const uint16_t* b,
+                     int64_t r, double* C, double* absdot)
+{
+    if (r < 0) return -2;
+    int rc = or_gemm_f64(codesA, scalesA, sgA, codesB, scalesB, sgB, M, N, K, C, absdot);
+    if (rc) return rc;
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double sa;
+            C[m * N + n] += lora_term(t, b, r, m, n, &sa);
+            if (absdot) absdot[m * N + n] += sa;
+        }
+    return 0;
+}
+
+int or_gemm_lora_f64_entries(const uint8_t* codesA, const uint8_t* scalesA, float sgA,
+                             const uint8_t* codesB, const uint8_t* scalesB, float sgB,
+                             int64_t M, int64_t N, int64_t K, const uint16_t* t,
+                             const uint16_t* b, int64_t r, const int64_t* em, const int64_t* en,
+                             int64_t count, double* out, double* absdot)
+{
+    if (r < 0) return -2;
+    int rc = or_gemm_f64_entries(codesA, scalesA, sgA, codesB, scalesB, sgB, M, N, K, em, en,
+                                 count, out, absdot);
+    if (rc) return rc;
+    for (int64_t i = 0; i < count; ++i) {
+        double sa;
+        out[i] += lora_term(t, b, r, em[i], en[i], &sa);
+        if (absdot) absdot[i] += sa;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Quantized-state AdamW second moment.  [FS4] sec. 3.3: (1) square root,      */
 /* (2) subtract the tile-wise mean, (3) fast Hadamard transform of the         */
 /* residual (times H16), (4) NVFP4 quantization; reconstruction                */

@@ -104,6 +104,24 @@ int or_qadamw_v_decode(const uint16_t* mu, const uint8_t* codes, const uint8_t* 
                        float sg, int64_t R, int64_t C, uint64_t seed, int use_signs,
                        float* v_out);
 
+/* Low-rank branch of the LoRA-SVD linear ([FS4] sec. 3.2 eq. (1), Appendix 9; reading in
+ * nvfp4_oracle.c).  Down-projection: t[M][r] = BF16(beta * x[M][K] a[r][K]^T), a in BF16
+ * bits; t64 (may be NULL) the binary64 value before rounding, tabs (may be NULL)
+ * |beta| sum_k |x a|. */
+int or_lora_down(const float* x, int64_t M, int64_t K, const uint16_t* a, int64_t r, float beta,
+                 uint16_t* t, double* t64, double* tabs);
+/* GEMM plus the up-projection: C = A B^T (dequantized, as or_gemm_f64) + t[M][r] b[N][r]^T
+ * (BF16 bits); absdot adds sum_j |t b|. */
+int or_gemm_lora_f64(const uint8_t* codesA, const uint8_t* scalesA, float sgA,
+                     const uint8_t* codesB, const uint8_t* scalesB, float sgB,
+                     int64_t M, int64_t N, int64_t K, const uint16_t* t, const uint16_t* b,
+                     int64_t r, double* C, double* absdot);
+int or_gemm_lora_f64_entries(const uint8_t* codesA, const uint8_t* scalesA, float sgA,
+                             const uint8_t* codesB, const uint8_t* scalesB, float sgB,
+                             int64_t M, int64_t N, int64_t K, const uint16_t* t,
+                             const uint16_t* b, int64_t r, const int64_t* em, const int64_t* en,
+                             int64_t count, double* out, double* absdot);
+
 /* Number of OpenMP threads the oracle runs with (1 without OpenMP). */
 /* Quantized-state AdamW step (reading in nvfp4_oracle.c): decodes m (NVFP4 1x16 of the
  * Hadamard-rotated moment) and v (second-moment pipeline), updates the moments and the
