@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 3
+#define NVFP4_ABI_VERSION 4
 
 enum nvfp4_status {
     NVFP4_OK = 0,
@@ -150,6 +150,21 @@ int nvfp4_dequantize(const nvfp4_qtensor* q, int64_t n, int64_t k, int out_dtype
  * K/2 a multiple of 16 bytes (K % 32 == 0), C 4-byte aligned. */
 int nvfp4_gemm(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
                int64_t K, float* c, int64_t ldc, void* stream);
+
+/* The W4A4 GEMM with the LoRA-SVD low-rank term fused into its epilogue:
+ *   C[M][N] = (nvfp4_gemm's product) + sum_j T[m][j] L[n][j].
+ * Passage: Full-Stack FP4 sec. 3.2 eq. (1) (Y = Q(X) Q(W_res)^T + beta (X L1^T) L2^T, the
+ * branch in BF16; dX likewise with (dY L2) L1) and Appendix 9 (the up-projection shares
+ * the GEMM's output).  T is the down-projection with beta already applied (as written by
+ * nvfp4_quantize_lora), L the up factor: L2 [N][rank] for Y, L1^T [N][rank] for dX.
+ * lora_t [M][rank] and lora_b [N][rank]: device BF16, row-major, 16-byte aligned, read
+ * only.  rank must be a multiple of 16 (rank 0 gives nvfp4_gemm); the term is formed by
+ * BF16 matrix-core products with FP32 accumulation onto fl(s_gA s_gB acc).  Other
+ * arguments and errors as nvfp4_gemm; a rank that is not a multiple of 16 gives
+ * NVFP4_ERR_SHAPE, a null factor with rank > 0 NVFP4_ERR_NULL. */
+int nvfp4_gemm_lora(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
+                    int64_t K, float* c, int64_t ldc, const uint16_t* lora_t,
+                    const uint16_t* lora_b, int64_t rank, void* stream);
 
 /* Device workspace (bytes) qadamw_v_encode needs. */
 size_t qadamw_v_workspace_bytes(int64_t rows, int64_t cols);

@@ -30,7 +30,7 @@ NVFP4_BLOCK_1D, NVFP4_BLOCK_2D = 0, 1
 EXPORTED = ["nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantize",
             "nvfp4_gemm", "qadamw_v_workspace_bytes", "qadamw_v_encode", "qadamw_v_decode",
             "nvfp4_status_string", "nvfp4_abi_version", "qadamw_step_workspace_bytes",
-            "qadamw_step"]
+            "qadamw_step", "nvfp4_gemm_lora"]
 
 
 class Nvfp4Error(RuntimeError):
@@ -59,7 +59,7 @@ class QTensorC(ctypes.Structure):
 
 
 _lib = None
-ABI_VERSION = 3   # NVFP4_ABI_VERSION of include/nvfp4.h this binding matches
+ABI_VERSION = 4   # NVFP4_ABI_VERSION of include/nvfp4.h this binding matches
 
 
 def load_library(path: Optional[str] = None):
@@ -83,6 +83,9 @@ def load_library(path: Optional[str] = None):
     lib.nvfp4_dequantize.argtypes = [P(QTensorC), i64, i64, ctypes.c_int, vp, i64, vp]
     lib.nvfp4_gemm.restype = ctypes.c_int
     lib.nvfp4_gemm.argtypes = [P(QTensorC), P(QTensorC), i64, i64, i64, vp, i64, vp]
+    lib.nvfp4_gemm_lora.restype = ctypes.c_int
+    lib.nvfp4_gemm_lora.argtypes = [P(QTensorC), P(QTensorC), i64, i64, i64, vp, i64, vp, vp, i64,
+                                    vp]
     lib.qadamw_v_workspace_bytes.restype = sz
     lib.qadamw_v_workspace_bytes.argtypes = [i64, i64]
     lib.qadamw_v_encode.restype = ctypes.c_int
@@ -218,6 +221,30 @@ def nvfp4_gemm(a, b, out=None):
     ac, bc = a.c(), b.c()
     _check(lib.nvfp4_gemm(ctypes.byref(ac), ctypes.byref(bc), M, N, K, _ptr(out), out.stride(0),
                           _stream(out.device)))
+    return out
+
+
+def nvfp4_gemm_lora(a, b, t, lb, out=None):
+    """C = A B^T + t lb^T: the W4A4 GEMM with the LoRA-SVD up-projection in its epilogue
+    (t [M][r], lb [N][r] contiguous bfloat16 on the GPU, r a multiple of 16)."""
+    lib = load_library()
+    _require_cuda(a.codes, b.codes, t, lb)
+    M, K = a.shape
+    N, K2 = b.shape
+    if K != K2:
+        raise Nvfp4Error(f"K mismatch {K} vs {K2}")
+    if t.dtype != torch.bfloat16 or lb.dtype != torch.bfloat16 or not t.is_contiguous() \
+            or not lb.is_contiguous() or t.dim() != 2 or lb.dim() != 2:
+        raise Nvfp4Error("t and lb must be contiguous 2-D bfloat16 tensors")
+    r = t.shape[1]
+    if t.shape[0] != M or lb.shape != (N, r):
+        raise Nvfp4Error(f"low-rank factors {tuple(t.shape)}, {tuple(lb.shape)} do not match "
+                         f"M={M}, N={N}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.codes.device)
+    ac, bc = a.c(), b.c()
+    _check(lib.nvfp4_gemm_lora(ctypes.byref(ac), ctypes.byref(bc), M, N, K, _ptr(out), out.stride(0),
+                               _ptr(t), _ptr(lb), r, _stream(out.device)))
     return out
 
 

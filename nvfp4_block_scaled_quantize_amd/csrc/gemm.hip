@@ -66,6 +66,9 @@ struct GArgs {
     float* c;
     int64_t ldc;
     int tiles_m, tiles_n;
+    const uint16_t* lt;   // low-rank term: T [M][lr] and L [N][lr] (BF16), or null
+    const uint16_t* lb;
+    int64_t lr;
 };
 
 // Packed tile layout: row r holds 64 bytes as four 16-byte chunks; chunk q sits at slot
@@ -181,8 +184,7 @@ __device__ __forceinline__ void mma_stage(const Frags& f, float16v (&acc)[4][4])
 // (32 rows) at a time, with a scheduling fence between block rows, so the compiler does
 // not pull all 256 accumulators into VGPRs at once.
 __device__ __forceinline__ void store_tile(const GArgs& g, const float16v (&acc)[4][4], int64_t m0,
-                                           int64_t n0, int wm, int wn, int h, int li) {
-    const float scale = *g.asg * *g.bsg;
+                                           int64_t n0, int wm, int wn, int h, int li, float scale) {
     const int64_t rbase = m0 + wm * 128 + 4 * h, cbase = n0 + wn * 128 + li;
     const bool full = m0 + GBM <= g.M && n0 + GBN <= g.N;
 #pragma unroll
@@ -198,6 +200,58 @@ __device__ __forceinline__ void store_tile(const GArgs& g, const float16v (&acc)
         }
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+// LoRA-SVD up-projection in the epilogue (Full-Stack FP4 sec. 3.2 eq. (1), Appendix 9: the
+// low-rank branch shares the GEMM's output tile).  For each 32-row block row of the wave's
+// sub-tile, T L^T is formed by BF16 MFMAs (32x32x16, FP32 accumulate, from zero) over the
+// rank in steps of 16, and each output is stored as fl(acc s_gA s_gB) + that term.  Lane
+// (li, h) supplies row li of the block and the rank entries 8h..8h+7 of the step: 16
+// contiguous bytes of T and of L.
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8v load_bf16x8(const uint16_t* base, int64_t row, int64_t rows,
+                                               int64_t ld, int64_t col) {
+    uint4 q = make_uint4(0u, 0u, 0u, 0u);
+    if (row < rows) q = *(const uint4*)(base + row * ld + col);
+    return __builtin_bit_cast(bf16x8v, q);
+}
+
+__device__ __forceinline__ void store_tile_lora(const GArgs& g, float16v (&acc)[4][4],
+                                                int64_t m0, int64_t n0, int wm, int wn, int h,
+                                                int li) {
+    const float scale = *g.asg * *g.bsg;
+    const int64_t ra = m0 + wm * 128 + li, rb = n0 + wn * 128 + li;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // block row i: each accumulator block is scaled into a temporary that the low-rank
+        // MFMAs take as C and write back in place (the block's own registers)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float16v c;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) c[r] = acc[i][j][r] * scale;
+            for (int64_t s = 0; s < g.lr; s += 16) {
+                const bf16x8v a = load_bf16x8(g.lt, ra + 32 * i, g.M, g.lr, s + 8 * h);
+                const bf16x8v b = load_bf16x8(g.lb, rb + 32 * j, g.N, g.lr, s + 8 * h);
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+            }
+            acc[i][j] = c;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    store_tile(g, acc, m0, n0, wm, wn, h, li, 1.0f);
+}
+
+// The epilogue, with the low-rank term as a compile-time switch so that the plain kernels
+// keep their register allocation.
+template <bool LORA>
+__device__ __forceinline__ void finish_tile(const GArgs& g, float16v (&acc)[4][4], int64_t m0,
+                                            int64_t n0, int wm, int wn, int h, int li) {
+    if constexpr (LORA)
+        store_tile_lora(g, acc, m0, n0, wm, wn, h, li);
+    else
+        store_tile(g, acc, m0, n0, wm, wn, h, li, *g.asg * *g.bsg);
 }
 
 // Tile of workgroup `bid`.  Workgroups are dealt to the eight XCDs round-robin (bid mod 8)
@@ -283,6 +337,7 @@ __device__ __forceinline__ void store_stage(uint8_t* buf, const StageRegs& r) {
     *(uint2*)(bs + t * 8) = r.sb;
 }
 
+template <bool LORA>
 __global__ __launch_bounds__(GThreads, 1) void k_gemm(GArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6, wm = wid >> 1, wn = wid & 1;
@@ -309,7 +364,7 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm(GArgs g) {
         if (s + 1 < nst) store_stage(lds + ((s + 1) & 1) * kStageBytes, regs);
         __syncthreads();
     }
-    store_tile(g, acc, m0, n0, wm, wn, h, li);
+    finish_tile<LORA>(g, acc, m0, n0, wm, wn, h, li);
 }
 
 // ---------------------------------------------------------------- direct staging path
@@ -524,6 +579,7 @@ __device__ __forceinline__ void piped_stage(const DmaCtx& c, int s, HalfFrags& l
     for (int x = 0; x < 4; ++x) { sa[x] = nsa[x]; sb[x] = nsb[x]; }
 }
 
+template <bool LORA>
 __global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     DmaCtx c;
@@ -565,27 +621,34 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
     make_pairs<0>(sa, sb, p);
     decode_slot<0>(lo, p, av, bv);
     for (int s = 0; s < c.nst; ++s) piped_stage(c, s, lo, hi, sa, sb, p, av, bv, acc);
-    store_tile(g, acc, c.m0, c.n0, c.wm, c.wn, c.h, c.li);
+    finish_tile<LORA>(g, acc, c.m0, c.n0, c.wm, c.wn, c.h, c.li);
 }
 
 }  // namespace nvfp4
 
 using namespace nvfp4;
 
-extern "C" int nvfp4_gemm(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
-                          int64_t K, float* c, int64_t ldc, void* stream) {
+static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
+                       int64_t K, float* c, int64_t ldc, const uint16_t* lt, const uint16_t* lb,
+                       int64_t lr, void* stream) {
     if (!a || !b || !a->gscale || !b->gscale) return NVFP4_ERR_NULL;
     if (M < 0 || N < 0 || K < 0 || K % 32 || ldc < N) return NVFP4_ERR_SHAPE;
+    if (lr < 0 || lr % 16) return NVFP4_ERR_SHAPE;
     if (M == 0 || N == 0) return NVFP4_OK;
     if (!c) return NVFP4_ERR_NULL;
     if (K > 0 && (!a->codes || !a->scales || !b->codes || !b->scales)) return NVFP4_ERR_NULL;
+    if (lr > 0 && (!lt || !lb)) return NVFP4_ERR_NULL;
     if (((uintptr_t)a->codes & 15) || ((uintptr_t)b->codes & 15) || ((uintptr_t)c & 3) ||
-        ((uintptr_t)a->gscale & 3) || ((uintptr_t)b->gscale & 3))
+        ((uintptr_t)a->gscale & 3) || ((uintptr_t)b->gscale & 3) || ((uintptr_t)lt & 15) ||
+        ((uintptr_t)lb & 15))
         return NVFP4_ERR_ALIGN;
     GArgs g;
     g.ac = a->codes; g.as = a->scales; g.asg = a->gscale;
     g.bc = b->codes; g.bs = b->scales; g.bsg = b->gscale;
     g.M = M; g.N = N; g.K = K; g.c = c; g.ldc = ldc;
+    g.lt = lr > 0 ? lt : nullptr;
+    g.lb = lr > 0 ? lb : nullptr;
+    g.lr = lr;
     const int64_t tiles_m = (M + GBM - 1) / GBM, tiles_n = (N + GBN - 1) / GBN;
     g.tiles_m = (int)tiles_m;
     g.tiles_n = (int)tiles_n;
@@ -595,16 +658,29 @@ extern "C" int nvfp4_gemm(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_
     const int64_t kbytes = K / 2, limit = (int64_t)kOutOfRange;
     const bool direct = K > 0 && K % 64 == 0 && ((uintptr_t)a->scales & 3) == 0 &&
                         ((uintptr_t)b->scales & 3) == 0 && M * kbytes < limit && N * kbytes < limit;
+    const void* fn = direct ? (lr > 0 ? (const void*)k_gemm_dma<true> : (const void*)k_gemm_dma<false>)
+                            : (lr > 0 ? (const void*)k_gemm<true> : (const void*)k_gemm<false>);
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            direct ? kGemmDmaLds : kGemmLds) != hipSuccess)
+        return NVFP4_ERR_HIP;
+    hipStream_t st = (hipStream_t)stream;
     if (direct) {
-        if (hipFuncSetAttribute((const void*)k_gemm_dma, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kGemmDmaLds) != hipSuccess)
-            return NVFP4_ERR_HIP;
-        k_gemm_dma<<<grid, GThreads, kGemmDmaLds, (hipStream_t)stream>>>(g);
+        if (lr > 0) k_gemm_dma<true><<<grid, GThreads, kGemmDmaLds, st>>>(g);
+        else k_gemm_dma<false><<<grid, GThreads, kGemmDmaLds, st>>>(g);
     } else {
-        if (hipFuncSetAttribute((const void*)k_gemm, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kGemmLds) != hipSuccess)
-            return NVFP4_ERR_HIP;
-        k_gemm<<<grid, GThreads, kGemmLds, (hipStream_t)stream>>>(g);
+        if (lr > 0) k_gemm<true><<<grid, GThreads, kGemmLds, st>>>(g);
+        else k_gemm<false><<<grid, GThreads, kGemmLds, st>>>(g);
     }
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+extern "C" int nvfp4_gemm(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
+                          int64_t K, float* c, int64_t ldc, void* stream) {
+    return gemm_launch(a, b, M, N, K, c, ldc, nullptr, nullptr, 0, stream);
+}
+
+extern "C" int nvfp4_gemm_lora(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M,
+                               int64_t N, int64_t K, float* c, int64_t ldc, const uint16_t* lora_t,
+                               const uint16_t* lora_b, int64_t rank, void* stream) {
+    return gemm_launch(a, b, M, N, K, c, ldc, lora_t, lora_b, rank, stream);
 }
