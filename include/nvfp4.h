@@ -132,6 +132,24 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t
                    const nvfp4_quant_params* p, const nvfp4_qtensor* row_out,
                    const nvfp4_qtensor* col_out, void* ws, size_t ws_bytes, void* stream);
 
+/* nvfp4_quantize with the LoRA-SVD down-projection fused into its first pass:
+ *   lora_t[rows][rank] = BF16(beta * x lora_a^T)   (nearest-even from the FP32 sum)
+ * besides the copies nvfp4_quantize writes (identical to its output for the same p).
+ * Passage: Full-Stack FP4 sec. 3.2 eq. (1) (the BF16 branch beta (X L1^T) L2^T next to the
+ * NVFP4 GEMM; for dX, (dY L2) L1) and Appendix 9 (the down-projection reuses the
+ * quantizer's read of X).  lora_a [rank][cols]: device BF16, row-major, 16-byte aligned
+ * (L1 for X, L2^T for dY).  beta: the branch factor, applied before the BF16 rounding (the
+ * up-projection then adds lora_t times the up factor; see nvfp4_gemm_lora).  The sum over
+ * cols is FP32 (BF16 matrix-core products), in a fixed order: parts of the columns summed
+ * separately, then the parts in order.
+ * Limits: dtype NVFP4_BF16 (else NVFP4_ERR_DTYPE); rank a multiple of 16 up to 64 and cols
+ * a multiple of 128 (else NVFP4_ERR_SHAPE); ws of nvfp4_quantize_lora_workspace_bytes. */
+size_t nvfp4_quantize_lora_workspace_bytes(int64_t rows, int64_t cols, int64_t rank);
+int nvfp4_quantize_lora(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                        const nvfp4_quant_params* p, const nvfp4_qtensor* row_out,
+                        const nvfp4_qtensor* col_out, const uint16_t* lora_a, int64_t rank,
+                        float beta, uint16_t* lora_t, void* ws, size_t ws_bytes, void* stream);
+
 /* Decode one copy: out[n][k] = (value(code) * s) * s_g, rounded once to binary32
  * (Full-Stack FP4 sec. 2), then to bfloat16 nearest-even if out_dtype is NVFP4_BF16.
  * Rotated copies decode to the rotated values.  out has row pitch ld_out elements

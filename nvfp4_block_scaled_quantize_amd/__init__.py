@@ -30,7 +30,8 @@ NVFP4_BLOCK_1D, NVFP4_BLOCK_2D = 0, 1
 EXPORTED = ["nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantize",
             "nvfp4_gemm", "qadamw_v_workspace_bytes", "qadamw_v_encode", "qadamw_v_decode",
             "nvfp4_status_string", "nvfp4_abi_version", "qadamw_step_workspace_bytes",
-            "qadamw_step", "nvfp4_gemm_lora"]
+            "qadamw_step", "nvfp4_gemm_lora", "nvfp4_quantize_lora_workspace_bytes",
+            "nvfp4_quantize_lora"]
 
 
 class Nvfp4Error(RuntimeError):
@@ -83,6 +84,11 @@ def load_library(path: Optional[str] = None):
     lib.nvfp4_dequantize.argtypes = [P(QTensorC), i64, i64, ctypes.c_int, vp, i64, vp]
     lib.nvfp4_gemm.restype = ctypes.c_int
     lib.nvfp4_gemm.argtypes = [P(QTensorC), P(QTensorC), i64, i64, i64, vp, i64, vp]
+    lib.nvfp4_quantize_lora_workspace_bytes.restype = sz
+    lib.nvfp4_quantize_lora_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.nvfp4_quantize_lora.restype = ctypes.c_int
+    lib.nvfp4_quantize_lora.argtypes = [vp, ctypes.c_int, i64, i64, i64, P(QuantParams), P(QTensorC),
+                                        P(QTensorC), vp, i64, ctypes.c_float, vp, vp, sz, vp]
     lib.nvfp4_gemm_lora.restype = ctypes.c_int
     lib.nvfp4_gemm_lora.argtypes = [P(QTensorC), P(QTensorC), i64, i64, i64, vp, i64, vp, vp, i64,
                                     vp]
@@ -222,6 +228,40 @@ def nvfp4_gemm(a, b, out=None):
     _check(lib.nvfp4_gemm(ctypes.byref(ac), ctypes.byref(bc), M, N, K, _ptr(out), out.stride(0),
                           _stream(out.device)))
     return out
+
+
+def nvfp4_quantize_lora(x, params, lora_a, beta, row_out=None, col_out=None, lora_t=None,
+                        workspace=None):
+    """nvfp4_quantize of a bfloat16 x with the LoRA-SVD down-projection
+    lora_t = BF16(beta x lora_a^T) fused into its first pass; returns (row, col, lora_t)."""
+    lib = load_library()
+    _require_cuda(x, lora_a)
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise Nvfp4Error("x must be a 2-D bfloat16 tensor with unit column stride")
+    if lora_a.dtype != torch.bfloat16 or not lora_a.is_contiguous() or lora_a.dim() != 2:
+        raise Nvfp4Error("lora_a must be a contiguous 2-D bfloat16 tensor")
+    R, C = x.shape
+    rank = lora_a.shape[0]
+    if lora_a.shape[1] != C:
+        raise Nvfp4Error(f"lora_a has {lora_a.shape[1]} columns, x {C}")
+    dev = x.device
+    if params.rowwise and row_out is None:
+        row_out = QTensor.empty(R, C, dev)
+    if params.colwise and col_out is None:
+        col_out = QTensor.empty(C, R, dev)
+    if lora_t is None:
+        lora_t = torch.empty((R, rank), dtype=torch.bfloat16, device=dev)
+    need = int(lib.nvfp4_quantize_lora_workspace_bytes(R, C, rank))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    rc_ = row_out.c() if params.rowwise else None
+    cc_ = col_out.c() if params.colwise else None
+    _check(lib.nvfp4_quantize_lora(_ptr(x), NVFP4_BF16, R, C, x.stride(0), ctypes.byref(params),
+                                   ctypes.byref(rc_) if rc_ is not None else None,
+                                   ctypes.byref(cc_) if cc_ is not None else None,
+                                   _ptr(lora_a), rank, float(beta), _ptr(lora_t), _ptr(workspace),
+                                   workspace.numel(), _stream(dev)))
+    return (row_out if params.rowwise else None), (col_out if params.colwise else None), lora_t
 
 
 def nvfp4_gemm_lora(a, b, t, lb, out=None):

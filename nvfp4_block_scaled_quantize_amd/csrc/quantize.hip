@@ -76,10 +76,36 @@ static int check_qtensor(const nvfp4_qtensor* q) {
     return NVFP4_OK;
 }
 
-extern "C" int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
-                              const nvfp4_quant_params* p, const nvfp4_qtensor* row_out,
-                              const nvfp4_qtensor* col_out, void* ws, size_t ws_bytes,
-                              void* stream) {
+// LoRA first pass: 64-row blocks times K-parts of kp columns (a multiple of 128), with about
+// 768 workgroups in all.
+struct LoraSplit {
+    int64_t row_blocks, parts, kp;
+};
+static LoraSplit lora_split(int64_t rows, int64_t cols) {
+    LoraSplit s;
+    s.row_blocks = (rows + kLoraRowsWG - 1) / kLoraRowsWG;
+    const int64_t steps = (cols + kLoraStep - 1) / kLoraStep;
+    int64_t target = (768 + s.row_blocks - 1) / (s.row_blocks > 0 ? s.row_blocks : 1);
+    if (target < 1) target = 1;
+    const int64_t steps_per_part = (steps + target - 1) / target;
+    s.kp = (steps_per_part > 0 ? steps_per_part : 1) * kLoraStep;
+    s.parts = (cols + s.kp - 1) / s.kp;
+    return s;
+}
+
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+extern "C" size_t nvfp4_quantize_lora_workspace_bytes(int64_t rows, int64_t cols, int64_t rank) {
+    if (rows <= 0 || cols <= 0 || rank <= 0) return 0;
+    const LoraSplit sp = lora_split(rows, cols);
+    return align256((size_t)(sp.row_blocks * sp.parts) * 2 * sizeof(float)) +
+           (size_t)(sp.parts * rows * rank) * sizeof(float);
+}
+
+static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                         const nvfp4_quant_params* p, const nvfp4_qtensor* row_out,
+                         const nvfp4_qtensor* col_out, const uint16_t* lora_a, int64_t rank,
+                         float beta, uint16_t* lora_t, void* ws, size_t ws_bytes, void* stream) {
     if (!p) return NVFP4_ERR_NULL;
     if (dtype != NVFP4_F32 && dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
     if (rows < 0 || cols < 0 || rows % 16 || cols % 16 || ld_x < cols) return NVFP4_ERR_SHAPE;
@@ -109,7 +135,8 @@ extern "C" int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t co
     if (!x) return NVFP4_ERR_NULL;
     const int64_t esize = dtype == NVFP4_BF16 ? 2 : 4;
     if (!aligned(x, 16) || (ld_x * esize) % 16) return NVFP4_ERR_ALIGN;
-    const size_t need = nvfp4_quantize_workspace_bytes(rows, cols, p);
+    const size_t need = lora_t ? nvfp4_quantize_lora_workspace_bytes(rows, cols, rank)
+                               : nvfp4_quantize_workspace_bytes(rows, cols, p);
     if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
     if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
 
@@ -137,7 +164,24 @@ extern "C" int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t co
     a.csg = a.colwise ? col_out->gscale : nullptr;
     a.partial = (float*)ws;
     a.ntiles = (int)quant_tiles(rows, cols, &a.tiles_c);
-    {   // k_amax: one wave per 16 x 512 wave tile, four per workgroup, at most about one
+    a.lora_a = nullptr;
+    a.lora_t = nullptr;
+    a.lora_part = nullptr;
+    a.lora_r = 0;
+    a.lora_parts = 0;
+    a.lora_kp = 0;
+    a.lora_beta = 0.0f;
+    if (lora_t) {   // the first pass is k_amax_lora: one workgroup per 64 rows and K-part
+        const LoraSplit sp = lora_split(rows, cols);
+        a.npart = (int)(sp.row_blocks * sp.parts);
+        a.lora_a = lora_a;
+        a.lora_t = lora_t;
+        a.lora_part = (float*)((uint8_t*)ws + align256((size_t)a.npart * 2 * sizeof(float)));
+        a.lora_r = (int)rank;
+        a.lora_parts = (int)sp.parts;
+        a.lora_kp = sp.kp;
+        a.lora_beta = beta;
+    } else {   // k_amax: one wave per 16 x 512 wave tile, four per workgroup, at most about one
         // round of resident workgroups (each then loops), never more than ntiles
         const int64_t wtiles = (rows / 16) * ((cols + kAmaxWaveCols - 1) / kAmaxWaveCols);
         int64_t np = (wtiles + 3) / 4;
@@ -151,6 +195,42 @@ extern "C" int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t co
     else
         (f < 8 ? launch_quant_f32_lo : launch_quant_f32_hi)(f, a, st);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+extern "C" int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                              const nvfp4_quant_params* p, const nvfp4_qtensor* row_out,
+                              const nvfp4_qtensor* col_out, void* ws, size_t ws_bytes,
+                              void* stream) {
+    return quantize_impl(x, dtype, rows, cols, ld_x, p, row_out, col_out, nullptr, 0, 0.0f,
+                         nullptr, ws, ws_bytes, stream);
+}
+
+__global__ void k_fill_u16(uint16_t* p, int64_t n, uint16_t v) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+extern "C" int nvfp4_quantize_lora(const void* x, int dtype, int64_t rows, int64_t cols,
+                                   int64_t ld_x, const nvfp4_quant_params* p,
+                                   const nvfp4_qtensor* row_out, const nvfp4_qtensor* col_out,
+                                   const uint16_t* lora_a, int64_t rank, float beta,
+                                   uint16_t* lora_t, void* ws, size_t ws_bytes, void* stream) {
+    if (!p) return NVFP4_ERR_NULL;
+    if (dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+    if (rank <= 0 || rank % 16 || rank > kLoraMaxRank) return NVFP4_ERR_SHAPE;
+    if (rows < 0 || cols < 0 || cols % kLoraStep) return NVFP4_ERR_SHAPE;
+    if (!lora_a || !lora_t) return NVFP4_ERR_NULL;
+    if (((uintptr_t)lora_a & 15) || ((uintptr_t)lora_t & 1)) return NVFP4_ERR_ALIGN;
+    if (rows > 0 && cols == 0) {   // an empty contraction: T = 0
+        int rc = quantize_impl(x, dtype, rows, cols, ld_x, p, row_out, col_out, nullptr, 0, 0.0f,
+                               nullptr, ws, ws_bytes, stream);
+        if (rc != NVFP4_OK) return rc;
+        const int64_t n = rows * rank;
+        k_fill_u16<<<(unsigned)((n + 255) / 256), 256, 0, (hipStream_t)stream>>>(lora_t, n, 0);
+        return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+    }
+    return quantize_impl(x, dtype, rows, cols, ld_x, p, row_out, col_out, lora_a, rank, beta,
+                         rows > 0 ? lora_t : nullptr, ws, ws_bytes, stream);
 }
 
 extern "C" int nvfp4_dequantize(const nvfp4_qtensor* q, int64_t n, int64_t k, int out_dtype,

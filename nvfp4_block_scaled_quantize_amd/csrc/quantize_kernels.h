@@ -46,7 +46,16 @@ struct QArgs {
     float* partial;  // [2][npart]: rowwise-copy and columnwise-copy amax per k_amax workgroup
     int tiles_c;
     int ntiles;
-    int npart;       // k_amax workgroups (<= ntiles)
+    int npart;       // first-pass workgroups, one partial maximum each per copy
+    // LoRA-SVD down-projection (lora_t null: none): lora_t[rows][lora_r] = BF16(beta x a^T)
+    // with a = lora_a[lora_r][cols]; the first pass leaves one FP32 partial per K-part of
+    // lora_kp columns in lora_part[lora_parts][rows][lora_r], the encode pass sums them.
+    const uint16_t* lora_a;
+    uint16_t* lora_t;
+    float* lora_part;
+    int lora_r, lora_parts;
+    int64_t lora_kp;
+    float lora_beta;
 };
 
 // One thread's 16-row x 8-column input patch.  bfloat16 stays packed two to a register
@@ -382,6 +391,17 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
     Patch<BF16> P;
     P.load(a.x, a.ld, r0, c0, valid);
 
+    // LoRA-SVD down-projection: T = BF16(beta * sum of the K-part partials, in part order)
+    if (a.lora_t) {
+        const int64_t total = a.rows * a.lora_r;
+        for (int64_t e = (int64_t)blockIdx.x * kThreads + t; e < total;
+             e += (int64_t)gridDim.x * kThreads) {
+            float sum = 0.0f;
+            for (int q = 0; q < a.lora_parts; ++q) sum += a.lora_part[q * total + e];
+            a.lora_t[e] = (uint16_t)f32_to_bf16_rne(sum * a.lora_beta);
+        }
+    }
+
     // tensor scales from the per-tile partial maxima
     float mr = 0.0f, mc = 0.0f;
     for (int i = t; i < a.npart; i += kThreads) {
@@ -536,9 +556,172 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
 }
 
 
+// ---------------------------------------------------------------- LoRA-SVD first pass
+// The quantizer's first pass with the LoRA-SVD down-projection fused in (Full-Stack FP4
+// sec. 3.2 eq. (1) and Appendix 9: the down-projection X L1^T reuses the quantizer's input
+// read).  Work decomposition: a workgroup takes 64 rows (16 per wave) and one K-part of
+// lora_kp columns, in steps of 128 columns.  Lane (i, g) of a wave (i = lane mod 16,
+// g = lane / 16) loads 32 consecutive bfloat16 of row i, columns 32g .. 32g + 31 of the
+// step; these 16 registers are at once
+//  * the A operands of four BF16 MFMAs 16x16x32: k-step j takes columns 32g + 8j .. +7 as
+//    the MFMA's k-slots 8g .. 8g + 7, and the B operands (the step's 128 columns of a, one
+//    16 x 128 slice per MFMA column block, staged in LDS by the workgroup) follow the same
+//    correspondence, so every column is summed exactly once;
+//  * the input of the partial maxima of k_amax: plain and row-rotated in-register (the
+//    lane holds two whole 16-chunks of its row), column-rotated across the 16 lanes that
+//    hold one 16-row chunk (stages 1 and 2 by DPP quad permutations, 4 and 8 by swizzles).
+// The low-rank partial of each K-part goes to lora_part; k_encode sums the parts in order.
+constexpr int kLoraStep = 128;
+constexpr int kLoraRowsWG = 64;
+constexpr int kLoraMaxRank = 64;
+typedef __bf16 bf16x8t __attribute__((ext_vector_type(8)));
+typedef float f32x4t __attribute__((ext_vector_type(4)));
+
+// The value of the lane whose index within the 16-lane row differs in bit H.
+template <int H>
+__device__ __forceinline__ float row_lane_xor(float v) {
+    const int b = __float_as_int(v);
+    if constexpr (H == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false));
+    else if constexpr (H == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false));
+    else return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x1F | (H << 10)));
+}
+
+// One butterfly stage of the column transform: lanes with bit H of their row index clear
+// take a + b, the others a - b (a the lower row's value, b the upper row's).
+template <int H>
+__device__ __forceinline__ float col_stage(float w, float sgn) {
+    return __builtin_fmaf(w, sgn, row_lane_xor<H>(w));
+}
+
+template <int H>
+__global__ __launch_bounds__(kThreads) void k_amax_lora(QArgs a) {
+    constexpr bool RHT_ROW = H & 1, RHT_COL = (H >> 1) & 1;
+    __shared__ uint4 bl[kLoraMaxRank * (kLoraStep / 8)];   // [rank][16 chunks], chunk ^ (row & 15)
+    __shared__ float red[8];
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int i = lane & 15, g = lane >> 4;
+    const int rblk = blockIdx.x / a.lora_parts, part = blockIdx.x % a.lora_parts;
+    const int64_t row = (int64_t)rblk * kLoraRowsWG + wid * 16 + i;
+    const bool rvalid = row < a.rows;
+    const int64_t kb = (int64_t)part * a.lora_kp;
+    const int64_t ke = kb + a.lora_kp < a.cols ? kb + a.lora_kp : a.cols;
+    const int nq = a.lora_r / 16;
+    const uint32_t signs =
+        (RHT_ROW || RHT_COL) ? __builtin_amdgcn_readfirstlane(rht_sign_bits(a.k0, a.k1)) : 0u;
+    const uint32_t cmask = RHT_COL ? col_sign_mask(signs, i) : 0u;
+    float sgn[4];   // butterfly sign of this lane's row index at stages 1, 2, 4, 8
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sgn[s] = (i >> s) & 1 ? -1.0f : 1.0f;
+    const uint16_t* xrow = (const uint16_t*)a.x + row * a.ld;
+
+    f32x4t acc[kLoraMaxRank / 16];
+#pragma unroll
+    for (int q = 0; q < kLoraMaxRank / 16; ++q) acc[q] = f32x4t{0.0f, 0.0f, 0.0f, 0.0f};
+    float mr = 0.0f, mc = 0.0f;
+
+    for (int64_t c = kb; c < ke; c += kLoraStep) {
+        __syncthreads();   // the previous step's slice of a has been read
+        for (int q = t; q < a.lora_r * 16; q += kThreads) {
+            const int rr = q >> 4, ch = q & 15;
+            bl[rr * 16 + (ch ^ (rr & 15))] = *(const uint4*)(a.lora_a + (int64_t)rr * a.cols + c + ch * 8);
+        }
+        uint32_t xw[16];
+        if (rvalid) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint4 u = *(const uint4*)(xrow + c + 32 * g + 8 * q);
+                xw[4 * q] = u.x; xw[4 * q + 1] = u.y; xw[4 * q + 2] = u.z; xw[4 * q + 3] = u.w;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) xw[q] = 0u;
+        }
+
+        // partial maxima
+        if ((a.rowwise && !RHT_ROW) || (a.colwise && !RHT_COL)) {
+            typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+            u16x2 m = {0, 0};
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, xw[q] & 0x7FFF7FFFu));
+            const float pm = fmaxf(__uint_as_float((uint32_t)m.x << 16), __uint_as_float((uint32_t)m.y << 16));
+            if (!RHT_ROW) mr = fmaxf(mr, pm);
+            if (!RHT_COL) mc = fmaxf(mc, pm);
+        }
+        if (RHT_ROW) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                float w[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const uint32_t d = xw[8 * hf + e / 2];
+                    w[e] = apply_sign(__uint_as_float((e & 1) ? (d & 0xFFFF0000u) : (d << 16)), signs, e);
+                }
+                wht16(w);
+                mr = fmaxf(mr, fmaxf(amax8(&w[0]), amax8(&w[8])));
+            }
+        }
+        if (RHT_COL) {
+            float am = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const uint32_t d = xw[q] ^ cmask;
+                float w0 = __uint_as_float(d << 16), w1 = __uint_as_float(d & 0xFFFF0000u);
+                w0 = col_stage<1>(w0, sgn[0]); w1 = col_stage<1>(w1, sgn[0]);
+                w0 = col_stage<2>(w0, sgn[1]); w1 = col_stage<2>(w1, sgn[1]);
+                w0 = col_stage<4>(w0, sgn[2]); w1 = col_stage<4>(w1, sgn[2]);
+                w0 = col_stage<8>(w0, sgn[3]); w1 = col_stage<8>(w1, sgn[3]);
+                am = fmaxf(am, fmaxf(fabsf(w0), fabsf(w1)));
+                if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+            mc = fmaxf(mc, am);
+        }
+
+        __syncthreads();   // the slice of a is in LDS
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8t av = __builtin_bit_cast(bf16x8t, make_uint4(xw[4 * j], xw[4 * j + 1], xw[4 * j + 2], xw[4 * j + 3]));
+#pragma unroll
+            for (int q = 0; q < kLoraMaxRank / 16; ++q) {
+                if (q < nq) {
+                    const int rr = 16 * q + i;
+                    const bf16x8t bv = __builtin_bit_cast(bf16x8t, bl[rr * 16 + ((4 * g + j) ^ (rr & 15))]);
+                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[q], 0, 0, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if (RHT_ROW) mr = mr * 0.25f;
+    if (RHT_COL) mc = mc * 0.25f;
+
+    // the K-part's partial of T: lane holds rows 4g .. 4g + 3 of column 16q + i of block q
+    const int64_t total = a.rows * a.lora_r;
+#pragma unroll
+    for (int q = 0; q < kLoraMaxRank / 16; ++q) {
+        if (q < nq) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t r = (int64_t)rblk * kLoraRowsWG + wid * 16 + 4 * g + v;
+                if (r < a.rows) a.lora_part[part * total + r * a.lora_r + 16 * q + i] = acc[q][v];
+            }
+        }
+    }
+    block_max2(mr, mc, red);
+    if (t == 0) {
+        a.partial[blockIdx.x] = mr;
+        a.partial[a.npart + blockIdx.x] = mc;
+    }
+}
+
 template <bool BF16, int F>
 void launch_quant(const QArgs& a, hipStream_t st) {
-    k_amax<BF16, (F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
+    if constexpr (BF16) {
+        if (a.lora_t) k_amax_lora<(F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
+        else k_amax<BF16, (F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
+    } else {
+        k_amax<BF16, (F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
+    }
     k_encode<BF16, F><<<a.ntiles, kThreads, 0, st>>>(a);
 }
 

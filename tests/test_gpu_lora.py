@@ -87,3 +87,96 @@ def test_gemm_lora_rejects_bad_rank(nv, oracle):
     t = torch.zeros((32, 8), dtype=torch.bfloat16, device=dev())
     with pytest.raises(nv.Nvfp4Error):
         nv.nvfp4_gemm_lora(ga, gb, t, t.clone())
+
+
+# ---------------------------------------------------------------- fused down-projection
+# nvfp4_quantize_lora: the NVFP4 copies must equal the oracle's bit for bit (the first pass
+# computes the tensor amax too), and T = BF16(beta x a^T) is compared with the oracle's
+# binary64 value: either the same BF16 value, or within half a BF16 ulp of the exact value
+# plus the FP32 accumulation bound (cols + 1) 2^-24 |beta| sum |x a|; almost all elements
+# must be the same value.
+def bf16_to_np(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_vals(b):
+    return (np.asarray(b, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_lora_t(t_gpu, t_or, t64, tabs, cols):
+    got, want = bf16_vals(t_gpu), bf16_vals(t_or)
+    same = got == want
+    ulp = np.maximum(np.abs(want), 2.0 ** -126) * 2.0 ** -7
+    bound = 0.5 * ulp + (cols + 1) * 2.0 ** -24 * tabs
+    assert np.all(same | (np.abs(got - t64) <= bound)), "low-rank values outside the bound"
+    assert same.mean() > 0.99, f"only {same.mean():.4f} of the low-rank values agree"
+
+
+LORA_MODES = {
+    "row": dict(rowwise=True),
+    "row+colRHT": dict(rowwise=True, colwise=True, rht_col=True, seed=0x5EED4),
+    "rowRHT+colRHT SR": dict(rowwise=True, colwise=True, rht_row=True, rht_col=True,
+                            round_row=1, round_col=1, seed=0x5EED4),
+    "rowRHT": dict(rowwise=True, rht_row=True, seed=11),
+    "col": dict(rowwise=False, colwise=True),
+}
+
+
+@pytest.mark.parametrize("mode", list(LORA_MODES))
+@pytest.mark.parametrize("R,C,r", [(64, 128, 16), (48, 256, 32), (272, 384, 64), (528, 640, 48)])
+def test_quantize_lora_small(nv, oracle, mode, R, C, r):
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    from gpu_util import assert_copy_equal
+    print(f"quantize_lora {mode} {R}x{C} rank {r}", flush=True)
+    x = synthetic.outlier_channels((R, C), R + C + r).to(torch.bfloat16)
+    la = synthetic.normal((r, C), 7 + r, C ** -0.5).to(torch.bfloat16)
+    beta = 0.5
+    kw = LORA_MODES[mode]
+    p = nv.quant_params(**kw)
+    row, col, t = nv.nvfp4_quantize_lora(x.to(dev()), p, la.to(dev()), beta)
+    torch.cuda.synchronize()
+    xo = x.float().numpy()
+    okw = dict(rowwise=kw.get("rowwise", True), colwise=kw.get("colwise", False),
+               round_row=kw.get("round_row", 0), round_col=kw.get("round_col", 0),
+               rht_row=kw.get("rht_row", False), rht_col=kw.get("rht_col", False),
+               seed=kw.get("seed", 0))
+    orow, ocol = oracle.quantize(xo, **okw)
+    if okw["rowwise"]:
+        assert_copy_equal(row, orow, "rowwise")
+    if okw["colwise"]:
+        assert_copy_equal(col, ocol, "colwise")
+    t_or, t64, tabs = oracle.lora_down(xo, bf16_to_np(la), beta)
+    check_lora_t(bf16_to_np(t), t_or, t64, tabs, C)
+
+
+def test_quantize_lora_full_size_x(nv, oracle):
+    """X 8192x3072 (row + column RHT copies) with the rank-64 down-projection of L1."""
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    from gpu_util import assert_copy_equal
+    print("quantize_lora full-size X 8192x3072 rank 64", flush=True)
+    x = synthetic.ffn()["X"]
+    lo = synthetic.lora()
+    p = nv.quant_params(rowwise=True, colwise=True, rht_col=True, seed=0x5EED4)
+    row, col, t = nv.nvfp4_quantize_lora(x.to(dev()), p, lo["L1"].to(dev()), lo["beta"])
+    torch.cuda.synchronize()
+    xo = x.float().numpy()
+    orow, ocol = oracle.quantize(xo, rowwise=True, colwise=True, rht_col=True, seed=0x5EED4)
+    assert_copy_equal(row, orow, "rowwise")
+    assert_copy_equal(col, ocol, "colwise")
+    rows = np.random.default_rng(3).choice(8192, 256, replace=False)
+    t_or, t64, tabs = oracle.lora_down(xo[rows], bf16_to_np(lo["L1"]), lo["beta"])
+    check_lora_t(bf16_to_np(t)[rows], t_or, t64, tabs, 3072)
+
+
+def test_quantize_lora_limits(nv):
+    x = torch.zeros((64, 128), dtype=torch.bfloat16, device=dev())
+    p = nv.quant_params(rowwise=True)
+    with pytest.raises(nv.Nvfp4Error):   # rank above 64
+        nv.nvfp4_quantize_lora(x, p, torch.zeros((80, 128), dtype=torch.bfloat16, device=dev()), 1.0)
+    with pytest.raises(nv.Nvfp4Error):   # cols not a multiple of 128
+        nv.nvfp4_quantize_lora(torch.zeros((64, 96), dtype=torch.bfloat16, device=dev()), p,
+                               torch.zeros((16, 96), dtype=torch.bfloat16, device=dev()), 1.0)
+    # zero input: T = 0 and the copies of a zero tensor
+    row, _, t = nv.nvfp4_quantize_lora(x, p, torch.ones((16, 128), dtype=torch.bfloat16, device=dev()), 1.0)
+    torch.cuda.synchronize()
+    assert torch.all(t == 0) and row.gscale.item() == 1.0
