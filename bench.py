@@ -428,16 +428,19 @@ def main():
         "kernels": kernels,
     }
 
-    out["extras"] = extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, stream)
+    out["extras"] = extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, synthetic, ffn)
     print(json.dumps(out))
 
 
-def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, stream, iters=20):
+def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream, iters=20):
     """Measurements outside the step, same method (HIP events on the launch stream):
-    the X and dY quantizes with 4/6 adaptive block scaling, the QKV-projection GEMM of the
-    3B model, and a plain device copy for the box's achievable HBM bandwidth."""
+    the X and dY quantizes with 4/6 adaptive block scaling; the LoRA-SVD branch at rank 64
+    (X quantize with the L1 down-projection fused, FFN-up GEMM with the L2 up-projection
+    fused, and for dX the dY quantize with L2^T and the dgrad GEMM with L1^T); the
+    QKV-projection GEMM of the 3B model; a plain device copy for the box's achievable HBM
+    bandwidth."""
     qkv = synthetic.qkv()
     Xq, Wqkv = qkv["X"].to(dev), qkv["W"].to(dev)
     p46x = nv.quant_params(rowwise=True, colwise=True, rht_col=True, seed=SEED_WGRAD, scale46=True)
@@ -451,11 +454,43 @@ def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, stream, iters=2
     dst = torch.empty_like(src)
     M, K = Xq.shape
     N = Wqkv.shape[0]
+    lo = synthetic.lora()
+    R = lo["L1"].shape[0]
+    L1 = lo["L1"].to(dev)                                # [r][hidden]
+    L2 = lo["L2"].to(dev)                                # [ffn][r]
+    L1T = lo["L1"].t().contiguous().to(dev)              # [hidden][r]
+    L2T = lo["L2"].t().contiguous().to(dev)              # [r][ffn]
+    tx = torch.empty((TOKENS, R), dtype=torch.bfloat16, device=dev)
+    tdy = torch.empty((TOKENS, R), dtype=torch.bfloat16, device=dev)
+    wsx = torch.empty(nv.load_library().nvfp4_quantize_lora_workspace_bytes(TOKENS, HIDDEN, R),
+                      dtype=torch.uint8, device=dev)
+    wsdy = torch.empty(nv.load_library().nvfp4_quantize_lora_workspace_bytes(TOKENS, FFN, R),
+                       dtype=torch.uint8, device=dev)
+    nv.nvfp4_quantize_lora(X, p_x, L1, lo["beta"], qx[0], qx[1], tx, wsx)
+    nv.nvfp4_quantize_lora(dY, p_dy, L2T, lo["beta"], qdy[0], qdy[1], tdy, wsdy)
+    Yl = torch.empty((TOKENS, FFN), dtype=torch.float32, device=dev)
+    dXl = torch.empty((TOKENS, HIDDEN), dtype=torch.float32, device=dev)
     cases = {
         "quant_X_row+colRHT_4/6": (lambda: nv.nvfp4_quantize(X, p46x, qx[0], qx[1], qx[2]),
                                    2 * TOKENS * HIDDEN + 2 * qbytes(TOKENS, HIDDEN), 0),
         "quant_dY_rowSR+colRHTSR_4/6": (lambda: nv.nvfp4_quantize(dY, p46dy, qdy[0], qdy[1], qdy[2]),
                                         2 * TOKENS * FFN + 2 * qbytes(TOKENS, FFN), 0),
+        "quant_X_row+colRHT_lora_r64": (
+            lambda: nv.nvfp4_quantize_lora(X, p_x, L1, lo["beta"], qx[0], qx[1], tx, wsx),
+            2 * TOKENS * HIDDEN + 2 * qbytes(TOKENS, HIDDEN) + 2 * TOKENS * R + 2 * R * HIDDEN,
+            2 * TOKENS * HIDDEN * R),
+        "gemm_ffn_up_lora_r64": (lambda: nv.nvfp4_gemm_lora(qx[0], qw[0], tx, L2, out=Yl),
+                                 qbytes(TOKENS, HIDDEN) + qbytes(FFN, HIDDEN) + 4 * TOKENS * FFN
+                                 + 2 * TOKENS * R + 2 * FFN * R,
+                                 2 * TOKENS * FFN * HIDDEN + 2 * TOKENS * FFN * R),
+        "quant_dY_rowSR+colRHTSR_lora_r64": (
+            lambda: nv.nvfp4_quantize_lora(dY, p_dy, L2T, lo["beta"], qdy[0], qdy[1], tdy, wsdy),
+            2 * TOKENS * FFN + 2 * qbytes(TOKENS, FFN) + 2 * TOKENS * R + 2 * R * FFN,
+            2 * TOKENS * FFN * R),
+        "gemm_dgrad_lora_r64": (lambda: nv.nvfp4_gemm_lora(qdy[0], qw[1], tdy, L1T, out=dXl),
+                                qbytes(TOKENS, FFN) + qbytes(HIDDEN, FFN) + 4 * TOKENS * HIDDEN
+                                + 2 * TOKENS * R + 2 * HIDDEN * R,
+                                2 * TOKENS * HIDDEN * FFN + 2 * TOKENS * HIDDEN * R),
         "gemm_qkv_8192x6144x3072": (lambda: nv.nvfp4_gemm(qa, qb, out=C),
                                     qbytes(M, K) + qbytes(N, K) + 4 * M * N, 2 * M * N * K),
         "hbm_copy_256MiB": (lambda: dst.copy_(src), 2 * (256 << 20), 0),
@@ -473,7 +508,9 @@ def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, stream, iters=2
         torch.cuda.synchronize()
         ms = s.elapsed_time(e) / iters
         d = {"ms": round(ms, 5), "GB/s": round(nbytes / ms / 1e6, 1)}
-        if flops:
+        if flops and name.startswith("quant"):
+            d["frac_hbm_peak"] = round(nbytes / ms / 1e6 / PEAK_HBM_GBPS, 4)
+        elif flops:
             d["TFLOP/s"] = round(flops / ms / 1e9, 1)
             d["frac_f16_peak"] = round(flops / ms / 1e9 / PEAK_F16_TFLOPS, 4)
         else:

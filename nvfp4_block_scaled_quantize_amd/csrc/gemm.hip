@@ -203,55 +203,81 @@ __device__ __forceinline__ void store_tile(const GArgs& g, const float16v (&acc)
 }
 
 // LoRA-SVD up-projection in the epilogue (Full-Stack FP4 sec. 3.2 eq. (1), Appendix 9: the
-// low-rank branch shares the GEMM's output tile).  For each 32-row block row of the wave's
-// sub-tile, T L^T is formed by BF16 MFMAs (32x32x16, FP32 accumulate, from zero) over the
-// rank in steps of 16, and each output is stored as fl(acc s_gA s_gB) + that term.  Lane
-// (li, h) supplies row li of the block and the rank entries 8h..8h+7 of the step: 16
-// contiguous bytes of T and of L.
+// low-rank branch shares the GEMM's output tile).  After the main loop the stage buffers are
+// free: the workgroup copies its 256 rows of T and of L, 64 rank entries at a time, into
+// LDS (one round trip instead of one per MFMA operand), then each accumulator block is
+// scaled by s_gA s_gB into a temporary that BF16 MFMAs 32x32x16 (FP32 accumulate) take as C,
+// written back in place.  LDS rows hold 8 chunks of 16 bytes, chunk c at c ^ (row mod 8),
+// so the fragment reads (16 bytes of 32 consecutive rows per half-wave) spread over the
+// banks.  Lane (li, h) supplies row li of the block and rank entries 8h..8h+7 of a step.
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+constexpr int kLoraChunk = 64;                    // rank entries staged per round
+constexpr int kLoraLdsRow = kLoraChunk * 2;       // bytes per staged row
 
-__device__ __forceinline__ bf16x8v load_bf16x8(const uint16_t* base, int64_t row, int64_t rows,
-                                               int64_t ld, int64_t col) {
-    uint4 q = make_uint4(0u, 0u, 0u, 0u);
-    if (row < rows) q = *(const uint4*)(base + row * ld + col);
-    return __builtin_bit_cast(bf16x8v, q);
+__device__ __forceinline__ void stage_lora(const GArgs& g, uint8_t* lds, int64_t m0, int64_t n0,
+                                           int64_t k0, int kc) {
+    // kc rank entries (a multiple of 16) from k0, rows of T then rows of L
+    const int chunks = kc / 8;                    // 16-byte chunks per row
+    for (int q = threadIdx.x; q < 2 * GBM * chunks; q += GThreads) {
+        const int which = q / (GBM * chunks), rem = q % (GBM * chunks);
+        const int row = rem / chunks, ch = rem % chunks;
+        const int64_t grow = (which ? n0 : m0) + row;
+        const int64_t rows = which ? g.N : g.M;
+        const uint16_t* src = which ? g.lb : g.lt;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (grow < rows) v = *(const uint4*)(src + grow * g.lr + k0 + ch * 8);
+        *(uint4*)(lds + which * GBM * kLoraLdsRow + row * kLoraLdsRow + ((ch ^ (row & 7)) << 4)) = v;
+    }
 }
 
-__device__ __forceinline__ void store_tile_lora(const GArgs& g, float16v (&acc)[4][4],
-                                                int64_t m0, int64_t n0, int wm, int wn, int h,
-                                                int li) {
+__device__ __forceinline__ bf16x8v lds_frag(const uint8_t* lds, int which, int row, int ch) {
+    return __builtin_bit_cast(bf16x8v, *(const uint4*)(lds + which * GBM * kLoraLdsRow +
+                                                        row * kLoraLdsRow + ((ch ^ (row & 7)) << 4)));
+}
+
+__device__ __forceinline__ void lora_epilogue(const GArgs& g, uint8_t* lds, float16v (&acc)[4][4],
+                                              int64_t m0, int64_t n0, int wm, int wn, int h, int li) {
     const float scale = *g.asg * *g.bsg;
-    const int64_t ra = m0 + wm * 128 + li, rb = n0 + wn * 128 + li;
+    const int ra = wm * 128 + li, rb = wn * 128 + li;
+    for (int64_t k0 = 0; k0 < g.lr; k0 += kLoraChunk) {
+        const int kc = g.lr - k0 < kLoraChunk ? (int)(g.lr - k0) : kLoraChunk;
+        __syncthreads();   // every wave is done with the stage buffers (or the previous chunk)
+        stage_lora(g, lds, m0, n0, k0, kc);
+        __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        // block row i: each accumulator block is scaled into a temporary that the low-rank
-        // MFMAs take as C and write back in place (the block's own registers)
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float16v c;
+            for (int j = 0; j < 4; ++j) {
+                float16v c;
+                if (k0 == 0) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) c[r] = acc[i][j][r] * scale;
-            for (int64_t s = 0; s < g.lr; s += 16) {
-                const bf16x8v a = load_bf16x8(g.lt, ra + 32 * i, g.M, g.lr, s + 8 * h);
-                const bf16x8v b = load_bf16x8(g.lb, rb + 32 * j, g.N, g.lr, s + 8 * h);
-                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+                    for (int r = 0; r < 16; ++r) c[r] = acc[i][j][r] * scale;
+                } else {
+                    c = acc[i][j];
+                }
+                for (int s = 0; s < kc; s += 16) {
+                    const bf16x8v a = lds_frag(lds, 0, ra + 32 * i, s / 8 + h);
+                    const bf16x8v b = lds_frag(lds, 1, rb + 32 * j, s / 8 + h);
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+                }
+                acc[i][j] = c;
             }
-            acc[i][j] = c;
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
-    store_tile(g, acc, m0, n0, wm, wn, h, li, 1.0f);
 }
 
 // The epilogue, with the low-rank term as a compile-time switch so that the plain kernels
 // keep their register allocation.
 template <bool LORA>
-__device__ __forceinline__ void finish_tile(const GArgs& g, float16v (&acc)[4][4], int64_t m0,
-                                            int64_t n0, int wm, int wn, int h, int li) {
-    if constexpr (LORA)
-        store_tile_lora(g, acc, m0, n0, wm, wn, h, li);
-    else
+__device__ __forceinline__ void finish_tile(const GArgs& g, uint8_t* lds, float16v (&acc)[4][4],
+                                            int64_t m0, int64_t n0, int wm, int wn, int h, int li) {
+    if constexpr (LORA) {
+        lora_epilogue(g, lds, acc, m0, n0, wm, wn, h, li);
+        store_tile(g, acc, m0, n0, wm, wn, h, li, 1.0f);
+    } else {
         store_tile(g, acc, m0, n0, wm, wn, h, li, *g.asg * *g.bsg);
+    }
 }
 
 // Tile of workgroup `bid`.  Workgroups are dealt to the eight XCDs round-robin (bid mod 8)
@@ -364,7 +390,7 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm(GArgs g) {
         if (s + 1 < nst) store_stage(lds + ((s + 1) & 1) * kStageBytes, regs);
         __syncthreads();
     }
-    finish_tile<LORA>(g, acc, m0, n0, wm, wn, h, li);
+    finish_tile<LORA>(g, lds, acc, m0, n0, wm, wn, h, li);
 }
 
 // ---------------------------------------------------------------- direct staging path
@@ -621,7 +647,7 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
     make_pairs<0>(sa, sb, p);
     decode_slot<0>(lo, p, av, bv);
     for (int s = 0; s < c.nst; ++s) piped_stage(c, s, lo, hi, sa, sb, p, av, bv, acc);
-    finish_tile<LORA>(g, acc, c.m0, c.n0, c.wm, c.wn, c.h, c.li);
+    finish_tile<LORA>(g, lds, acc, c.m0, c.n0, c.wm, c.wn, c.h, c.li);
 }
 
 }  // namespace nvfp4
@@ -654,6 +680,7 @@ static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M
     g.tiles_n = (int)tiles_n;
     const unsigned grid = (unsigned)(tiles_m * tiles_n);
     static_assert(kGemmDmaLds <= 160 * 1024 && kGemmLds <= 160 * 1024, "LDS budget");
+    static_assert(2 * GBM * kLoraLdsRow <= kGemmLds, "low-rank staging fits the stage buffers");
     // direct path: whole 4-byte scale words per row and stage, 32-bit buffer offsets
     const int64_t kbytes = K / 2, limit = (int64_t)kOutOfRange;
     const bool direct = K > 0 && K % 64 == 0 && ((uintptr_t)a->scales & 3) == 0 &&
