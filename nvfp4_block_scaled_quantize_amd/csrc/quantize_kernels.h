@@ -593,10 +593,121 @@ __device__ __forceinline__ float col_stage(float w, float sgn) {
     return __builtin_fmaf(w, sgn, row_lane_xor<H>(w));
 }
 
+// Step loads: this lane's 32 values of its row, and its share of the step's slice of a
+// (NQ 16-row blocks x 128 columns: NQ 16-byte chunks per thread, chunk q = t + 256 k).
+__device__ __forceinline__ void lora_load_x(const uint16_t* xrow, bool rvalid, int64_t c, int g,
+                                            uint4 (&xw)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        xw[q] = rvalid ? *(const uint4*)(xrow + c + 32 * g + 8 * q) : make_uint4(0u, 0u, 0u, 0u);
+}
+template <int NQ>
+__device__ __forceinline__ void lora_load_a(const QArgs& a, int64_t c, int t, uint4 (&lw)[NQ]) {
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+        const int q = t + kThreads * k;
+        lw[k] = *(const uint4*)(a.lora_a + (int64_t)(q >> 4) * a.cols + c + (q & 15) * 8);
+    }
+}
+template <int NQ>
+__device__ __forceinline__ void lora_store_a(uint4* bl, int t, const uint4 (&lw)[NQ]) {
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+        const int q = t + kThreads * k, rr = q >> 4, ch = q & 15;
+        bl[rr * 16 + (ch ^ (rr & 15))] = lw[k];
+    }
+}
+
+// The partial maxima of one step's 32 values (see k_amax_lora).
 template <int H>
+__device__ __forceinline__ void lora_step_amax(const QArgs& a, const uint4 (&xv)[4], uint32_t signs,
+                                               uint32_t cmask, const float (&sgn)[4], float& mr,
+                                               float& mc) {
+    constexpr bool RHT_ROW = H & 1, RHT_COL = (H >> 1) & 1;
+    uint32_t xw[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        xw[4 * q] = xv[q].x; xw[4 * q + 1] = xv[q].y; xw[4 * q + 2] = xv[q].z; xw[4 * q + 3] = xv[q].w;
+    }
+    if ((a.rowwise && !RHT_ROW) || (a.colwise && !RHT_COL)) {
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+        u16x2 m = {0, 0};
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, xw[q] & 0x7FFF7FFFu));
+        const float pm = fmaxf(__uint_as_float((uint32_t)m.x << 16), __uint_as_float((uint32_t)m.y << 16));
+        if (!RHT_ROW) mr = fmaxf(mr, pm);
+        if (!RHT_COL) mc = fmaxf(mc, pm);
+    }
+    if (RHT_ROW) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            float w[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t d = xw[8 * hf + e / 2];
+                w[e] = apply_sign(__uint_as_float((e & 1) ? (d & 0xFFFF0000u) : (d << 16)), signs, e);
+            }
+            wht16(w);
+            mr = fmaxf(mr, fmaxf(amax8(&w[0]), amax8(&w[8])));
+        }
+    }
+    if (RHT_COL) {
+        float am = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const uint32_t d = xw[q] ^ cmask;
+            float w0 = __uint_as_float(d << 16), w1 = __uint_as_float(d & 0xFFFF0000u);
+            w0 = col_stage<1>(w0, sgn[0]); w1 = col_stage<1>(w1, sgn[0]);
+            w0 = col_stage<2>(w0, sgn[1]); w1 = col_stage<2>(w1, sgn[1]);
+            w0 = col_stage<4>(w0, sgn[2]); w1 = col_stage<4>(w1, sgn[2]);
+            w0 = col_stage<8>(w0, sgn[3]); w1 = col_stage<8>(w1, sgn[3]);
+            am = fmaxf(am, fmaxf(fabsf(w0), fabsf(w1)));
+        }
+        mc = fmaxf(mc, am);
+    }
+}
+
+template <int NQ>
+__device__ __forceinline__ void lora_step_mma(const uint4 (&xv)[4], const uint4* bl, int i, int g,
+                                              f32x4t (&acc)[NQ]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bf16x8t av = __builtin_bit_cast(bf16x8t, xv[j]);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int rr = 16 * q + i;
+            const bf16x8t bv = __builtin_bit_cast(bf16x8t, bl[rr * 16 + ((4 * g + j) ^ (rr & 15))]);
+            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[q], 0, 0, 0);
+        }
+    }
+}
+
+// One 128-column step: its maxima and MFMAs from (xv, bl[cur]) while the loads of the next
+// step (xn, lw) are in flight; then the next slice of a goes to the other LDS buffer.
+template <int H, int NQ>
+__device__ __forceinline__ void lora_step(const QArgs& a, const uint4 (&xv)[4], uint4 (&xn)[4],
+                                          uint4 (&lw)[NQ], uint4* bcur, uint4* bnext, bool more,
+                                          int64_t cnext, const uint16_t* xrow, bool rvalid, int t,
+                                          int i, int g, uint32_t signs, uint32_t cmask,
+                                          const float (&sgn)[4], float& mr, float& mc,
+                                          f32x4t (&acc)[NQ]) {
+    if (more) {
+        lora_load_x(xrow, rvalid, cnext, g, xn);
+        lora_load_a<NQ>(a, cnext, t, lw);
+    }
+    lora_step_amax<H>(a, xv, signs, cmask, sgn, mr, mc);
+    lora_step_mma<NQ>(xv, bcur, i, g, acc);
+    if (more) lora_store_a<NQ>(bnext, t, lw);
+    __syncthreads();
+}
+
+template <int H, int NQ>
 __global__ __launch_bounds__(kThreads) void k_amax_lora(QArgs a) {
     constexpr bool RHT_ROW = H & 1, RHT_COL = (H >> 1) & 1;
-    __shared__ uint4 bl[kLoraMaxRank * (kLoraStep / 8)];   // [rank][16 chunks], chunk ^ (row & 15)
+    // [2 buffers][NQ*16 rows][16 chunks], chunk ^ (row & 15): the next step's slice is
+    // written into one buffer while the MFMAs read the other
+    __shared__ uint4 bl[2][NQ * 16 * (kLoraStep / 8)];
     __shared__ float red[8];
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     const int i = lane & 15, g = lane >> 4;
@@ -605,7 +716,6 @@ __global__ __launch_bounds__(kThreads) void k_amax_lora(QArgs a) {
     const bool rvalid = row < a.rows;
     const int64_t kb = (int64_t)part * a.lora_kp;
     const int64_t ke = kb + a.lora_kp < a.cols ? kb + a.lora_kp : a.cols;
-    const int nq = a.lora_r / 16;
     const uint32_t signs =
         (RHT_ROW || RHT_COL) ? __builtin_amdgcn_readfirstlane(rht_sign_bits(a.k0, a.k1)) : 0u;
     const uint32_t cmask = RHT_COL ? col_sign_mask(signs, i) : 0u;
@@ -614,83 +724,25 @@ __global__ __launch_bounds__(kThreads) void k_amax_lora(QArgs a) {
     for (int s = 0; s < 4; ++s) sgn[s] = (i >> s) & 1 ? -1.0f : 1.0f;
     const uint16_t* xrow = (const uint16_t*)a.x + row * a.ld;
 
-    f32x4t acc[kLoraMaxRank / 16];
+    f32x4t acc[NQ];
 #pragma unroll
-    for (int q = 0; q < kLoraMaxRank / 16; ++q) acc[q] = f32x4t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int q = 0; q < NQ; ++q) acc[q] = f32x4t{0.0f, 0.0f, 0.0f, 0.0f};
     float mr = 0.0f, mc = 0.0f;
 
-    for (int64_t c = kb; c < ke; c += kLoraStep) {
-        __syncthreads();   // the previous step's slice of a has been read
-        for (int q = t; q < a.lora_r * 16; q += kThreads) {
-            const int rr = q >> 4, ch = q & 15;
-            bl[rr * 16 + (ch ^ (rr & 15))] = *(const uint4*)(a.lora_a + (int64_t)rr * a.cols + c + ch * 8);
-        }
-        uint32_t xw[16];
-        if (rvalid) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint4 u = *(const uint4*)(xrow + c + 32 * g + 8 * q);
-                xw[4 * q] = u.x; xw[4 * q + 1] = u.y; xw[4 * q + 2] = u.z; xw[4 * q + 3] = u.w;
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 16; ++q) xw[q] = 0u;
-        }
-
-        // partial maxima
-        if ((a.rowwise && !RHT_ROW) || (a.colwise && !RHT_COL)) {
-            typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-            u16x2 m = {0, 0};
-#pragma unroll
-            for (int q = 0; q < 16; ++q)
-                m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, xw[q] & 0x7FFF7FFFu));
-            const float pm = fmaxf(__uint_as_float((uint32_t)m.x << 16), __uint_as_float((uint32_t)m.y << 16));
-            if (!RHT_ROW) mr = fmaxf(mr, pm);
-            if (!RHT_COL) mc = fmaxf(mc, pm);
-        }
-        if (RHT_ROW) {
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                float w[16];
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const uint32_t d = xw[8 * hf + e / 2];
-                    w[e] = apply_sign(__uint_as_float((e & 1) ? (d & 0xFFFF0000u) : (d << 16)), signs, e);
-                }
-                wht16(w);
-                mr = fmaxf(mr, fmaxf(amax8(&w[0]), amax8(&w[8])));
-            }
-        }
-        if (RHT_COL) {
-            float am = 0.0f;
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const uint32_t d = xw[q] ^ cmask;
-                float w0 = __uint_as_float(d << 16), w1 = __uint_as_float(d & 0xFFFF0000u);
-                w0 = col_stage<1>(w0, sgn[0]); w1 = col_stage<1>(w1, sgn[0]);
-                w0 = col_stage<2>(w0, sgn[1]); w1 = col_stage<2>(w1, sgn[1]);
-                w0 = col_stage<4>(w0, sgn[2]); w1 = col_stage<4>(w1, sgn[2]);
-                w0 = col_stage<8>(w0, sgn[3]); w1 = col_stage<8>(w1, sgn[3]);
-                am = fmaxf(am, fmaxf(fabsf(w0), fabsf(w1)));
-                if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-            }
-            mc = fmaxf(mc, am);
-        }
-
-        __syncthreads();   // the slice of a is in LDS
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bf16x8t av = __builtin_bit_cast(bf16x8t, make_uint4(xw[4 * j], xw[4 * j + 1], xw[4 * j + 2], xw[4 * j + 3]));
-#pragma unroll
-            for (int q = 0; q < kLoraMaxRank / 16; ++q) {
-                if (q < nq) {
-                    const int rr = 16 * q + i;
-                    const bf16x8t bv = __builtin_bit_cast(bf16x8t, bl[rr * 16 + ((4 * g + j) ^ (rr & 15))]);
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[q], 0, 0, 0);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    uint4 x0[4], x1[4], lw[NQ];
+    lora_load_x(xrow, rvalid, kb, g, x0);
+    lora_load_a<NQ>(a, kb, t, lw);
+    lora_store_a<NQ>(bl[0], t, lw);
+    __syncthreads();
+    // two steps per trip with ping-pong buffers, so nothing is copied
+    for (int64_t c = kb; c < ke; c += 2 * kLoraStep) {
+        const bool more0 = c + kLoraStep < ke;
+        lora_step<H, NQ>(a, x0, x1, lw, bl[0], bl[1], more0, c + kLoraStep, xrow, rvalid, t, i, g,
+                         signs, cmask, sgn, mr, mc, acc);
+        if (!more0) break;
+        const bool more1 = c + 2 * kLoraStep < ke;
+        lora_step<H, NQ>(a, x1, x0, lw, bl[1], bl[0], more1, c + 2 * kLoraStep, xrow, rvalid, t, i,
+                         g, signs, cmask, sgn, mr, mc, acc);
     }
     if (RHT_ROW) mr = mr * 0.25f;
     if (RHT_COL) mc = mc * 0.25f;
@@ -698,13 +750,11 @@ __global__ __launch_bounds__(kThreads) void k_amax_lora(QArgs a) {
     // the K-part's partial of T: lane holds rows 4g .. 4g + 3 of column 16q + i of block q
     const int64_t total = a.rows * a.lora_r;
 #pragma unroll
-    for (int q = 0; q < kLoraMaxRank / 16; ++q) {
-        if (q < nq) {
+    for (int q = 0; q < NQ; ++q) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t r = (int64_t)rblk * kLoraRowsWG + wid * 16 + 4 * g + v;
-                if (r < a.rows) a.lora_part[part * total + r * a.lora_r + 16 * q + i] = acc[q][v];
-            }
+        for (int v = 0; v < 4; ++v) {
+            const int64_t r = (int64_t)rblk * kLoraRowsWG + wid * 16 + 4 * g + v;
+            if (r < a.rows) a.lora_part[part * total + r * a.lora_r + 16 * q + i] = acc[q][v];
         }
     }
     block_max2(mr, mc, red);
@@ -714,10 +764,20 @@ __global__ __launch_bounds__(kThreads) void k_amax_lora(QArgs a) {
     }
 }
 
+template <int H>
+void launch_amax_lora(const QArgs& a, hipStream_t st) {
+    switch (a.lora_r / 16) {
+    case 1: k_amax_lora<H, 1><<<a.npart, kThreads, 0, st>>>(a); break;
+    case 2: k_amax_lora<H, 2><<<a.npart, kThreads, 0, st>>>(a); break;
+    case 3: k_amax_lora<H, 3><<<a.npart, kThreads, 0, st>>>(a); break;
+    default: k_amax_lora<H, 4><<<a.npart, kThreads, 0, st>>>(a); break;
+    }
+}
+
 template <bool BF16, int F>
 void launch_quant(const QArgs& a, hipStream_t st) {
     if constexpr (BF16) {
-        if (a.lora_t) k_amax_lora<(F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
+        if (a.lora_t) launch_amax_lora<(F >> 2)>(a, st);
         else k_amax<BF16, (F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
     } else {
         k_amax<BF16, (F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
