@@ -436,7 +436,8 @@ def main():
 
 def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream, iters=20):
     """Measurements outside the step, same method (HIP events on the launch stream):
-    the X and dY quantizes with 4/6 adaptive block scaling; the LoRA-SVD branch at rank 64
+    the X and dY quantizes with 4/6 adaptive block scaling; eq. (2)'s Wgrad operand of X
+    requantized from the rowwise copy; the LoRA-SVD branch at rank 64
     (X quantize with the L1 down-projection fused, FFN-up GEMM with the L2 up-projection
     fused, and for dX the dY quantize with L2^T and the dgrad GEMM with L1^T); the
     QKV-projection GEMM of the 3B model; a plain device copy for the box's achievable HBM
@@ -468,6 +469,11 @@ def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream, ite
                        dtype=torch.uint8, device=dev)
     nv.nvfp4_quantize_lora(X, p_x, L1, lo["beta"], qx[0], qx[1], tx, wsx)
     nv.nvfp4_quantize_lora(dY, p_dy, L2T, lo["beta"], qdy[0], qdy[1], tdy, wsdy)
+    p_req = nv.quant_params(rowwise=False, colwise=True, rht_col=True, round_col=nv.NVFP4_SR,
+                            seed=SEED_WGRAD)
+    qreq = nv.QTensor.empty(HIDDEN, TOKENS, dev)
+    wsreq = torch.empty(max(nv.load_library().nvfp4_requantize_cols_workspace_bytes(TOKENS, HIDDEN), 16),
+                        dtype=torch.uint8, device=dev)
     Yl = torch.empty((TOKENS, FFN), dtype=torch.float32, device=dev)
     dXl = torch.empty((TOKENS, HIDDEN), dtype=torch.float32, device=dev)
     cases = {
@@ -491,6 +497,10 @@ def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream, ite
                                 qbytes(TOKENS, FFN) + qbytes(HIDDEN, FFN) + 4 * TOKENS * HIDDEN
                                 + 2 * TOKENS * R + 2 * HIDDEN * R,
                                 2 * TOKENS * HIDDEN * FFN + 2 * TOKENS * HIDDEN * R),
+        # eq. (2): the Wgrad operand of X from its rowwise copy (column RHT, SR)
+        "requant_X_cols_from_rowcopy": (
+            lambda: nv.nvfp4_requantize_cols(qx[0], p_req, qreq, wsreq),
+            2 * qbytes(TOKENS, HIDDEN), 0),
         "gemm_qkv_8192x6144x3072": (lambda: nv.nvfp4_gemm(qa, qb, out=C),
                                     qbytes(M, K) + qbytes(N, K) + 4 * M * N, 2 * M * N * K),
         "hbm_copy_256MiB": (lambda: dst.copy_(src), 2 * (256 << 20), 0),

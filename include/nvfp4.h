@@ -150,6 +150,20 @@ int nvfp4_quantize_lora(const void* x, int dtype, int64_t rows, int64_t cols, in
                         const nvfp4_qtensor* col_out, const uint16_t* lora_a, int64_t rank,
                         float beta, uint16_t* lora_t, void* ws, size_t ws_bytes, void* stream);
 
+/* The columnwise copy of a rowwise copy's decoded values: Full-Stack FP4 eq. (2) takes the
+ * Wgrad operand Q_16x1(H^T Q_1x16(X)), the columnwise (16x1, optionally rotated)
+ * quantization of the already quantized activation.  row_in is a rowwise copy of a
+ * rows x cols tensor (as nvfp4_quantize writes it); its values fl(fl(v s) s_g) are
+ * quantized as nvfp4_quantize would quantize them with p, into col_out [cols][rows/2],
+ * [cols][rows/16].  p must ask for the columnwise copy only (rowwise 0, colwise 1, 1x16
+ * blocks, no row Hadamard; round_col, rht_col, seed, scale46 as in nvfp4_quantize), else
+ * NVFP4_ERR_MODE.  Reads 0.5625 bytes per element instead of the input's 2 or 4.
+ * ws of nvfp4_requantize_cols_workspace_bytes; rows, cols multiples of 16. */
+size_t nvfp4_requantize_cols_workspace_bytes(int64_t rows, int64_t cols);
+int nvfp4_requantize_cols(const nvfp4_qtensor* row_in, int64_t rows, int64_t cols,
+                          const nvfp4_quant_params* p, const nvfp4_qtensor* col_out, void* ws,
+                          size_t ws_bytes, void* stream);
+
 /* Decode one copy: out[n][k] = (value(code) * s) * s_g, rounded once to binary32
  * (Full-Stack FP4 sec. 2), then to bfloat16 nearest-even if out_dtype is NVFP4_BF16.
  * Rotated copies decode to the rotated values.  out has row pitch ld_out elements

@@ -31,7 +31,8 @@ EXPORTED = ["nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantiz
             "nvfp4_gemm", "qadamw_v_workspace_bytes", "qadamw_v_encode", "qadamw_v_decode",
             "nvfp4_status_string", "nvfp4_abi_version", "qadamw_step_workspace_bytes",
             "qadamw_step", "nvfp4_gemm_lora", "nvfp4_quantize_lora_workspace_bytes",
-            "nvfp4_quantize_lora"]
+            "nvfp4_quantize_lora", "nvfp4_requantize_cols_workspace_bytes",
+            "nvfp4_requantize_cols"]
 
 
 class Nvfp4Error(RuntimeError):
@@ -89,6 +90,11 @@ def load_library(path: Optional[str] = None):
     lib.nvfp4_quantize_lora.restype = ctypes.c_int
     lib.nvfp4_quantize_lora.argtypes = [vp, ctypes.c_int, i64, i64, i64, P(QuantParams), P(QTensorC),
                                         P(QTensorC), vp, i64, ctypes.c_float, vp, vp, sz, vp]
+    lib.nvfp4_requantize_cols_workspace_bytes.restype = sz
+    lib.nvfp4_requantize_cols_workspace_bytes.argtypes = [i64, i64]
+    lib.nvfp4_requantize_cols.restype = ctypes.c_int
+    lib.nvfp4_requantize_cols.argtypes = [P(QTensorC), i64, i64, P(QuantParams), P(QTensorC), vp,
+                                          sz, vp]
     lib.nvfp4_gemm_lora.restype = ctypes.c_int
     lib.nvfp4_gemm_lora.argtypes = [P(QTensorC), P(QTensorC), i64, i64, i64, vp, i64, vp, vp, i64,
                                     vp]
@@ -262,6 +268,24 @@ def nvfp4_quantize_lora(x, params, lora_a, beta, row_out=None, col_out=None, lor
                                    _ptr(lora_a), rank, float(beta), _ptr(lora_t), _ptr(workspace),
                                    workspace.numel(), _stream(dev)))
     return (row_out if params.rowwise else None), (col_out if params.colwise else None), lora_t
+
+
+def nvfp4_requantize_cols(row_q, params, col_out=None, workspace=None):
+    """The columnwise copy of a rowwise copy's decoded values (Full-Stack FP4 eq. (2)'s
+    Q_16x1(H^T Q_1x16(X))); params ask for the columnwise copy only."""
+    lib = load_library()
+    _require_cuda(row_q.codes)
+    R, C = row_q.shape
+    dev = row_q.codes.device
+    if col_out is None:
+        col_out = QTensor.empty(C, R, dev)
+    need = int(lib.nvfp4_requantize_cols_workspace_bytes(R, C))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    rq, cq = row_q.c(), col_out.c()
+    _check(lib.nvfp4_requantize_cols(ctypes.byref(rq), R, C, ctypes.byref(params), ctypes.byref(cq),
+                                     _ptr(workspace), workspace.numel(), _stream(dev)))
+    return col_out
 
 
 def nvfp4_gemm_lora(a, b, t, lb, out=None):

@@ -141,6 +141,9 @@ static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, i
     if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
 
     QArgs a;
+    a.in_codes = nullptr;
+    a.in_scales = nullptr;
+    a.in_sg = nullptr;
     a.x = x;
     a.rows = rows;
     a.cols = cols;
@@ -231,6 +234,88 @@ extern "C" int nvfp4_quantize_lora(const void* x, int dtype, int64_t rows, int64
     }
     return quantize_impl(x, dtype, rows, cols, ld_x, p, row_out, col_out, lora_a, rank, beta,
                          rows > 0 ? lora_t : nullptr, ws, ws_bytes, stream);
+}
+
+namespace nvfp4 {
+void launch_requant_cols(int f, const QArgs& a, hipStream_t st) {
+    switch (f) {
+    case 0: launch_quant<2, 0>(a, st); break;
+    case 2: launch_quant<2, 2>(a, st); break;
+    case 8: launch_quant<2, 8>(a, st); break;
+    default: launch_quant<2, 10>(a, st); break;
+    }
+}
+}  // namespace nvfp4
+
+extern "C" size_t nvfp4_requantize_cols_workspace_bytes(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return (size_t)quant_tiles(rows, cols, nullptr) * 2 * sizeof(float);
+}
+
+extern "C" int nvfp4_requantize_cols(const nvfp4_qtensor* row_in, int64_t rows, int64_t cols,
+                                     const nvfp4_quant_params* p, const nvfp4_qtensor* col_out,
+                                     void* ws, size_t ws_bytes, void* stream) {
+    if (!p || !row_in || !col_out) return NVFP4_ERR_NULL;
+    if (rows < 0 || cols < 0 || rows % 16 || cols % 16) return NVFP4_ERR_SHAPE;
+    if (p->rowwise || !p->colwise || p->block != NVFP4_BLOCK_1D || p->rht_row ||
+        (p->round_col != NVFP4_RNE && p->round_col != NVFP4_SR) ||
+        (p->scale46 != 0 && p->scale46 != 1))
+        return NVFP4_ERR_MODE;
+    hipStream_t st = (hipStream_t)stream;
+    if (rows == 0 || cols == 0) {
+        if (!col_out->gscale) return NVFP4_ERR_NULL;
+        k_fill_scale_one<<<1, 64, 0, st>>>(nullptr, col_out->gscale);
+        return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+    }
+    int rc;
+    if ((rc = check_qtensor(row_in)) != NVFP4_OK) return rc;
+    if ((rc = check_qtensor(col_out)) != NVFP4_OK) return rc;
+    const size_t need = nvfp4_requantize_cols_workspace_bytes(rows, cols);
+    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
+    QArgs a;
+    a.in_codes = row_in->codes;
+    a.in_scales = row_in->scales;
+    a.in_sg = row_in->gscale;
+    a.x = nullptr;
+    a.rows = rows;
+    a.cols = cols;
+    a.ld = cols;
+    a.is_bf16 = 0;
+    a.rowwise = 0;
+    a.colwise = 1;
+    a.block2d = 0;
+    a.sr_row = 0;
+    a.sr_col = p->round_col == NVFP4_SR;
+    a.rht_row = 0;
+    a.rht_col = p->rht_col != 0;
+    a.scale46 = p->scale46 != 0;
+    a.k0 = (uint32_t)p->seed;
+    a.k1 = (uint32_t)(p->seed >> 32);
+    a.rcodes = nullptr;
+    a.rscales = nullptr;
+    a.rsg = nullptr;
+    a.ccodes = col_out->codes;
+    a.cscales = col_out->scales;
+    a.csg = col_out->gscale;
+    a.partial = (float*)ws;
+    a.ntiles = (int)quant_tiles(rows, cols, &a.tiles_c);
+    a.lora_a = nullptr;
+    a.lora_t = nullptr;
+    a.lora_part = nullptr;
+    a.lora_r = 0;
+    a.lora_parts = 0;
+    a.lora_kp = 0;
+    a.lora_beta = 0.0f;
+    {
+        const int64_t wtiles = (rows / 16) * ((cols + kAmaxWaveCols - 1) / kAmaxWaveCols);
+        int64_t np = (wtiles + 3) / 4;
+        if (np > 768) np = 768;
+        if (np > a.ntiles) np = a.ntiles;
+        a.npart = (int)(np > 0 ? np : 1);
+    }
+    launch_requant_cols((a.sr_col << 1) | (a.rht_col << 3), a, st);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
 extern "C" int nvfp4_dequantize(const nvfp4_qtensor* q, int64_t n, int64_t k, int out_dtype,

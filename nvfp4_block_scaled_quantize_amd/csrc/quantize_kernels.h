@@ -43,6 +43,10 @@ struct QArgs {
     uint8_t* ccodes;
     uint8_t* cscales;
     float* csg;
+    // input kind 2 (eq. (2)'s double quantization): the rowwise NVFP4 copy x is decoded from
+    const uint8_t* in_codes;
+    const uint8_t* in_scales;
+    const float* in_sg;
     float* partial;  // [2][npart]: rowwise-copy and columnwise-copy amax per k_amax workgroup
     int tiles_c;
     int ntiles;
@@ -61,9 +65,9 @@ struct QArgs {
 // One thread's 16-row x 8-column input patch.  bfloat16 stays packed two to a register
 // (64 VGPRs rather than 128) and is widened where it is used: a bfloat16 is the upper
 // half of the binary32 with the same value.
-template <bool BF16> struct Patch;
+template <int IN> struct Patch;   // IN: 0 binary32, 1 bfloat16, 2 a rowwise NVFP4 copy
 
-template <> struct Patch<true> {
+template <> struct Patch<1> {
     uint32_t p[16][4];
     __device__ __forceinline__ void load(const void* x, int64_t ld, int64_t r0, int64_t c0, bool valid) {
         if (!valid) {
@@ -102,7 +106,7 @@ template <> struct Patch<true> {
     }
 };
 
-template <> struct Patch<false> {
+template <> struct Patch<0> {
     float p[16][8];
     __device__ __forceinline__ void load(const void* x, int64_t ld, int64_t r0, int64_t c0, bool valid) {
         if (!valid) {
@@ -139,6 +143,40 @@ template <> struct Patch<false> {
     }
 };
 
+// A rowwise NVFP4 copy decoded to binary32, fl(fl(v s) s_g) (v s is exact): the input of
+// the columnwise copy in Full-Stack FP4 eq. (2), Q_16x1(H^T Q_1x16(X)).  A patch row's 8
+// columns are one 4-byte group of codes inside one 16-element block.
+template <> struct Patch<2> : Patch<0> {
+    __device__ __forceinline__ void load_q(const QArgs& a, int64_t r0, int64_t c0, bool valid) {
+        if (!valid) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) p[i][e] = 0.0f;
+            return;
+        }
+        const float sg = *a.in_sg;
+        const int64_t cp = a.cols / 2, sp = a.cols / 16;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t w = *(const uint32_t*)(a.in_codes + (r0 + i) * cp + c0 / 2);
+            const float s = e4m3_value(a.in_scales[(r0 + i) * sp + c0 / 16]);
+            const float2v q0 = fp4x2_to_f32<0>(w), q1 = fp4x2_to_f32<1>(w);
+            const float2v q2 = fp4x2_to_f32<2>(w), q3 = fp4x2_to_f32<3>(w);
+            const float v[8] = {q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[i][e] = (v[e] * s) * sg;
+        }
+    }
+};
+
+template <int IN>
+__device__ __forceinline__ void load_patch(Patch<IN>& P, const QArgs& a, int64_t r0, int64_t c0,
+                                           bool valid) {
+    if constexpr (IN == 2) P.load_q(a, r0, c0, valid);
+    else P.load(a.x, a.ld, r0, c0, valid);
+}
+
 // The random Hadamard transform of a 16-chunk is (1/4) H16 (D v): the sign flips D are
 // applied to the packed patch beforehand (flip_row_signs / flip_col_signs: one XOR per
 // packed pair), the butterflies here, and the factor 1/4 by the caller (an exact scaling,
@@ -165,22 +203,22 @@ __device__ __forceinline__ void wht_pair8(float w[8], float sgn) {
 
 // Row signs: element (i, e) of the lane's 8 columns sits at position half * 8 + e of its
 // 16-chunk.  Column signs: the patch's 16 rows are one 16-chunk of every column.
-template <bool BF16>
+template <int IN>
 __device__ __forceinline__ uint32_t row_sign_mask(uint32_t signs, int half, int h) {
     const uint32_t s = signs >> (half * 8 + 2 * h);
-    return Patch<BF16>::pair_mask(s & 1u, (s >> 1) & 1u);
+    return Patch<IN>::pair_mask(s & 1u, (s >> 1) & 1u);
 }
 __device__ __forceinline__ uint32_t col_sign_mask(uint32_t signs, int i) {
     const uint32_t b = (signs >> i) & 1u;
     return (b << 15) | (b << 31);
 }
 
-template <bool BF16>
-__device__ __forceinline__ void flip_signs(Patch<BF16>& P, uint32_t signs, int half, bool rows,
+template <int IN>
+__device__ __forceinline__ void flip_signs(Patch<IN>& P, uint32_t signs, int half, bool rows,
                                            bool cols) {
     uint32_t rm[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) rm[h] = rows ? row_sign_mask<BF16>(signs, half, h) : 0u;
+    for (int h = 0; h < 4; ++h) rm[h] = rows ? row_sign_mask<IN>(signs, half, h) : 0u;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const uint32_t cm = cols ? col_sign_mask(signs, i) : 0u;
@@ -219,13 +257,13 @@ __device__ __forceinline__ void block_max2(float& a, float& b, float* red) {
 // Hadamard transform).  The rowwise transform pairs this lane with lane ^ 1 (positions 8..15
 // of the 16-chunk when this lane's column is a multiple of 16).  The factor 1/4 is applied
 // to the maxima: x -> fl(x / 4) is monotone, so max fl(|w| / 4) = fl(max |w| / 4).
-template <bool BF16, bool RHT_ROW, bool RHT_COL>
-__device__ __forceinline__ void patch_amax(const QArgs& a, Patch<BF16>& P, uint32_t signs,
+template <int IN, bool RHT_ROW, bool RHT_COL>
+__device__ __forceinline__ void patch_amax(const QArgs& a, Patch<IN>& P, uint32_t signs,
                                            int half, float& mr, float& mc) {
     float plain = 0.0f, arow = 0.0f, acol = 0.0f;
     if ((a.rowwise && !RHT_ROW) || (a.colwise && !RHT_COL)) plain = P.amax();
     if (RHT_ROW) {
-        flip_signs<BF16>(P, signs, half, true, false);
+        flip_signs<IN>(P, signs, half, true, false);
         const float sgn = half ? -1.0f : 1.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -238,7 +276,7 @@ __device__ __forceinline__ void patch_amax(const QArgs& a, Patch<BF16>& P, uint3
         arow = arow * 0.25f;
     }
     if (RHT_COL) {
-        flip_signs<BF16>(P, signs, half, RHT_ROW, true);   // undo the row signs, apply the column signs
+        flip_signs<IN>(P, signs, half, RHT_ROW, true);   // undo the row signs, apply the column signs
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             float w[16];
@@ -257,7 +295,7 @@ constexpr int kAmaxWaveCols = 512;   // columns of a k_amax wave tile (64 lanes 
 
 // Specialised on the input dtype and the Hadamard flags (bit 0: rowwise copy, bit 1:
 // columnwise copy) so that each variant keeps its 16x8 patch in registers.
-template <bool BF16, int H>
+template <int IN, int H>
 __global__ __launch_bounds__(kThreads) void k_amax(QArgs a) {
     constexpr bool RHT_ROW = H & 1, RHT_COL = (H >> 1) & 1;
     __shared__ float red[8];
@@ -270,9 +308,9 @@ __global__ __launch_bounds__(kThreads) void k_amax(QArgs a) {
     for (int64_t w = (int64_t)blockIdx.x * 4 + wid; w < nwt; w += (int64_t)gridDim.x * 4) {
         const int64_t r0 = (w / wcols) * 16;
         const int64_t c0 = (w % wcols) * kAmaxWaveCols + lane * 8;
-        Patch<BF16> P;
-        P.load(a.x, a.ld, r0, c0, c0 < a.cols);
-        patch_amax<BF16, RHT_ROW, RHT_COL>(a, P, signs, lane & 1, mr, mc);
+        Patch<IN> P;
+        load_patch(P, a, r0, c0, c0 < a.cols);
+        patch_amax<IN, RHT_ROW, RHT_COL>(a, P, signs, lane & 1, mr, mc);
     }
     block_max2(mr, mc, red);
     if (t == 0) {
@@ -372,7 +410,7 @@ __device__ __forceinline__ float uniform_f(float v) {
 // exact for every block whose codes can differ: no 4/6 scaling (its squared errors use the
 // rotated values themselves) and 2^-92 <= s_g <= 2^110 (no reciprocal is then subnormal,
 // and elements small enough to be rounded by the 1/4 quantize to 0 either way).
-template <bool BF16, int F>
+template <int IN, int F>
 __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
     constexpr bool SR_ROW = F & 1, SR_COL = (F >> 1) & 1;
     constexpr bool RHT_ROW = (F >> 2) & 1, RHT_COL = (F >> 3) & 1;
@@ -388,8 +426,8 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
     const int half = pc & 1;
 
     // the patch loads go out first and land while the tensor scales are formed
-    Patch<BF16> P;
-    P.load(a.x, a.ld, r0, c0, valid);
+    Patch<IN> P;
+    load_patch(P, a, r0, c0, valid);
 
     // LoRA-SVD down-projection: T = BF16(beta * sum of the K-part partials, in part order)
     if (a.lora_t) {
@@ -433,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
     }
 
     if (a.rowwise) {
-        if (RHT_ROW) flip_signs<BF16>(P, signs, half, true, false);
+        if (RHT_ROW) flip_signs<IN>(P, signs, half, true, false);
         const float sgn = half ? -1.0f : 1.0f;
         const int64_t rpitch = a.cols / 2, spitch = a.cols / 16;
         uint8_t* const cbase = a.rcodes + r0 * rpitch + c0 / 2;
@@ -491,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
 
     if (a.colwise) {
         // from the loaded (or row-flipped) signs to the column signs
-        if (RHT_COL || RHT_ROW) flip_signs<BF16>(P, signs, half, RHT_ROW, RHT_COL);
+        if (RHT_COL || RHT_ROW) flip_signs<IN>(P, signs, half, RHT_ROW, RHT_COL);
         static_for<0, 8>([&](auto J) {
             constexpr int j = decltype(J)::value;
             float w[16];
@@ -774,15 +812,15 @@ void launch_amax_lora(const QArgs& a, hipStream_t st) {
     }
 }
 
-template <bool BF16, int F>
+template <int IN, int F>
 void launch_quant(const QArgs& a, hipStream_t st) {
-    if constexpr (BF16) {
+    if constexpr (IN == 1) {
         if (a.lora_t) launch_amax_lora<(F >> 2)>(a, st);
-        else k_amax<BF16, (F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
+        else k_amax<IN, (F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
     } else {
-        k_amax<BF16, (F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
+        k_amax<IN, (F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
     }
-    k_encode<BF16, F><<<a.ntiles, kThreads, 0, st>>>(a);
+    k_encode<IN, F><<<a.ntiles, kThreads, 0, st>>>(a);
 }
 
 // Each launch unit covers one dtype and half of the 16 option combinations.
@@ -790,5 +828,6 @@ void launch_quant_bf16_lo(int f, const QArgs& a, hipStream_t st);
 void launch_quant_bf16_hi(int f, const QArgs& a, hipStream_t st);
 void launch_quant_f32_lo(int f, const QArgs& a, hipStream_t st);
 void launch_quant_f32_hi(int f, const QArgs& a, hipStream_t st);
+void launch_requant_cols(int f, const QArgs& a, hipStream_t st);
 
 }  // namespace nvfp4

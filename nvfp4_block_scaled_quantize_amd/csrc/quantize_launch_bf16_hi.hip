@@ -7,7 +7,7 @@ namespace nvfp4 {
 
 void launch_quant_bf16_hi(int f, const QArgs& a, hipStream_t st) {
     switch (f) {
-#define NVFP4_CASE(F) case F: launch_quant<true, F>(a, st); break;
+#define NVFP4_CASE(F) case F: launch_quant<1, F>(a, st); break;
     NVFP4_CASE(8) NVFP4_CASE(9) NVFP4_CASE(10) NVFP4_CASE(11) NVFP4_CASE(12) NVFP4_CASE(13) NVFP4_CASE(14) NVFP4_CASE(15)
 #undef NVFP4_CASE
     }

@@ -7,7 +7,7 @@ namespace nvfp4 {
 
 void launch_quant_bf16_lo(int f, const QArgs& a, hipStream_t st) {
     switch (f) {
-#define NVFP4_CASE(F) case F: launch_quant<true, F>(a, st); break;
+#define NVFP4_CASE(F) case F: launch_quant<1, F>(a, st); break;
     NVFP4_CASE(0) NVFP4_CASE(1) NVFP4_CASE(2) NVFP4_CASE(3) NVFP4_CASE(4) NVFP4_CASE(5) NVFP4_CASE(6) NVFP4_CASE(7)
 #undef NVFP4_CASE
     }

@@ -258,6 +258,16 @@ def lora_down(x, a, beta):
     return t, t64, tabs
 
 
+def requantize_cols(q_row, round_col=RNE, rht_col=False, seed=0, scale46=False):
+    """Full-Stack FP4 eq. (2): the Wgrad operand Q_16x1(H^T Q_1x16(X)) is the columnwise
+    quantization of the dequantized rowwise copy Q_1x16(X) (reading: the decoded values
+    fl(fl(v s) s_g) are quantized exactly as an input tensor would be)."""
+    xh = dequantize(q_row)
+    _, col = quantize(xh, rowwise=False, colwise=True, round_col=round_col, rht_col=rht_col,
+                      seed=seed, scale46=scale46)
+    return col
+
+
 def gemm_lora_f64(qa, qb, t, b):
     """A B^T over the dequantized operands plus t b^T (t [M][r], b [N][r] BF16 bits),
     binary64; returns (C, sum of |terms|)."""

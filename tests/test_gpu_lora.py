@@ -180,3 +180,53 @@ def test_quantize_lora_limits(nv):
     row, _, t = nv.nvfp4_quantize_lora(x, p, torch.ones((16, 128), dtype=torch.bfloat16, device=dev()), 1.0)
     torch.cuda.synchronize()
     assert torch.all(t == 0) and row.gscale.item() == 1.0
+
+
+# ---------------------------------------------------------------- eq. (2) double quantization
+# nvfp4_requantize_cols gets the oracle's rowwise copy and must reproduce the oracle's
+# columnwise quantization of its decoded values bit for bit.
+REQ_MODES = {
+    "rne": dict(),
+    "rht": dict(rht_col=True, seed=0x5EED4),
+    "sr": dict(round_col=1, seed=21),
+    "rht+sr": dict(rht_col=True, round_col=1, seed=0x5EED4),
+    "rht+sr 4/6": dict(rht_col=True, round_col=1, seed=0x5EED4, scale46=True),
+}
+
+
+@pytest.mark.parametrize("mode", list(REQ_MODES))
+@pytest.mark.parametrize("R,C", [(16, 16), (48, 80), (272, 400), (528, 160)])
+def test_requantize_cols_small(nv, oracle, mode, R, C):
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    from gpu_util import assert_copy_equal
+    print(f"requantize_cols {mode} {R}x{C}", flush=True)
+    x = synthetic.outlier_channels((R, C), 31 + R + C).to(torch.bfloat16).float().numpy()
+    orow, _ = oracle.quantize(x)
+    kw = REQ_MODES[mode]
+    p = nv.quant_params(rowwise=False, colwise=True, **kw)
+    col = nv.nvfp4_requantize_cols(to_gpu_qtensor(nv, orow), p)
+    torch.cuda.synchronize()
+    want = oracle.requantize_cols(orow, round_col=kw.get("round_col", 0),
+                                  rht_col=kw.get("rht_col", False), seed=kw.get("seed", 0),
+                                  scale46=kw.get("scale46", False))
+    assert_copy_equal(col, want, "requantized columnwise")
+
+
+def test_requantize_cols_full_size(nv, oracle):
+    """X 8192x3072: the Wgrad operand of eq. (2) (column RHT, SR) from the rowwise copy."""
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    from gpu_util import assert_copy_equal
+    print("requantize_cols full-size X 8192x3072", flush=True)
+    x = synthetic.ffn()["X"].float().numpy()
+    orow, _ = oracle.quantize(x)
+    p = nv.quant_params(rowwise=False, colwise=True, rht_col=True, round_col=1, seed=0x5EED4)
+    col = nv.nvfp4_requantize_cols(to_gpu_qtensor(nv, orow), p)
+    torch.cuda.synchronize()
+    want = oracle.requantize_cols(orow, round_col=1, rht_col=True, seed=0x5EED4)
+    assert_copy_equal(col, want, "requantized columnwise")
+
+
+def test_requantize_cols_refuses_rowwise(nv):
+    q = nv.QTensor.empty(32, 32, dev())
+    with pytest.raises(nv.Nvfp4Error):
+        nv.nvfp4_requantize_cols(q, nv.quant_params(rowwise=True, colwise=True))

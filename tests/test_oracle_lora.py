@@ -115,3 +115,31 @@ def test_gemm_lora_with_zero_operands_is_the_low_rank_product(oracle):
     C2, _ = oracle.gemm_lora_f64(qa2, qb2, t, b)
     C20, _ = oracle.gemm_f64(qa2, qb2)
     assert np.allclose(C2 - C20, ref, rtol=1e-12, atol=1e-12 * np.abs(C20).max())
+
+
+# ---------------------------------------------------------------- eq. (2) double quantization
+def test_requantize_cols_of_a_representable_tensor_is_single_quantization(oracle):
+    """When X already holds decoded NVFP4 values with one tensor scale, Q_1x16 returns the
+    same values, so Q_16x1(H^T Q_1x16(X)) must equal Q_16x1(H^T X)."""
+    rng = np.random.default_rng(12)
+    x0 = (rng.standard_normal((64, 96)) * np.exp(rng.standard_normal((64, 1)))).astype(np.float32)
+    q, _ = oracle.quantize(x0)
+    x = oracle.dequantize(q)                     # representable values
+    q2, _ = oracle.quantize(x)
+    assert np.array_equal(oracle.dequantize(q2), x)   # the rowwise copy reproduces them
+    for kw in (dict(), dict(rht_col=True, seed=5), dict(round_col=oracle.SR, seed=7),
+               dict(rht_col=True, round_col=oracle.SR, seed=9)):
+        got = oracle.requantize_cols(q2, **kw)
+        _, want = oracle.quantize(x, rowwise=False, colwise=True, **kw)
+        assert np.array_equal(got.codes, want.codes) and np.array_equal(got.scales, want.scales)
+        assert got.sg == want.sg
+
+
+def test_requantize_cols_differs_from_single_quantization(oracle):
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((64, 128)).astype(np.float32)
+    qr, _ = oracle.quantize(x)
+    got = oracle.requantize_cols(qr, rht_col=True, seed=3)
+    _, single = oracle.quantize(x, rowwise=False, colwise=True, rht_col=True, seed=3)
+    assert not np.array_equal(got.codes, single.codes)   # the row rounding shows through
+    assert got.codes.shape == single.codes.shape and got.scales.shape == single.scales.shape
