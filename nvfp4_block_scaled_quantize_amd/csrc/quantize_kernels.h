@@ -606,30 +606,14 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
 //    16 x 128 slice per MFMA column block, staged in LDS by the workgroup) follow the same
 //    correspondence, so every column is summed exactly once;
 //  * the input of the partial maxima of k_amax: plain and row-rotated in-register (the
-//    lane holds two whole 16-chunks of its row), column-rotated across the 16 lanes that
-//    hold one 16-row chunk (stages 1 and 2 by DPP quad permutations, 4 and 8 by swizzles).
+//    lane holds two whole 16-chunks of its row); for the column rotation the wave's step
+//    tile is transposed through LDS so that each lane holds 16 rows of two columns.
 // The low-rank partial of each K-part goes to lora_part; k_encode sums the parts in order.
 constexpr int kLoraStep = 128;
 constexpr int kLoraRowsWG = 64;
 constexpr int kLoraMaxRank = 64;
 typedef __bf16 bf16x8t __attribute__((ext_vector_type(8)));
 typedef float f32x4t __attribute__((ext_vector_type(4)));
-
-// The value of the lane whose index within the 16-lane row differs in bit H.
-template <int H>
-__device__ __forceinline__ float row_lane_xor(float v) {
-    const int b = __float_as_int(v);
-    if constexpr (H == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false));
-    else if constexpr (H == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false));
-    else return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x1F | (H << 10)));
-}
-
-// One butterfly stage of the column transform: lanes with bit H of their row index clear
-// take a + b, the others a - b (a the lower row's value, b the upper row's).
-template <int H>
-__device__ __forceinline__ float col_stage(float w, float sgn) {
-    return __builtin_fmaf(w, sgn, row_lane_xor<H>(w));
-}
 
 // Step loads: this lane's 32 values of its row, and its share of the step's slice of a
 // (NQ 16-row blocks x 128 columns: NQ 16-byte chunks per thread, chunk q = t + 256 k).
@@ -659,8 +643,7 @@ __device__ __forceinline__ void lora_store_a(uint4* bl, int t, const uint4 (&lw)
 // The partial maxima of one step's 32 values (see k_amax_lora).
 template <int H>
 __device__ __forceinline__ void lora_step_amax(const QArgs& a, const uint4 (&xv)[4], uint32_t signs,
-                                               uint32_t cmask, const float (&sgn)[4], float& mr,
-                                               float& mc) {
+                                               uint4* tw, int lane, float& mr, float& mc) {
     constexpr bool RHT_ROW = H & 1, RHT_COL = (H >> 1) & 1;
     uint32_t xw[16];
 #pragma unroll
@@ -691,18 +674,24 @@ __device__ __forceinline__ void lora_step_amax(const QArgs& a, const uint4 (&xv)
         }
     }
     if (RHT_COL) {
-        float am = 0.0f;
+        // the column rotation needs a row chunk's 16 values in one lane: the wave's 16 x 128
+        // step tile goes through its LDS area (16-byte chunk c of row r at c ^ r, conflict-free
+        // both ways) and comes back as rows 0..15 of columns 2 lane, 2 lane + 1
+        const int i = lane & 15, g = lane >> 4;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const uint32_t d = xw[q] ^ cmask;
-            float w0 = __uint_as_float(d << 16), w1 = __uint_as_float(d & 0xFFFF0000u);
-            w0 = col_stage<1>(w0, sgn[0]); w1 = col_stage<1>(w1, sgn[0]);
-            w0 = col_stage<2>(w0, sgn[1]); w1 = col_stage<2>(w1, sgn[1]);
-            w0 = col_stage<4>(w0, sgn[2]); w1 = col_stage<4>(w1, sgn[2]);
-            w0 = col_stage<8>(w0, sgn[3]); w1 = col_stage<8>(w1, sgn[3]);
-            am = fmaxf(am, fmaxf(fabsf(w0), fabsf(w1)));
+        for (int q = 0; q < 4; ++q) tw[i * 16 + ((4 * g + q) ^ i)] = xv[q];
+        const uint32_t* tw32 = (const uint32_t*)tw;
+        float w0[16], w1[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint32_t d = tw32[r * 64 + ((((lane >> 2) ^ r) & 15) << 2) + (lane & 3)] ^
+                               col_sign_mask(signs, r);
+            w0[r] = __uint_as_float(d << 16);
+            w1[r] = __uint_as_float(d & 0xFFFF0000u);
         }
-        mc = fmaxf(mc, am);
+        wht16(w0);
+        wht16(w1);
+        mc = fmaxf(mc, fmaxf(fmaxf(amax8(&w0[0]), amax8(&w0[8])), fmaxf(amax8(&w1[0]), amax8(&w1[8]))));
     }
 }
 
@@ -727,14 +716,13 @@ template <int H, int NQ>
 __device__ __forceinline__ void lora_step(const QArgs& a, const uint4 (&xv)[4], uint4 (&xn)[4],
                                           uint4 (&lw)[NQ], uint4* bcur, uint4* bnext, bool more,
                                           int64_t cnext, const uint16_t* xrow, bool rvalid, int t,
-                                          int i, int g, uint32_t signs, uint32_t cmask,
-                                          const float (&sgn)[4], float& mr, float& mc,
-                                          f32x4t (&acc)[NQ]) {
+                                          int i, int g, uint32_t signs, uint4* tw, int lane,
+                                          float& mr, float& mc, f32x4t (&acc)[NQ]) {
     if (more) {
         lora_load_x(xrow, rvalid, cnext, g, xn);
         lora_load_a<NQ>(a, cnext, t, lw);
     }
-    lora_step_amax<H>(a, xv, signs, cmask, sgn, mr, mc);
+    lora_step_amax<H>(a, xv, signs, tw, lane, mr, mc);
     lora_step_mma<NQ>(xv, bcur, i, g, acc);
     if (more) lora_store_a<NQ>(bnext, t, lw);
     __syncthreads();
@@ -746,6 +734,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_lora(QArgs a) {
     // [2 buffers][NQ*16 rows][16 chunks], chunk ^ (row & 15): the next step's slice is
     // written into one buffer while the MFMAs read the other
     __shared__ uint4 bl[2][NQ * 16 * (kLoraStep / 8)];
+    __shared__ uint4 tws[4][16 * 16];   // per wave: the step tile for the column rotation
     __shared__ float red[8];
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     const int i = lane & 15, g = lane >> 4;
@@ -756,10 +745,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_lora(QArgs a) {
     const int64_t ke = kb + a.lora_kp < a.cols ? kb + a.lora_kp : a.cols;
     const uint32_t signs =
         (RHT_ROW || RHT_COL) ? __builtin_amdgcn_readfirstlane(rht_sign_bits(a.k0, a.k1)) : 0u;
-    const uint32_t cmask = RHT_COL ? col_sign_mask(signs, i) : 0u;
-    float sgn[4];   // butterfly sign of this lane's row index at stages 1, 2, 4, 8
-#pragma unroll
-    for (int s = 0; s < 4; ++s) sgn[s] = (i >> s) & 1 ? -1.0f : 1.0f;
+    uint4* tw = tws[wid];
     const uint16_t* xrow = (const uint16_t*)a.x + row * a.ld;
 
     f32x4t acc[NQ];
@@ -776,11 +762,11 @@ __global__ __launch_bounds__(kThreads) void k_amax_lora(QArgs a) {
     for (int64_t c = kb; c < ke; c += 2 * kLoraStep) {
         const bool more0 = c + kLoraStep < ke;
         lora_step<H, NQ>(a, x0, x1, lw, bl[0], bl[1], more0, c + kLoraStep, xrow, rvalid, t, i, g,
-                         signs, cmask, sgn, mr, mc, acc);
+                         signs, tw, lane, mr, mc, acc);
         if (!more0) break;
         const bool more1 = c + 2 * kLoraStep < ke;
         lora_step<H, NQ>(a, x1, x0, lw, bl[1], bl[0], more1, c + 2 * kLoraStep, xrow, rvalid, t, i,
-                         g, signs, cmask, sgn, mr, mc, acc);
+                         g, signs, tw, lane, mr, mc, acc);
     }
     if (RHT_ROW) mr = mr * 0.25f;
     if (RHT_COL) mc = mc * 0.25f;
