@@ -437,7 +437,8 @@ def main():
 def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream, iters=20):
     """Measurements outside the step, same method (HIP events on the launch stream):
     the X and dY quantizes with 4/6 adaptive block scaling; eq. (2)'s Wgrad operand of X
-    requantized from the rowwise copy; the LoRA-SVD branch at rank 64
+    requantized from the rowwise copy; one NVFP4 Newton-Schulz iteration (3072 x 9216); the
+    LoRA-SVD branch at rank 64
     (X quantize with the L1 down-projection fused, FFN-up GEMM with the L2 up-projection
     fused, and for dX the dY quantize with L2^T and the dgrad GEMM with L1^T); the
     QKV-projection GEMM of the 3B model; a plain device copy for the box's achievable HBM
@@ -474,6 +475,9 @@ def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream, ite
     qreq = nv.QTensor.empty(HIDDEN, TOKENS, dev)
     wsreq = torch.empty(max(nv.load_library().nvfp4_requantize_cols_workspace_bytes(TOKENS, HIDDEN), 16),
                         dtype=torch.uint8, device=dev)
+    Xns = synthetic.normal((HIDDEN, FFN), SEED_QADAMW + 7, 1.0 / (HIDDEN ** 0.5 + FFN ** 0.5)).to(dev)
+    wsns = torch.empty(nv.load_library().nvfp4_ns_step_workspace_bytes(HIDDEN, FFN), dtype=torch.uint8,
+                       device=dev)
     Yl = torch.empty((TOKENS, FFN), dtype=torch.float32, device=dev)
     dXl = torch.empty((TOKENS, HIDDEN), dtype=torch.float32, device=dev)
     cases = {
@@ -501,6 +505,10 @@ def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream, ite
         "requant_X_cols_from_rowcopy": (
             lambda: nv.nvfp4_requantize_cols(qx[0], p_req, qreq, wsreq),
             2 * qbytes(TOKENS, HIDDEN), 0),
+        # NVFP4 Root: one quantized Newton-Schulz iteration on W_up's 3072 x 9216 orientation
+        # (three quantizes, A = qX qX^T, B = b A + c qA qA', X = a X + qB qX')
+        "ns_step_3072x9216": (lambda: nv.nvfp4_ns_step(Xns, 1.5, -0.5, 0.0, SEED_WGRAD, True, wsns),
+                              0, 2 * HIDDEN * HIDDEN * (2 * FFN + HIDDEN)),
         "gemm_qkv_8192x6144x3072": (lambda: nv.nvfp4_gemm(qa, qb, out=C),
                                     qbytes(M, K) + qbytes(N, K) + 4 * M * N, 2 * M * N * K),
         "hbm_copy_256MiB": (lambda: dst.copy_(src), 2 * (256 << 20), 0),

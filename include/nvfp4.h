@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 4
+#define NVFP4_ABI_VERSION 5
 
 enum nvfp4_status {
     NVFP4_OK = 0,
@@ -197,6 +197,32 @@ int nvfp4_gemm(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_
 int nvfp4_gemm_lora(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
                     int64_t K, float* c, int64_t ldc, const uint16_t* lora_t,
                     const uint16_t* lora_b, int64_t rank, void* stream);
+
+/* The W4A4 GEMM with a linear epilogue: C = alpha * (nvfp4_gemm's product) + beta * D,
+ * each element stored as fma(fl(alpha s_gA s_gB), acc, fl(beta d)).  D [M][N] FP32 with
+ * row pitch ldd >= N, 4-byte aligned; D may be C itself (same pitch): each element of D is
+ * read by the thread that writes the same element of C.  Passage: Full-Stack FP4 sec. 3.4
+ * (the quantized Newton-Schulz updates B = b A + c qA qA' and X = a X + qB qX').  Other
+ * arguments and errors as nvfp4_gemm; a null D gives NVFP4_ERR_NULL. */
+int nvfp4_gemm_axpby(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
+                     int64_t K, float alpha, const float* d, int64_t ldd, float beta, float* c,
+                     int64_t ldc, void* stream);
+
+/* One quantized Newton-Schulz iteration of NVFP4 Root (Full-Stack FP4 sec. 3.4; the
+ * iteration X = a X + b X (X^T X) + c X (X^T X)^2 of sec. 2 in the wide orientation):
+ *   qX = Q_1x16(X H), qX' = Q_16x1(H^T X), A = qX qX^T,
+ *   qA = Q_1x16(A H), qA' = Q_16x1(H^T A), B = b A + c qA qA',
+ *   qB = Q_1x16(B H), X <- a X + qB qX'.
+ * x [m][n] FP32 row-major, 16-byte aligned, updated in place.  Every quantization is
+ * nearest-even with 1x16 / 16x1 blocks, 4/6 scaling when scale46 = 1 (the pages'), and the
+ * random Hadamard of seed (one per iteration; use a fresh seed per iteration).  a, b, c:
+ * the caller's coefficients (the pages take shape-specialised ones from Root and print
+ * none).  A and B are FP32 m x m.  m and n must be multiples of 32 (else
+ * NVFP4_ERR_SHAPE); ws: nvfp4_ns_step_workspace_bytes(m, n) bytes, 256-byte aligned.
+ * The call enqueues six kernels' worth of work (three quantizes, three GEMMs). */
+size_t nvfp4_ns_step_workspace_bytes(int64_t m, int64_t n);
+int nvfp4_ns_step(float* x, int64_t m, int64_t n, float a, float b, float c, uint64_t seed,
+                  int32_t scale46, void* ws, size_t ws_bytes, void* stream);
 
 /* Device workspace (bytes) qadamw_v_encode needs. */
 size_t qadamw_v_workspace_bytes(int64_t rows, int64_t cols);

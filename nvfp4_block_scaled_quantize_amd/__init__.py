@@ -32,7 +32,8 @@ EXPORTED = ["nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantiz
             "nvfp4_status_string", "nvfp4_abi_version", "qadamw_step_workspace_bytes",
             "qadamw_step", "nvfp4_gemm_lora", "nvfp4_quantize_lora_workspace_bytes",
             "nvfp4_quantize_lora", "nvfp4_requantize_cols_workspace_bytes",
-            "nvfp4_requantize_cols"]
+            "nvfp4_requantize_cols", "nvfp4_gemm_axpby", "nvfp4_ns_step_workspace_bytes",
+            "nvfp4_ns_step"]
 
 
 class Nvfp4Error(RuntimeError):
@@ -61,7 +62,7 @@ class QTensorC(ctypes.Structure):
 
 
 _lib = None
-ABI_VERSION = 4   # NVFP4_ABI_VERSION of include/nvfp4.h this binding matches
+ABI_VERSION = 5   # NVFP4_ABI_VERSION of include/nvfp4.h this binding matches
 
 
 def load_library(path: Optional[str] = None):
@@ -95,6 +96,14 @@ def load_library(path: Optional[str] = None):
     lib.nvfp4_requantize_cols.restype = ctypes.c_int
     lib.nvfp4_requantize_cols.argtypes = [P(QTensorC), i64, i64, P(QuantParams), P(QTensorC), vp,
                                           sz, vp]
+    lib.nvfp4_gemm_axpby.restype = ctypes.c_int
+    lib.nvfp4_gemm_axpby.argtypes = [P(QTensorC), P(QTensorC), i64, i64, i64, ctypes.c_float, vp, i64,
+                                     ctypes.c_float, vp, i64, vp]
+    lib.nvfp4_ns_step_workspace_bytes.restype = sz
+    lib.nvfp4_ns_step_workspace_bytes.argtypes = [i64, i64]
+    lib.nvfp4_ns_step.restype = ctypes.c_int
+    lib.nvfp4_ns_step.argtypes = [vp, i64, i64, ctypes.c_float, ctypes.c_float, ctypes.c_float, u64,
+                                  i32, vp, sz, vp]
     lib.nvfp4_gemm_lora.restype = ctypes.c_int
     lib.nvfp4_gemm_lora.argtypes = [P(QTensorC), P(QTensorC), i64, i64, i64, vp, i64, vp, vp, i64,
                                     vp]
@@ -286,6 +295,40 @@ def nvfp4_requantize_cols(row_q, params, col_out=None, workspace=None):
     _check(lib.nvfp4_requantize_cols(ctypes.byref(rq), R, C, ctypes.byref(params), ctypes.byref(cq),
                                      _ptr(workspace), workspace.numel(), _stream(dev)))
     return col_out
+
+
+def nvfp4_gemm_axpby(a, b, alpha, d, beta, out=None):
+    """C = alpha * A B^T + beta * d (d float32 [M][N]; out may be d)."""
+    lib = load_library()
+    _require_cuda(a.codes, b.codes, d)
+    M, K = a.shape
+    N, K2 = b.shape
+    if K != K2:
+        raise Nvfp4Error(f"K mismatch {K} vs {K2}")
+    if d.dtype != torch.float32 or d.dim() != 2 or d.shape != (M, N) or d.stride(1) != 1:
+        raise Nvfp4Error("d must be a float32 [M][N] tensor with unit column stride")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.codes.device)
+    ac, bc = a.c(), b.c()
+    _check(lib.nvfp4_gemm_axpby(ctypes.byref(ac), ctypes.byref(bc), M, N, K, float(alpha), _ptr(d),
+                                d.stride(0), float(beta), _ptr(out), out.stride(0), _stream(out.device)))
+    return out
+
+
+def nvfp4_ns_step(x, a, b, c, seed, scale46=True, workspace=None):
+    """One quantized Newton-Schulz iteration on x (float32 [m][n], contiguous), in place."""
+    lib = load_library()
+    _require_cuda(x)
+    if x.dtype != torch.float32 or x.dim() != 2 or not x.is_contiguous():
+        raise Nvfp4Error("x must be a contiguous 2-D float32 tensor")
+    m, n = x.shape
+    if workspace is None:
+        workspace = torch.empty(max(int(lib.nvfp4_ns_step_workspace_bytes(m, n)), 256),
+                                dtype=torch.uint8, device=x.device)
+    _check(lib.nvfp4_ns_step(_ptr(x), m, n, float(a), float(b), float(c),
+                             int(seed) & 0xFFFFFFFFFFFFFFFF, int(scale46), _ptr(workspace),
+                             workspace.numel(), _stream(x.device)))
+    return x
 
 
 def nvfp4_gemm_lora(a, b, t, lb, out=None):

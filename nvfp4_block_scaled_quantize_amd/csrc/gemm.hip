@@ -69,7 +69,14 @@ struct GArgs {
     const uint16_t* lt;   // low-rank term: T [M][lr] and L [N][lr] (BF16), or null
     const uint16_t* lb;
     int64_t lr;
+    const float* d;       // C = alpha * product + beta * D (the EpiAxpby kernels)
+    int64_t ldd;
+    float alpha, beta;
 };
+
+// Epilogue variants: plain product; plus the LoRA-SVD low-rank term; alpha * product +
+// beta * D (the Newton-Schulz updates).
+enum { EpiPlain = 0, EpiLora = 1, EpiAxpby = 2 };
 
 // Packed tile layout: row r holds 64 bytes as four 16-byte chunks; chunk q sits at slot
 // q ^ (r/4 mod 4), which keeps both the staging stores (four lanes per row) and the
@@ -267,14 +274,40 @@ __device__ __forceinline__ void lora_epilogue(const GArgs& g, uint8_t* lds, floa
     }
 }
 
-// The epilogue, with the low-rank term as a compile-time switch so that the plain kernels
-// keep their register allocation.
-template <bool LORA>
+// alpha * product + beta * D, stored as fma(fl(alpha s_gA s_gB), acc, fl(beta d)).  Each
+// element of D is read by the lane that writes the same element of C, so D may be C.
+__device__ __forceinline__ void store_tile_axpby(const GArgs& g, const float16v (&acc)[4][4],
+                                                 int64_t m0, int64_t n0, int wm, int wn, int h,
+                                                 int li) {
+    const float as = (*g.asg * *g.bsg) * g.alpha;
+    const int64_t rbase = m0 + wm * 128 + 4 * h, cbase = n0 + wn * 128 + li;
+    const bool full = m0 + GBM <= g.M && n0 + GBN <= g.N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+            const float* drow = g.d + row * g.ldd + cbase;
+            float* rowp = g.c + row * g.ldc + cbase;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (full || (row < g.M && cbase + j * 32 < g.N))
+                    rowp[j * 32] = __builtin_fmaf(as, acc[i][j][r], g.beta * drow[j * 32]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The epilogue variant is a compile-time switch so that the plain kernels keep their
+// register allocation.
+template <int EPI>
 __device__ __forceinline__ void finish_tile(const GArgs& g, uint8_t* lds, float16v (&acc)[4][4],
                                             int64_t m0, int64_t n0, int wm, int wn, int h, int li) {
-    if constexpr (LORA) {
+    if constexpr (EPI == EpiLora) {
         lora_epilogue(g, lds, acc, m0, n0, wm, wn, h, li);
         store_tile(g, acc, m0, n0, wm, wn, h, li, 1.0f);
+    } else if constexpr (EPI == EpiAxpby) {
+        store_tile_axpby(g, acc, m0, n0, wm, wn, h, li);
     } else {
         store_tile(g, acc, m0, n0, wm, wn, h, li, *g.asg * *g.bsg);
     }
@@ -363,7 +396,7 @@ __device__ __forceinline__ void store_stage(uint8_t* buf, const StageRegs& r) {
     *(uint2*)(bs + t * 8) = r.sb;
 }
 
-template <bool LORA>
+template <int EPI>
 __global__ __launch_bounds__(GThreads, 1) void k_gemm(GArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6, wm = wid >> 1, wn = wid & 1;
@@ -390,7 +423,7 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm(GArgs g) {
         if (s + 1 < nst) store_stage(lds + ((s + 1) & 1) * kStageBytes, regs);
         __syncthreads();
     }
-    finish_tile<LORA>(g, lds, acc, m0, n0, wm, wn, h, li);
+    finish_tile<EPI>(g, lds, acc, m0, n0, wm, wn, h, li);
 }
 
 // ---------------------------------------------------------------- direct staging path
@@ -605,7 +638,7 @@ __device__ __forceinline__ void piped_stage(const DmaCtx& c, int s, HalfFrags& l
     for (int x = 0; x < 4; ++x) { sa[x] = nsa[x]; sb[x] = nsb[x]; }
 }
 
-template <bool LORA>
+template <int EPI>
 __global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     DmaCtx c;
@@ -647,7 +680,7 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
     make_pairs<0>(sa, sb, p);
     decode_slot<0>(lo, p, av, bv);
     for (int s = 0; s < c.nst; ++s) piped_stage(c, s, lo, hi, sa, sb, p, av, bv, acc);
-    finish_tile<LORA>(g, lds, acc, c.m0, c.n0, c.wm, c.wn, c.h, c.li);
+    finish_tile<EPI>(g, lds, acc, c.m0, c.n0, c.wm, c.wn, c.h, c.li);
 }
 
 }  // namespace nvfp4
@@ -656,7 +689,8 @@ using namespace nvfp4;
 
 static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
                        int64_t K, float* c, int64_t ldc, const uint16_t* lt, const uint16_t* lb,
-                       int64_t lr, void* stream) {
+                       int64_t lr, const float* d, int64_t ldd, float alpha, float beta,
+                       void* stream) {
     if (!a || !b || !a->gscale || !b->gscale) return NVFP4_ERR_NULL;
     if (M < 0 || N < 0 || K < 0 || K % 32 || ldc < N) return NVFP4_ERR_SHAPE;
     if (lr < 0 || lr % 16) return NVFP4_ERR_SHAPE;
@@ -664,6 +698,8 @@ static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M
     if (!c) return NVFP4_ERR_NULL;
     if (K > 0 && (!a->codes || !a->scales || !b->codes || !b->scales)) return NVFP4_ERR_NULL;
     if (lr > 0 && (!lt || !lb)) return NVFP4_ERR_NULL;
+    if (d && ldd < N) return NVFP4_ERR_SHAPE;
+    if (d && ((uintptr_t)d & 3)) return NVFP4_ERR_ALIGN;
     if (((uintptr_t)a->codes & 15) || ((uintptr_t)b->codes & 15) || ((uintptr_t)c & 3) ||
         ((uintptr_t)a->gscale & 3) || ((uintptr_t)b->gscale & 3) || ((uintptr_t)lt & 15) ||
         ((uintptr_t)lb & 15))
@@ -675,6 +711,11 @@ static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M
     g.lt = lr > 0 ? lt : nullptr;
     g.lb = lr > 0 ? lb : nullptr;
     g.lr = lr;
+    g.d = d;
+    g.ldd = d ? ldd : 0;
+    g.alpha = alpha;
+    g.beta = beta;
+    const int epi = d ? EpiAxpby : (lr > 0 ? EpiLora : EpiPlain);
     const int64_t tiles_m = (M + GBM - 1) / GBM, tiles_n = (N + GBN - 1) / GBN;
     g.tiles_m = (int)tiles_m;
     g.tiles_n = (int)tiles_n;
@@ -685,29 +726,41 @@ static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M
     const int64_t kbytes = K / 2, limit = (int64_t)kOutOfRange;
     const bool direct = K > 0 && K % 64 == 0 && ((uintptr_t)a->scales & 3) == 0 &&
                         ((uintptr_t)b->scales & 3) == 0 && M * kbytes < limit && N * kbytes < limit;
-    const void* fn = direct ? (lr > 0 ? (const void*)k_gemm_dma<true> : (const void*)k_gemm_dma<false>)
-                            : (lr > 0 ? (const void*)k_gemm<true> : (const void*)k_gemm<false>);
+    const void* fns[2][3] = {{(const void*)k_gemm<EpiPlain>, (const void*)k_gemm<EpiLora>,
+                              (const void*)k_gemm<EpiAxpby>},
+                             {(const void*)k_gemm_dma<EpiPlain>, (const void*)k_gemm_dma<EpiLora>,
+                              (const void*)k_gemm_dma<EpiAxpby>}};
+    const void* fn = fns[direct ? 1 : 0][epi];
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                             direct ? kGemmDmaLds : kGemmLds) != hipSuccess)
         return NVFP4_ERR_HIP;
     hipStream_t st = (hipStream_t)stream;
     if (direct) {
-        if (lr > 0) k_gemm_dma<true><<<grid, GThreads, kGemmDmaLds, st>>>(g);
-        else k_gemm_dma<false><<<grid, GThreads, kGemmDmaLds, st>>>(g);
+        if (epi == EpiAxpby) k_gemm_dma<EpiAxpby><<<grid, GThreads, kGemmDmaLds, st>>>(g);
+        else if (epi == EpiLora) k_gemm_dma<EpiLora><<<grid, GThreads, kGemmDmaLds, st>>>(g);
+        else k_gemm_dma<EpiPlain><<<grid, GThreads, kGemmDmaLds, st>>>(g);
     } else {
-        if (lr > 0) k_gemm<true><<<grid, GThreads, kGemmLds, st>>>(g);
-        else k_gemm<false><<<grid, GThreads, kGemmLds, st>>>(g);
+        if (epi == EpiAxpby) k_gemm<EpiAxpby><<<grid, GThreads, kGemmLds, st>>>(g);
+        else if (epi == EpiLora) k_gemm<EpiLora><<<grid, GThreads, kGemmLds, st>>>(g);
+        else k_gemm<EpiPlain><<<grid, GThreads, kGemmLds, st>>>(g);
     }
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
 extern "C" int nvfp4_gemm(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
                           int64_t K, float* c, int64_t ldc, void* stream) {
-    return gemm_launch(a, b, M, N, K, c, ldc, nullptr, nullptr, 0, stream);
+    return gemm_launch(a, b, M, N, K, c, ldc, nullptr, nullptr, 0, nullptr, 0, 1.0f, 0.0f, stream);
 }
 
 extern "C" int nvfp4_gemm_lora(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M,
                                int64_t N, int64_t K, float* c, int64_t ldc, const uint16_t* lora_t,
                                const uint16_t* lora_b, int64_t rank, void* stream) {
-    return gemm_launch(a, b, M, N, K, c, ldc, lora_t, lora_b, rank, stream);
+    return gemm_launch(a, b, M, N, K, c, ldc, lora_t, lora_b, rank, nullptr, 0, 1.0f, 0.0f, stream);
+}
+
+extern "C" int nvfp4_gemm_axpby(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M,
+                                int64_t N, int64_t K, float alpha, const float* d, int64_t ldd,
+                                float beta, float* c, int64_t ldc, void* stream) {
+    if (!d) return NVFP4_ERR_NULL;
+    return gemm_launch(a, b, M, N, K, c, ldc, nullptr, nullptr, 0, d, ldd, alpha, beta, stream);
 }

@@ -268,6 +268,31 @@ def requantize_cols(q_row, round_col=RNE, rht_col=False, seed=0, scale46=False):
     return col
 
 
+def ns_step(x, a, b, c, seed, scale46=True):
+    """One quantized Newton-Schulz iteration of NVFP4 Root (Full-Stack FP4 sec. 3.4):
+    qX = Q_1x16(X H), qX' = Q_16x1(H^T X), A = qX qX^T, qA = Q_1x16(A H),
+    qA' = Q_16x1(H^T A), B = b A + c qA qA', qB = Q_1x16(B H), X' = a X + qB qX'.
+    Readings: every quantization nearest-even with 4/6 scaling and one random Hadamard
+    (seed) for the whole iteration; the GEMM products are binary64 over the dequantized
+    copies, A and B are held in binary32 (the GEMM output precision) before being
+    quantized, and B and X' are formed in binary64 and rounded once to binary32.
+    Returns (X', A, B) as binary32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    qx, qxc = quantize(x, rowwise=True, colwise=True, rht_row=True, rht_col=True, seed=seed,
+                       scale46=scale46)
+    A64, _ = gemm_f64(qx, qx)
+    A = A64.astype(np.float32)
+    qa, qac = quantize(A, rowwise=True, colwise=True, rht_row=True, rht_col=True, seed=seed,
+                       scale46=scale46)
+    P, _ = gemm_f64(qa, qac)
+    B = (np.float64(np.float32(b)) * A.astype(np.float64) + np.float64(np.float32(c)) * P) \
+        .astype(np.float32)
+    qb, _ = quantize(B, rowwise=True, rht_row=True, seed=seed, scale46=scale46)
+    Q, _ = gemm_f64(qb, qxc)
+    xn = (np.float64(np.float32(a)) * x.astype(np.float64) + Q).astype(np.float32)
+    return xn, A, B
+
+
 def gemm_lora_f64(qa, qb, t, b):
     """A B^T over the dequantized operands plus t b^T (t [M][r], b [N][r] BF16 bits),
     binary64; returns (C, sum of |terms|)."""

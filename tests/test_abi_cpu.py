@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(nv):
 
 def test_version_and_status_strings(nv):
     lib = nv.load_library()
-    assert lib.nvfp4_abi_version() == nv.ABI_VERSION == 4
+    assert lib.nvfp4_abi_version() == nv.ABI_VERSION == 5
     assert lib.nvfp4_status_string(0) == b"ok"
     for code in range(-7, 0):
         s = lib.nvfp4_status_string(code)
