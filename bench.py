@@ -227,7 +227,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU path is a design note, not part of this build)", file=sys.stderr)
+              "(the multi-GPU path is a design note only)", file=sys.stderr)
         sys.exit(2)
     import torch
     import nvfp4_block_scaled_quantize_amd as nv
@@ -441,7 +441,7 @@ def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream, ite
     LoRA-SVD branch at rank 64
     (X quantize with the L1 down-projection fused, FFN-up GEMM with the L2 up-projection
     fused, and for dX the dY quantize with L2^T and the dgrad GEMM with L1^T); the
-    QKV-projection GEMM of the 3B model; a plain device copy for the box's achievable HBM
+    QKV-projection GEMM of the 3B model; a plain device copy for the device's achievable HBM
     bandwidth."""
     qkv = synthetic.qkv()
     Xq, Wqkv = qkv["X"].to(dev), qkv["W"].to(dev)

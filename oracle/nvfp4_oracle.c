@@ -245,7 +245,7 @@ static int all_finite(const float* x, int64_t count)
 /* 4/6 adaptive block scaling.  [FS4] sec. 3 (and the introduction's list of
  * primitives) applies "4/6 scaling" to every NVFP4 quantization and the related-work
  * paragraph describes it as MSE-optimal adaptive block scaling; the rule itself is not
- * given.  Reading (listed in the design doc): each 1x16 block has two candidate E4M3 scales,
+ * given.  Reading: each 1x16 block has two candidate E4M3 scales,
  * the usual one mapping the block amax to 6 and one mapping it to 4, both formed by the
  * same nearest-even saturating encode with the tensor scale unchanged; the block keeps
  * the candidate whose nearest-even quantization has the smaller squared error, 6 on a
@@ -639,7 +639,7 @@ int or_qadamw_v_decode(const uint16_t* mu, const uint8_t* codes, const uint8_t* 
 /* m_t = beta1 m_{t-1} + g_t and v_t = beta2 v_{t-1} + (1 - beta2) g_t^2; sec.   */
 /* 3.3 stores m_t through a Hadamard rotation, stochastic rounding and 4/6       */
 /* scaling, and v_t through the sqrt / tile-mean / Hadamard / NVFP4 pipeline.   */
-/* The update itself is not printed.  Readings: the gradient        */
+/* The update itself is not printed.  Readings: the gradient                    */
 /* coefficient of m is a parameter (1 in the pages' form, 1 - beta1 in the      */
 /* common one); the update is decoupled AdamW with caller-supplied bias          */
 /* multipliers, w <- w - lr (bias1 m / (sqrt(bias2 v) + eps) + wd w); the m      */
