@@ -34,9 +34,10 @@ __device__ __forceinline__ U4 philox10(U4 c, uint32_t k0, uint32_t k1) {
         uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
         uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
         U4 n;
-        n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+        // three-way exclusive or in one v_bitop3_b32 (truth table 0x96)
+        n.x = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c.y, k0, 0x96);
         n.y = (uint32_t)p1;
-        n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+        n.z = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c.w, k1, 0x96);
         n.w = (uint32_t)p0;
         c = n;
         k0 += 0x9E3779B9u;
@@ -49,10 +50,6 @@ __device__ __forceinline__ U4 philox10(U4 c, uint32_t k0, uint32_t k1) {
 __device__ __forceinline__ U4 sr_words(uint64_t g, uint32_t copy, uint32_t k0, uint32_t k1) {
     U4 c = {(uint32_t)g, (uint32_t)(g >> 32), copy, kTagSR};
     return philox10(c, k0, k1);
-}
-
-__device__ __forceinline__ uint32_t word_of(const U4& w, int i) {
-    return i == 0 ? w.x : (i == 1 ? w.y : (i == 2 ? w.z : w.w));
 }
 
 // 16 sign bits of the random Hadamard diagonal (bit i set -> -1).
@@ -97,21 +94,20 @@ __device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b) {
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
 }
 
-// Stochastic rounding of x * rcp to an E2M1 code with 16 random bits r16: the magnitude
-// u = |x| rcp goes to its upper grid neighbour iff frac + r16 / 2^16 >= 1, frac being u's
-// position between its two neighbours (saturating at 6).  Only the 16 bits of u just
-// below the grid spacing can change that decision, so it is taken exactly on integers:
-//   u >= 1: the grid keeps one mantissa bit, and rounding up is the carry of
-//           bits(u) + (r16 << 6) out of the 22 dropped mantissa bits; the kept exponent
-//           and mantissa bit then read as code + 252 (clamped to 7 = 6.0);
-//   u <  1: the spacing is 1/2, and floor(u * 2^17) + r16 carries into bit 16 exactly
-//           when 2u's fraction plus r16 / 2^16 reaches 1; the quotient is the code (0..2).
-// No branches: both candidates are formed and one is selected.
-__device__ __forceinline__ uint32_t sr_code(float x, float rcp, uint32_t r16) {
-    const float u = fabsf(x) * rcp;
-    const uint32_t ca = min(((__float_as_uint(u) + (r16 << 6)) >> 22) - 252u, 7u);
-    const uint32_t cb = ((uint32_t)(fminf(u, 1.0f) * 131072.0f) + r16) >> 16;
-    return (u < 1.0f ? cb : ca) | ((__float_as_uint(x) >> 28) & 8u);
+// Stochastic rounding of one value v = x * rcp to an E2M1 code with 16 random bits r16: the
+// magnitude |v| goes to its upper grid neighbour iff floor(frac * 2^16) + r16 >= 2^16, frac
+// being its position between its two grid neighbours (saturating at 6, sign copied).
+// gfx950's v_cvt_scalef32_sr_pk_fp4_f32 rounds the first value of its pair by adding bits
+// 10..31 of its seed to the 22 leading bits of that fraction and keeping the carry, in the
+// subnormal range (|v| < 1, spacing 1/2) as in the normal one.  With seed = r16 << 16 the
+// six low added bits are zero, so the carry is the rule's exactly.  The second value of the
+// pair is 0.0, whose code is 0 for every seed.  Only byte 0 of the result is defined (code in
+// bits 0..3, bits 4..7 zero): the compiler does not carry the builtin's first operand into
+// the bytes the instruction leaves alone.  (A GPU test compares the conversion with the
+// plain rule for every finite binary32 value.)
+__device__ __forceinline__ uint32_t cvt_fp4_sr(float v, uint32_t seed) {
+    const float2v p = {v, 0.0f};
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, seed, 1.0f, 0);
 }
 
 // Decode the two E2M1 codes in byte SEL of w to binary32 (exact).

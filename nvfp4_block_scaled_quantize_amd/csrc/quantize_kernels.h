@@ -329,16 +329,25 @@ __device__ __forceinline__ uint32_t encode8_rne(const float w[8], float rcp) {
     return r;
 }
 
-// Codes for 8 values (one dword), stochastic, with the 4 Philox words of their group.
+// Codes for 8 values (one dword), stochastic, with the 4 Philox words of their group:
+// element 2b takes the low half of word b, element 2b + 1 the high half.  Each conversion
+// leaves its code in byte 0 of its result; byte permutes gather the even codes into the
+// bytes of one dword and the odd ones into another, which is shifted into the high nibbles.
 __device__ __forceinline__ uint32_t encode8_sr(const float w[8], float rcp, const U4& rw) {
-    uint32_t r = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        uint32_t word = word_of(rw, e >> 1);
-        uint32_t r16 = (e & 1) ? (word >> 16) : (word & 0xFFFFu);
-        r |= sr_code(w[e], rcp, r16) << (4 * e);
-    }
-    return r;
+    const uint32_t c0 = cvt_fp4_sr(w[0] * rcp, rw.x << 16);
+    const uint32_t c1 = cvt_fp4_sr(w[1] * rcp, rw.x & 0xFFFF0000u);
+    const uint32_t c2 = cvt_fp4_sr(w[2] * rcp, rw.y << 16);
+    const uint32_t c3 = cvt_fp4_sr(w[3] * rcp, rw.y & 0xFFFF0000u);
+    const uint32_t c4 = cvt_fp4_sr(w[4] * rcp, rw.z << 16);
+    const uint32_t c5 = cvt_fp4_sr(w[5] * rcp, rw.z & 0xFFFF0000u);
+    const uint32_t c6 = cvt_fp4_sr(w[6] * rcp, rw.w << 16);
+    const uint32_t c7 = cvt_fp4_sr(w[7] * rcp, rw.w & 0xFFFF0000u);
+    // selector bytes 0..3 pick bytes of the second operand, 4..7 of the first, 0x0C gives 0
+    const uint32_t ev = __builtin_amdgcn_perm(c2, c0, 0x0C0C0400u) |
+                        __builtin_amdgcn_perm(c6, c4, 0x04000C0Cu);
+    const uint32_t od = __builtin_amdgcn_perm(c3, c1, 0x0C0C0400u) |
+                        __builtin_amdgcn_perm(c7, c5, 0x04000C0Cu);
+    return ev | (od << 4);
 }
 
 // 4/6 adaptive block scaling: squared error of 8 values quantized nearest-even with block

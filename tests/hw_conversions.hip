@@ -8,6 +8,11 @@
 //  * E2M1 element: v_cvt_scalef32_pk_fp4_f32 at scale 1.0 against the threshold form of
 //    nearest-even rounding to {0, 0.5, 1, 1.5, 2, 3, 4, 6} (ties to the even code,
 //    saturation at 6, sign copied), for every finite binary32.
+//  * E2M1 stochastic rounding: v_cvt_scalef32_sr_pk_fp4_f32 at scale 1.0, first value of
+//    the pair with seed r16 << 16 (second value 0.0), against the rule "up iff
+//    floor(frac * 2^16) + r16 >= 2^16" (frac: the position between the two grid
+//    neighbours, in binary64; saturation at 6, sign copied).  Every finite binary32 with a
+//    hashed r16, and every r16 for the multiples of 1/256 in [0, 8) of both signs.
 // Nothing here is shared with the library's kernels.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -57,15 +62,56 @@ __global__ void k_check_e2m1(uint64_t lo, uint32_t n, unsigned long long* bad, u
     if (ref != hw && atomicAdd(bad, 1ull) == 0ull) *first = bits;
 }
 
-// Runs both checks; returns 0 and fills counts[0..1] (mismatches) and first[0..1] (first
-// mismatching input bits), or a HIP error code.
+// Stochastic rounding by its definition, in binary64 (u - grid[k] and the division by the
+// spacing are exact there).
+__device__ uint32_t e2m1_sr_rule(float x, uint32_t r16) {
+    const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    const uint32_t sign = (__float_as_uint(x) >> 28) & 8u;
+    const double u = fabs((double)x);
+    if (u >= 6.0) return 7u | sign;
+    uint32_t k = 0;
+    while (k < 7 && grid[k + 1] <= u) ++k;
+    const double frac = (u - grid[k]) / (grid[k + 1] - grid[k]);
+    const double t = floor(frac * 65536.0);
+    return (t + (double)r16 >= 65536.0 ? k + 1 : k) | sign;
+}
+
+__device__ uint32_t e2m1_sr_hw(float x, uint32_t r16) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 p = {x, 0.0f};
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, r16 << 16, 1.0f, 0) & 0xFFu;
+}
+
+// every finite binary32, r16 from a multiplicative hash of its bits
+__global__ void k_check_sr_all(uint64_t lo, uint32_t n, unsigned long long* bad, uint32_t* first) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t bits = (uint32_t)(lo + i);
+    if ((bits & 0x7F800000u) == 0x7F800000u) return;
+    const float x = __uint_as_float(bits);
+    const uint32_t r16 = (bits * 0x9E3779B1u) >> 16;
+    if (e2m1_sr_rule(x, r16) != e2m1_sr_hw(x, r16) && atomicAdd(bad, 1ull) == 0ull) *first = bits;
+}
+
+// index i: r16 = i mod 2^16, x = +-(j / 256) with j = (i >> 17) in [0, 2048), sign bit 16
+__global__ void k_check_sr_thresholds(unsigned long long* bad, uint32_t* first) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;   // grid covers exactly 2^28
+    const uint32_t r16 = i & 0xFFFFu;
+    const float m = (float)(i >> 17) * 0.00390625f;
+    const float x = ((i >> 16) & 1u) ? -m : m;
+    if (e2m1_sr_rule(x, r16) != e2m1_sr_hw(x, r16) && atomicAdd(bad, 1ull) == 0ull)
+        *first = __float_as_uint(x);
+}
+
+// Runs the checks; returns 0 and fills counts[0..2] (mismatches: E4M3, E2M1 nearest-even,
+// E2M1 stochastic) and first[0..2] (first mismatching input bits), or a HIP error code.
 extern "C" int hwcheck_run(unsigned long long* counts, uint32_t* first) {
     unsigned long long* d_bad = nullptr;
     uint32_t* d_first = nullptr;
-    if (hipMalloc(&d_bad, 2 * sizeof(unsigned long long)) != hipSuccess) return 1;
-    if (hipMalloc(&d_first, 2 * sizeof(uint32_t)) != hipSuccess) return 1;
-    hipMemset(d_bad, 0, 2 * sizeof(unsigned long long));
-    hipMemset(d_first, 0, 2 * sizeof(uint32_t));
+    if (hipMalloc(&d_bad, 3 * sizeof(unsigned long long)) != hipSuccess) return 1;
+    if (hipMalloc(&d_first, 3 * sizeof(uint32_t)) != hipSuccess) return 1;
+    (void)hipMemset(d_bad, 0, 3 * sizeof(unsigned long long));
+    (void)hipMemset(d_first, 0, 3 * sizeof(uint32_t));
     const uint32_t chunk = 1u << 28;
     const uint32_t nonneg = 0x7F800000u;   // every non-negative finite pattern
     for (uint32_t lo = 0; lo < nonneg; lo += chunk) {
@@ -74,10 +120,13 @@ extern "C" int hwcheck_run(unsigned long long* counts, uint32_t* first) {
     }
     for (uint64_t lo = 0; lo < (1ull << 32); lo += chunk)
         k_check_e2m1<<<chunk / 256, 256>>>(lo, chunk, d_bad + 1, d_first + 1);
+    for (uint64_t lo = 0; lo < (1ull << 32); lo += chunk)
+        k_check_sr_all<<<chunk / 256, 256>>>(lo, chunk, d_bad + 2, d_first + 2);
+    k_check_sr_thresholds<<<(1u << 28) / 256, 256>>>(d_bad + 2, d_first + 2);
     int rc = hipDeviceSynchronize() == hipSuccess ? 0 : 2;
-    hipMemcpy(counts, d_bad, 2 * sizeof(unsigned long long), hipMemcpyDeviceToHost);
-    hipMemcpy(first, d_first, 2 * sizeof(uint32_t), hipMemcpyDeviceToHost);
-    hipFree(d_bad);
-    hipFree(d_first);
+    (void)hipMemcpy(counts, d_bad, 3 * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+    (void)hipMemcpy(first, d_first, 3 * sizeof(uint32_t), hipMemcpyDeviceToHost);
+    (void)hipFree(d_bad);
+    (void)hipFree(d_first);
     return rc;
 }
