@@ -28,16 +28,24 @@ typedef float float16v __attribute__((ext_vector_type(16)));
 // ---------------------------------------------------------------- Philox4x32-10
 struct U4 { uint32_t x, y, z, w; };
 
+// VEC: per-lane counters, the three-way exclusive ors as one v_bitop3_b32 each (truth table
+// 0x96).  Otherwise plain exclusive ors, which the compiler keeps on the scalar unit when the
+// counter and key are uniform (v_bitop3_b32 is a vector instruction).
+template <bool VEC = true>
 __device__ __forceinline__ U4 philox10(U4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
         uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
         uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
         U4 n;
-        // three-way exclusive or in one v_bitop3_b32 (truth table 0x96)
-        n.x = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c.y, k0, 0x96);
+        if constexpr (VEC) {
+            n.x = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c.y, k0, 0x96);
+            n.z = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c.w, k1, 0x96);
+        } else {
+            n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+            n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+        }
         n.y = (uint32_t)p1;
-        n.z = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c.w, k1, 0x96);
         n.w = (uint32_t)p0;
         c = n;
         k0 += 0x9E3779B9u;
@@ -55,7 +63,7 @@ __device__ __forceinline__ U4 sr_words(uint64_t g, uint32_t copy, uint32_t k0, u
 // 16 sign bits of the random Hadamard diagonal (bit i set -> -1).
 __device__ __forceinline__ uint32_t rht_sign_bits(uint32_t k0, uint32_t k1) {
     U4 c = {0u, 0u, 0u, kTagRHT};
-    return philox10(c, k0, k1).x & 0xFFFFu;
+    return philox10<false>(c, k0, k1).x & 0xFFFFu;
 }
 
 __device__ __forceinline__ float apply_sign(float v, uint32_t bits, int i) {

@@ -125,12 +125,18 @@ __global__ __launch_bounds__(QVThreads) void k_qv_pass1(QVArgs a) {
 
 __global__ __launch_bounds__(QVThreads) void k_qv_pass2(QVArgs a) {
     __shared__ float red[4];
+    __shared__ float rtab[128];   // element reciprocal per scale code
     float am = 0.0f;
     for (int i = threadIdx.x; i < a.nblocks; i += QVThreads) am = fmaxf(am, a.partial[i]);
     am = block_max1(am, red);
-    float sg = __fdiv_rn(am, 2688.0f);
-    if (sg == 0.0f) sg = 1.0f;
+    const float sg = uniform_f(sg_from_amax(am));
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.sg = sg;
+    if (threadIdx.x < 128) {
+        const uint32_t t = threadIdx.x;
+        rtab[t] = t ? __fdiv_rn(1.0f, e4m3_value(t) * sg) : 0.0f;
+    }
+    __syncthreads();
+    const CopyScale csc{sg, __fdiv_rn(1.0f, sg), sg >= 0x1p-92f, rtab};
 
     int64_t r, c;
     bool valid;
@@ -141,9 +147,8 @@ __global__ __launch_bounds__(QVThreads) void k_qv_pass2(QVArgs a) {
     float bm = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(e[i]));
-    const uint32_t scode = e4m3_encode(__fdiv_rn(__fdiv_rn(bm, 6.0f), sg));
-    const float d = e4m3_value(scode) * sg;
-    const float rcp = scode ? __fdiv_rn(1.0f, d) : 0.0f;
+    const uint32_t scode = csc.code(bm, 6.0f, kRcp6);
+    const float rcp = csc.rcp(scode);
     uint32_t lo = 0, hi = 0;
     lo = cvt_fp4x2<0>(lo, e[0] * rcp, e[1] * rcp);
     lo = cvt_fp4x2<1>(lo, e[2] * rcp, e[3] * rcp);
@@ -332,14 +337,23 @@ __global__ __launch_bounds__(QVThreads) void k_qs_pass1(QSArgs a) {
 
 __global__ __launch_bounds__(QVThreads) void k_qs_pass2(QSArgs a) {
     __shared__ float red[8];
+    __shared__ float rtab[2][128];   // element reciprocal per scale code: m, v
     float am = 0.0f, av = 0.0f;
     for (int i = threadIdx.x; i < a.nblocks; i += QVThreads) {
         am = fmaxf(am, a.partial[i]);
         av = fmaxf(av, a.partial[a.nblocks + i]);
     }
     block_max2(am, av, red);
-    const float sgm = sg_from_amax(am), sgv = sg_from_amax(av);
+    const float sgm = uniform_f(sg_from_amax(am)), sgv = uniform_f(sg_from_amax(av));
     if (blockIdx.x == 0 && threadIdx.x == 0) { *a.msgo = sgm; *a.vsgo = sgv; }
+    {
+        const uint32_t t = threadIdx.x & 127;
+        const float sg = threadIdx.x < 128 ? sgm : sgv;
+        rtab[threadIdx.x >> 7][t] = t ? __fdiv_rn(1.0f, e4m3_value(t) * sg) : 0.0f;
+    }
+    __syncthreads();
+    const CopyScale msc{sgm, __fdiv_rn(1.0f, sgm), sgm >= 0x1p-92f, rtab[0]};
+    const CopyScale vsc{sgv, __fdiv_rn(1.0f, sgv), sgv >= 0x1p-92f, rtab[1]};
 
     int64_t r, c;
     bool valid;
@@ -374,14 +388,15 @@ __global__ __launch_bounds__(QVThreads) void k_qs_pass2(QSArgs a) {
         float bm = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(y[i]));
-        uint32_t sc = e4m3_encode(__fdiv_rn(__fdiv_rn(bm, 6.0f), sgm));
-        const uint32_t sc4 = e4m3_encode(__fdiv_rn(__fdiv_rn(bm, 4.0f), sgm));
+        uint32_t sc = msc.code(bm, 6.0f, kRcp6);
+        const uint32_t sc4 = msc.code(bm, 4.0f, 0.25f);
+        const float s6 = e4m3_value(sc), s4 = e4m3_value(sc4);
+        const float q6 = msc.rcp(sc), q4 = msc.rcp(sc4);
         uint32_t t0, t1, t2, t3;
-        const float e6 = sse8_rne(&y[0], sc, sgm, t0) + sse8_rne(&y[8], sc, sgm, t1);
-        const float e4 = sse8_rne(&y[0], sc4, sgm, t2) + sse8_rne(&y[8], sc4, sgm, t3);
+        const float e6 = sse8_rne(&y[0], s6, q6, sgm, t0) + sse8_rne(&y[8], s6, q6, sgm, t1);
+        const float e4 = sse8_rne(&y[0], s4, q4, sgm, t2) + sse8_rne(&y[8], s4, q4, sgm, t3);
         sc = e4 < e6 ? sc4 : sc;
-        const float d = e4m3_value(sc) * sgm;
-        const float rcp = sc ? __fdiv_rn(1.0f, d) : 0.0f;
+        const float rcp = e4 < e6 ? q4 : q6;
         const uint64_t g0 = ((uint64_t)r * (uint64_t)a.cols + (uint64_t)c) >> 3;
         const uint32_t lo = encode8_sr(&y[0], rcp, sr_words(g0, 0u, a.sk0, a.sk1));
         const uint32_t hi = encode8_sr(&y[8], rcp, sr_words(g0 + 1, 0u, a.sk0, a.sk1));
@@ -396,9 +411,8 @@ __global__ __launch_bounds__(QVThreads) void k_qs_pass2(QSArgs a) {
         float bm = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(e[i]));
-        const uint32_t sc = e4m3_encode(__fdiv_rn(__fdiv_rn(bm, 6.0f), sgv));
-        const float d = e4m3_value(sc) * sgv;
-        const float rcp = sc ? __fdiv_rn(1.0f, d) : 0.0f;
+        const uint32_t sc = vsc.code(bm, 6.0f, kRcp6);
+        const float rcp = vsc.rcp(sc);
         const uint32_t lo = encode8_rne(&e[0], rcp), hi = encode8_rne(&e[8], rcp);
         if (valid) {
             *(uint2*)(a.vco + r * (a.cols / 2) + c / 2) = make_uint2(lo, hi);
