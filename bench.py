@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "NVFP4 quantize GB/s + W4A4 GEMM TFLOP/s at 8192×3072×9216 (% of roofline)"
 PEAK_HBM_GBPS = 8000.0
 PEAK_F16_TFLOPS = 2500.0   # dense f16/bf16 MFMA, MI355X
+PEAK_FP4_TFLOPS = 10100.0  # dense FP4 MFMA, MI355X: the hardware ceiling of a 4-bit GEMM
 TOKENS, HIDDEN, FFN = 8192, 3072, 9216
 SEED_WGRAD, SEED_QADAMW = 0x5EED4, 0x5EED5
 
@@ -123,8 +124,8 @@ def trace_summary(d):
     import csv
     import glob as _glob
     stats = list(csv.DictReader(open(_glob.glob(os.path.join(d, "*kernel_stats.csv"))[0])))
-    trace = list(csv.DictReader(open(_glob.glob(os.path.join(d, "*kernel_trace.csv"))[0])))
-    trace = [r for r in trace if "nvfp4::" in r["Kernel_Name"]]
+    raw = list(csv.DictReader(open(_glob.glob(os.path.join(d, "*kernel_trace.csv"))[0])))
+    trace = [r for r in raw if "nvfp4::" in r["Kernel_Name"]]
     trace.sort(key=lambda r: int(r["Start_Timestamp"]))
     dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace]
     per = {}
@@ -136,16 +137,23 @@ def trace_summary(d):
              "#       -- python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline",
              "#   python3 bench.py --trace-summary <kt>",
              "# per kernel (all steps, warm-up included):",
-             f"# {'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'share%':>7s}"]
+             f"# {'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'med_us':>9s} {'min_us':>9s} {'max_us':>9s} {'share%':>7s}"]
+    alld = {}
+    for r in raw:
+        alld.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     for r in stats:
+        v = sorted(alld.get(r["Name"], [])) or [float("nan")]
         lines.append(f"{r['Name'][:62]:62s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
-                     f"{int(r['MinNs']) / 1e3:9.2f} {int(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):7.2f}")
+                     f"{v[len(v) // 2]:9.2f} {int(r['MinNs']) / 1e3:9.2f} {int(r['MaxNs']) / 1e3:9.2f} "
+                     f"{float(r['Percentage']):7.2f}")
     lines.append("# per call of the step (sum of its kernels' durations), from the dispatch trace:")
-    lines.append(f"# {'call':28s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}")
+    lines.append(f"# {'call':28s} {'calls':>6s} {'avg_us':>9s} {'med_us':>9s} {'min_us':>9s} {'max_us':>9s}")
     for key, _ in STEP_ORDER:
-        v = per.get(key, [])
+        v = sorted(per.get(key, []))
         if v:
-            lines.append(f"{key:30s} {len(v):6d} {sum(v) / len(v):9.2f} {min(v):9.2f} {max(v):9.2f}")
+            lines.append(f"{key:30s} {len(v):6d} {sum(v) / len(v):9.2f} {v[len(v) // 2]:9.2f} "
+                         f"{min(v):9.2f} {max(v):9.2f}")
     out = os.path.join(ROOT, "profiles", "ffn3b_step_kernel_stats.txt")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -378,6 +386,7 @@ def main():
         if kind == "gemm":
             d["TFLOP/s"] = round(flops / ms / 1e9, 1)
             d["frac_f16_peak"] = round(flops / ms / 1e9 / PEAK_F16_TFLOPS, 4)
+            d["frac_fp4_peak"] = round(flops / ms / 1e9 / PEAK_FP4_TFLOPS, 4)
         d["GB/s"] = round(nbytes / ms / 1e6, 1)
         if kind == "quant":
             d["frac_hbm_peak"] = round(nbytes / ms / 1e6 / PEAK_HBM_GBPS, 4)
@@ -428,10 +437,45 @@ def main():
         "kernels": kernels,
     }
 
+    out["kernels_isolated"] = isolated(torch, dev, calls, work, stream)
     out["extras"] = extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, synthetic, ffn)
     print(json.dumps(out))
+
+
+def isolated(torch, dev, calls, work, stream, reps=10):
+    """Each call of the step on its own, median of `reps` HIP-event timings: cold (512 MiB
+    of scratch written before every call, so the 256 MB last-level cache holds none of its
+    inputs) and warm (the call repeated back to back, inputs left in the caches)."""
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    res = {}
+    for name, fn in calls():
+        kind, nbytes, flops = work[name]
+        times = {}
+        for mode in ("cold", "warm"):
+            ev = []
+            fn()
+            for i in range(reps):
+                if mode == "cold":
+                    scratch.fill_(i & 0xFF)
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record(stream)
+                fn()
+                e.record(stream)
+                ev.append((s, e))
+            torch.cuda.synchronize()
+            t = sorted(s.elapsed_time(e) for s, e in ev)
+            times[mode] = t[len(t) // 2]
+        d = {"cold_ms": round(times["cold"], 5), "warm_ms": round(times["warm"], 5)}
+        if kind == "gemm":
+            d["cold_TFLOP/s"] = round(flops / times["cold"] / 1e9, 1)
+            d["warm_TFLOP/s"] = round(flops / times["warm"] / 1e9, 1)
+        else:
+            d["cold_GB/s"] = round(nbytes / times["cold"] / 1e6, 1)
+            d["warm_GB/s"] = round(nbytes / times["warm"] / 1e6, 1)
+        res[name] = d
+    return res
 
 
 def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream, iters=20):
@@ -531,6 +575,7 @@ def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream, ite
         elif flops:
             d["TFLOP/s"] = round(flops / ms / 1e9, 1)
             d["frac_f16_peak"] = round(flops / ms / 1e9 / PEAK_F16_TFLOPS, 4)
+            d["frac_fp4_peak"] = round(flops / ms / 1e9 / PEAK_FP4_TFLOPS, 4)
         else:
             d["frac_hbm_peak"] = round(nbytes / ms / 1e6 / PEAK_HBM_GBPS, 4)
         res[name] = d
@@ -553,8 +598,29 @@ def cpu_baseline(args, synthetic, ffn):
     t2 = time.perf_counter()
     flops = 2.0 * rows * FFN * HIDDEN
     qbytes_ = 2 * (rows + FFN) * HIDDEN + qbytes(rows, HIDDEN) + qbytes(FFN, HIDDEN)
+    # the same at one thread, on 1/16 of the rows and W_up (the GEMM scales with both)
+    threads = oracle.num_threads()
+    r1, n1 = max(rows // 16, 16), FFN // 16
+    oracle.set_num_threads(1)
+    t3 = time.perf_counter()
+    qa1, _ = oracle.quantize(x[:r1])
+    qb1, _ = oracle.quantize(w[:n1], block2d=True)
+    oracle.gemm_f64(qa1, qb1)
+    t4 = time.perf_counter()
+    oracle.set_num_threads(threads)
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(flops / (t2 - t0) / 1e12, 6), "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": threads, "kind": "oracle", "cpu_model": model, "nproc": os.cpu_count(),
+            "one_thread": {"TFLOP/s": round(2.0 * r1 * n1 * HIDDEN / (t4 - t3) / 1e12, 6),
+                           "sample": f"X[:{r1}] and W_up[:{n1}], quantize + binary64 GEMM",
+                           "seconds": round(t4 - t3, 2)},
             "sample": f"FFN-up: quantize X[:{rows}] (1x16) and W_up 9216x3072 (16x16), then the "
                       f"binary64 GEMM {rows}x9216x3072; TFLOP/s counts the GEMM flops over the "
                       f"quantize+GEMM time",

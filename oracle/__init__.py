@@ -64,6 +64,7 @@ def _load():
         "or_qadamw_v_encode": (ctypes.c_int, [P, i64, i64, u64, ctypes.c_int, P, P, P, P]),
         "or_qadamw_v_decode": (ctypes.c_int, [P, P, P, f32, i64, i64, u64, ctypes.c_int, P]),
         "or_num_threads": (ctypes.c_int, []),
+        "or_set_num_threads": (None, [ctypes.c_int]),
         "or_lora_down": (ctypes.c_int, [P, i64, i64, P, i64, f32, P, P, P]),
         "or_gemm_lora_f64": (ctypes.c_int, [P, P, f32, P, P, f32, i64, i64, i64, P, P, i64, P, P]),
         "or_gemm_lora_f64_entries": (ctypes.c_int, [P, P, f32, P, P, f32, i64, i64, i64, P, P, i64,
@@ -119,6 +120,11 @@ def bf16_value(b):
 
 def num_threads():
     return _load().or_num_threads()
+
+
+def set_num_threads(n):
+    """Thread count of the C oracle's row loops (timing only: results do not depend on it)."""
+    _load().or_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- generator, transforms

@@ -707,3 +707,13 @@ int or_num_threads(void)
     return 1;
 #endif
 }
+
+/* Thread count of the OpenMP row loops (timing only; results do not depend on it). */
+void or_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

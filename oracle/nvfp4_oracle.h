@@ -138,6 +138,7 @@ int or_qadamw_step(float* w, const float* g, int64_t R, int64_t C,
                    float* m_new_out, float* v_new_out);
 
 int or_num_threads(void);
+void or_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
