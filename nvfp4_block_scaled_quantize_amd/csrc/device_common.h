@@ -169,6 +169,10 @@ __device__ __forceinline__ void static_for(Fn&& f) {
 __device__ __forceinline__ float xor1(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
+// The value held by lane ^ 2 (DPP quad permutation [2,3,0,1]).
+__device__ __forceinline__ float xor2(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
 
 // Correctly rounded a / b from r_b = RN(1 / b) (Markstein's correction: q = RN(a r_b) is
 // within one ulp, the residual a - q b is exact in one fma, and RN(q + residual * r_b) is

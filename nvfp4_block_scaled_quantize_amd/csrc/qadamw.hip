@@ -203,6 +203,50 @@ __global__ __launch_bounds__(QVThreads) void k_qv_decode(const uint16_t* mu, con
     for (int q = 0; q < 4; ++q) p[q] = make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
 }
 
+// The same for cols a multiple of 1024, laid out for whole-wave stores (as the dequantizer's
+// wide kernel): a wave takes 1024 consecutive elements of one row in four slices of 256, and
+// in slice q lane l holds positions 4 (l mod 4) .. + 3 of block 16 q + l / 4, so a block is one
+// DPP quad.  The butterfly's stages 1 and 2 stay in-register, stages 4 and 8 pair the lane
+// with lane ^ 1 and lane ^ 2: the lower lane forms a + b, the upper b' - b'' as p - w with
+// p the partner's value, the same operations on the same operands as wht16.
+__global__ __launch_bounds__(QVThreads) void k_qv_decode_w(const uint16_t* mu, const uint8_t* codes,
+                                                           const uint8_t* scales, const float* gs,
+                                                           int64_t nwaves, int64_t cols, uint32_t k0,
+                                                           uint32_t k1, int use_signs, float* out) {
+    const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w >= nwaves) return;
+    const int lane = threadIdx.x & 63, j = lane & 3;
+    const int64_t spans = cols >> 10, kb = cols / 16;
+    const int64_t r = w / spans, c0 = (w - r * spans) << 10;
+    const float sg = *gs;
+    const uint32_t signs = use_signs ? rht_sign_bits(k0, k1) : 0u;
+    const float up1 = (j & 1) ? -1.0f : 1.0f, up2 = (j & 2) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t c = c0 + q * 256 + 4 * lane, b = c / 16;
+        const uint32_t cw = *(const uint16_t*)(codes + r * (cols / 2) + c / 2);
+        const float s = e4m3_value(scales[r * kb + b]);
+        const float muf = bf16_to_f32(mu[(r / 16) * kb + b]);
+        const float2v p0 = fp4x2_to_f32<0>(cw), p1 = fp4x2_to_f32<1>(cw);
+        float x[4] = {(p0.x * s) * sg, (p0.y * s) * sg, (p1.x * s) * sg, (p1.y * s) * sg};
+        // stages 1 and 2 (positions within the lane)
+        float a = x[0] + x[1], bb = x[0] - x[1], cc = x[2] + x[3], d = x[2] - x[3];
+        x[0] = a + cc; x[2] = a - cc; x[1] = bb + d; x[3] = bb - d;
+        // stage 4: lane ^ 1; stage 8: lane ^ 2
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] = __builtin_fmaf(x[t], up1, xor1(x[t]));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] = __builtin_fmaf(x[t], up2, xor2(x[t]));
+        float o[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float z = apply_sign(x[t] * 0.25f, signs, 4 * j + t) + muf;
+            o[t] = z * z;
+        }
+        *(float4*)(out + r * cols + c) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+}
+
 // ---------------------------------------------------------------- full AdamW step
 // Full-Stack FP4 sec. 2 (moments m = beta1 m + c g, v = beta2 v + (1 - beta2) g^2) and sec.
 // 3.3 (m stored through a Hadamard rotation, 4/6 scaling and stochastic rounding; v through
@@ -472,10 +516,17 @@ extern "C" int qadamw_v_decode(const uint16_t* mu, const nvfp4_qtensor* q, int64
     if (!q->codes || !q->scales || !q->gscale || !mu || !v_out) return NVFP4_ERR_NULL;
     if (((uintptr_t)v_out & 15) || ((uintptr_t)q->codes & 7) || ((uintptr_t)mu & 1))
         return NVFP4_ERR_ALIGN;
-    const int64_t blocks = rows * (cols / 16);
-    k_qv_decode<<<(unsigned)((blocks + 255) / 256), 256, 0, (hipStream_t)stream>>>(
-        mu, q->codes, q->scales, q->gscale, rows, cols, (uint32_t)seed, (uint32_t)(seed >> 32),
-        use_signs != 0, v_out);
+    if (cols % 1024 == 0) {
+        const int64_t nwaves = rows * (cols / 1024);
+        k_qv_decode_w<<<(unsigned)((nwaves + 3) / 4), 256, 0, (hipStream_t)stream>>>(
+            mu, q->codes, q->scales, q->gscale, nwaves, cols, (uint32_t)seed,
+            (uint32_t)(seed >> 32), use_signs != 0, v_out);
+    } else {
+        const int64_t blocks = rows * (cols / 16);
+        k_qv_decode<<<(unsigned)((blocks + 255) / 256), 256, 0, (hipStream_t)stream>>>(
+            mu, q->codes, q->scales, q->gscale, rows, cols, (uint32_t)seed, (uint32_t)(seed >> 32),
+            use_signs != 0, v_out);
+    }
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

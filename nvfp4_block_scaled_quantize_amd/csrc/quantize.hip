@@ -51,6 +51,40 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* codes, const uin
     }
 }
 
+// The same for k a multiple of 1024, laid out for whole-wave stores: a wave takes 1024
+// consecutive elements of one row in four slices of 256, and in slice q lane l decodes the
+// four elements at 256 q + 4 l (two code bytes of block 16 q + l / 4).  Each store
+// instruction of the wave then writes 1 KB (f32) or 512 B (bf16) of contiguous output,
+// where one block per lane writes 16 bytes every 64.
+__global__ __launch_bounds__(256) void k_dequant_w(const uint8_t* codes, const uint8_t* scales,
+                                                   const float* gscale, int64_t nwaves, int64_t k,
+                                                   int out_bf16, void* out, int64_t ld_out) {
+    const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w >= nwaves) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t spans = k >> 10;
+    const int64_t r = w / spans, c0 = (w - r * spans) << 10;
+    const float sg = *gscale;
+    const uint8_t* crow = codes + r * (k / 2);
+    const uint8_t* srow = scales + r * (k / 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t c = c0 + q * 256 + 4 * lane;
+        const uint32_t cw = *(const uint16_t*)(crow + c / 2);
+        const float s = e4m3_value(srow[c / 16]);
+        const float2v p0 = fp4x2_to_f32<0>(cw), p1 = fp4x2_to_f32<1>(cw);
+        const float o0 = (p0.x * s) * sg, o1 = (p0.y * s) * sg;
+        const float o2 = (p1.x * s) * sg, o3 = (p1.y * s) * sg;
+        if (!out_bf16) {
+            *(float4*)((float*)out + r * ld_out + c) = make_float4(o0, o1, o2, o3);
+        } else {
+            *(uint2*)((uint16_t*)out + r * ld_out + c) =
+                make_uint2(f32_to_bf16_rne(o0) | (f32_to_bf16_rne(o1) << 16),
+                           f32_to_bf16_rne(o2) | (f32_to_bf16_rne(o3) << 16));
+        }
+    }
+}
+
 }  // namespace nvfp4
 
 using namespace nvfp4;
@@ -329,9 +363,15 @@ extern "C" int nvfp4_dequantize(const nvfp4_qtensor* q, int64_t n, int64_t k, in
     if (!out) return NVFP4_ERR_NULL;
     const int64_t esize = out_dtype == NVFP4_BF16 ? 2 : 4;
     if (!aligned(out, 16) || (ld_out * esize) % 16) return NVFP4_ERR_ALIGN;
-    const int64_t blocks = n * (k / 16);
-    const int64_t grid = (blocks + 255) / 256;
-    k_dequant<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>(q->codes, q->scales, q->gscale, n, k,
-                                                             out_dtype == NVFP4_BF16, out, ld_out);
+    if (k % 1024 == 0) {
+        const int64_t nwaves = n * (k / 1024);
+        k_dequant_w<<<(unsigned)((nwaves + 3) / 4), 256, 0, (hipStream_t)stream>>>(
+            q->codes, q->scales, q->gscale, nwaves, k, out_dtype == NVFP4_BF16, out, ld_out);
+    } else {
+        const int64_t blocks = n * (k / 16);
+        const int64_t grid = (blocks + 255) / 256;
+        k_dequant<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>(q->codes, q->scales, q->gscale, n,
+                                                                 k, out_dtype == NVFP4_BF16, out, ld_out);
+    }
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }

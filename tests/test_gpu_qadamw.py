@@ -37,7 +37,8 @@ def check(nv, oracle, v, seed, use_signs):
     assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("shape", [(16, 16), (48, 80), (64, 512), (272, 400)])
+# widths that are multiples of 1024 decode in the whole-wave layout
+@pytest.mark.parametrize("shape", [(16, 16), (48, 80), (64, 512), (272, 400), (32, 1024), (48, 2048)])
 @pytest.mark.parametrize("use_signs", [0, 1])
 def test_qadamw_matches_oracle(nv, oracle, shape, use_signs):
     from nvfp4_block_scaled_quantize_amd import synthetic

@@ -140,13 +140,20 @@ def test_empty_and_zero_tensors(nv, oracle):
     run_case(nv, oracle, z, "rowcol", 1)
 
 
+# (272, 400): one block per lane; widths that are multiples of 1024 take the whole-wave
+# layout, also into a row-strided output view
+@pytest.mark.parametrize("shape,pad", [((272, 400), 0), ((48, 2048), 0), ((32, 3072), 64)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_dequantize_matches_oracle(nv, oracle, out_dtype):
-    x = make_input((272, 400), 11, torch.float32).numpy()
+def test_dequantize_matches_oracle(nv, oracle, out_dtype, shape, pad):
+    print(f"dequantize {shape} pad={pad} {out_dtype}", flush=True)
+    x = make_input(shape, 11, torch.float32).numpy()
     orow, _ = oracle.quantize(x, round_row=1, seed=4)
     gq = to_gpu_qtensor(nv, orow)
-    out = nv.nvfp4_dequantize(gq, out_dtype=out_dtype)
+    big = torch.full((shape[0], shape[1] + pad), 7.0, dtype=out_dtype, device=dev())
+    out = nv.nvfp4_dequantize(gq, out_dtype=out_dtype, out=big[:, :shape[1]])
     torch.cuda.synchronize()
+    if pad:
+        assert torch.all(big[:, shape[1]:] == 7.0)   # the padding columns are left alone
     ref = torch.from_numpy(oracle.dequantize(orow))
     if out_dtype == torch.bfloat16:
         ref = ref.to(torch.bfloat16)          # torch's nearest-even rounding
