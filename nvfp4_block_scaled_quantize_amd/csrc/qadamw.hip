@@ -38,6 +38,33 @@ struct QVArgs {
     int nblocks;   // workgroups
 };
 
+// Correctly rounded square roots of 16 non-negative finite values, in place.  The hardware
+// estimate v_sqrt_f32 is within one ulp for inputs of at least 2^-96; the root is then s,
+// or s - ulp when (s - ulp) s >= x, or s + ulp when (s + ulp) s < x (residuals by fma,
+// exact), which is also right for x = 0.  This is the library square root's own sequence
+// for that range, without its rescaling of tiny inputs and its special-value checks.  When
+// any lane of the wave holds a value in (0, 2^-96), the whole wave takes sqrtf instead.
+__device__ __forceinline__ void sqrt16_rn(float y[16]) {
+    // bits - 1 of a value in (0, 2^-96) is below that of 2^-96; 0 wraps to the top
+    uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mn = min(mn, __float_as_uint(y[i]) - 1u);
+    if (__builtin_amdgcn_ballot_w64(mn < 0x0F7FFFFFu) != 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] = sqrtf(y[i]);
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float x = y[i], s = __builtin_amdgcn_sqrtf(x);
+        const float sm = __uint_as_float(__float_as_uint(s) - 1u);
+        const float sp = __uint_as_float(__float_as_uint(s) + 1u);
+        float r = __builtin_fmaf(-sm, s, x) <= 0.0f ? sm : s;
+        r = __builtin_fmaf(-sp, s, x) > 0.0f ? sp : r;
+        y[i] = r;
+    }
+}
+
 __device__ __forceinline__ float tree16_row(const float y[16]) {
     float t[8], u[4], w[2];
 #pragma unroll
@@ -53,10 +80,7 @@ __device__ __forceinline__ float tree16_row(const float y[16]) {
 // transformed residual e.  The 16 lanes 16k .. 16k+15 hold the rows of one 16x16 tile.
 // All 64 lanes must call it (cross-lane shuffles).
 __device__ __forceinline__ uint32_t residual_from(float y[16], uint32_t signs, float e[16]) {
-    // sqrtf lowers to the correctly rounded square root on gfx950 (checked against IEEE
-    // sqrt on 4M log-normal and subnormal inputs); __fsqrt_rn is not, so it is avoided.
-#pragma unroll
-    for (int i = 0; i < 16; ++i) y[i] = sqrtf(y[i]);
+    sqrt16_rn(y);
     float s = tree16_row(y);
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) s = s + __shfl_xor(s, o, 64);
@@ -416,9 +440,13 @@ __global__ __launch_bounds__(QVThreads) void k_qs_pass2(QSArgs a) {
             const float4 f = pw[q];
             w[4 * q] = f.x; w[4 * q + 1] = f.y; w[4 * q + 2] = f.z; w[4 * q + 3] = f.w;
         }
+        float rt[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) rt[i] = a.bias2 * v[i];
+        sqrt16_rn(rt);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const float den = sqrtf(a.bias2 * v[i]) + a.eps;
+            const float den = rt[i] + a.eps;
             const float upd = __fdiv_rn(a.bias1 * m[i], den) + a.wd * w[i];
             w[i] = w[i] - a.lr * upd;
         }

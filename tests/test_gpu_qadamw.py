@@ -51,3 +51,17 @@ def test_qadamw_full_size(nv, oracle):
     from nvfp4_block_scaled_quantize_amd import synthetic
     v = synthetic.qadamw()["v"]       # 9216 x 3072 log-normal(-18, 3)
     check(nv, oracle, v, synthetic.RHT_SEED_QADAMW, 1)
+
+
+def test_qadamw_tiny_values(nv, oracle):
+    """Second moments below 2^-96 (normal and subnormal) take the rescaled square root; 2^-96
+    itself and everything above take the short one.  Both must round as IEEE sqrt."""
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    v = synthetic.lognormal((64, 512), 77)
+    v[3, :16] = 1e-35
+    v[5, 20] = 1e-40                                  # subnormal
+    v[7, 3] = 2.0 ** -96                              # the boundary itself (exact in f32)
+    v[9, 9] = float(np.nextafter(np.float32(2.0 ** -96), np.float32(0)))
+    v[40:56, 256:272] = 3e-33                         # a whole tile of them
+    check(nv, oracle, v, 0x5EED5, 1)
+

@@ -93,6 +93,20 @@ def test_step_from_zero_state(nv, oracle):
     check_step(nv, oracle, w, grad(R, C, 9, False), qm, mu, qv, 0x53520200, False)
 
 
+def test_step_tiny_second_moments(nv, oracle):
+    """Gradients of 1e-20 from the zero state give second moments far below 2^-96 (some
+    subnormal): the weight update's square roots take the rescaled path for those waves."""
+    R, C = 64, 256
+    z = np.zeros((R, C), dtype=np.float32)
+    qm = oracle.quantize_rows(z, rounding=oracle.SR, seed=1, scale46=True)
+    mu, qv = oracle.qadamw_v_encode(z, seed=V_SEED)
+    w = np.random.default_rng(12).standard_normal((R, C)).astype(np.float32)
+    g = grad(R, C, 13, False)
+    g[:16, :64] = 1e-20
+    g[20, 5] = 3e-23
+    check_step(nv, oracle, w, g, qm, mu, qv, 0x53520300, False)
+
+
 def test_step_full_size(nv, oracle):
     from nvfp4_block_scaled_quantize_amd import synthetic
     R, C = 9216, 3072                      # the FFN weight's state, log-normal v as for Q-AdamW
