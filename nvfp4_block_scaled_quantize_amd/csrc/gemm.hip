@@ -608,6 +608,11 @@ __device__ __forceinline__ void piped_stage(const DmaCtx& c, int s, HalfFrags& l
     decode_slot<4>(hi, p, av, bv);
     mma_slot(an, bn, acc);
     pace<5>();
+    // Slot 4's operands must be formed here, under slot 3's MFMAs: without this the compiler
+    // sinks their decode past the branch below, into the half of the stage that already
+    // carries the next stage's slot 0, and that half becomes VALU-bound.
+#pragma unroll
+    for (int x = 0; x < 4; ++x) asm volatile("" : "+v"(av[x]), "+v"(bv[x]));
     // lo is dead: stage s + 1 must be in LDS (its loads were issued two stages ago)
     const int last = s + 2 < c.nst ? s + 2 : c.nst - 1;   // last stage issued so far
     wait_meet(last - (s + 1));
