@@ -106,3 +106,16 @@ def lora(rank=64, hidden=3072, ffn_dim=9216, seed=DATA_SEEDS["lora"]):
     return {"L1": bf16(normal((rank, hidden), seed, hidden ** -0.5)),
             "L2": bf16(normal((ffn_dim, rank), seed + 1000, 0.02)),
             "beta": 0.5}
+
+
+def random_nvfp4_parts(n, k, seed, device="cpu", max_scale_code=0x7E):
+    """Codes and scale bytes of an n x k NVFP4 copy drawn uniformly with a seeded torch
+    generator on `device`: every byte is two valid E2M1 codes, and E4M3 scale codes run up to
+    max_scale_code (0x7F is the format's NaN).  An operand with no quantization pass behind
+    it, for shapes too large to quantize on the host."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=device).random_(0, 256, generator=g)
+    scales = torch.empty((n, k // 16), dtype=torch.uint8, device=device).random_(
+        0, max_scale_code + 1, generator=g)
+    return codes, scales
+

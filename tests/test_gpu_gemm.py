@@ -100,3 +100,28 @@ def test_gemm_full_size_sampled(nv, oracle, name, M, N, K):
     print(f"gemm full-size {name} {M}x{N}x{K}", flush=True)
     qa, qb = quantized_pair(oracle, M, N, K, 1000 + M + N)
     sampled_check(nv, oracle, qa, qb, M, N, 5)
+
+
+def test_gemm_operand_over_2gib(nv, oracle):
+    """A holds 2 GiB + 64 KiB of codes, past the direct path's 32-bit buffer offsets, so the
+    generic path runs.  Rows on both sides of the 2^31-byte offset, the first and last rows
+    and 32 random rows are checked against the oracle's binary64 product."""
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    M, N, K = (1 << 19) + 16, 16, 8192            # A codes: M K / 2 = 2^31 + 65536 bytes
+    print(f"gemm with a {M * K // 2} byte operand, {M}x{N}x{K}", flush=True)
+    ca, sa = synthetic.random_nvfp4_parts(M, K, 21, device=dev())
+    cb, sb = synthetic.random_nvfp4_parts(N, K, 22, device=dev())
+    c = nv.nvfp4_gemm(nv.QTensor(ca, sa, torch.ones((1,), device=dev())),
+                      nv.QTensor(cb, sb, torch.ones((1,), device=dev())))
+    torch.cuda.synchronize()
+    edge = (1 << 31) // (K // 2)                  # first row that starts past 2^31 bytes
+    rng = np.random.default_rng(23)
+    rows = sorted(set([0, edge - 1, edge, edge + 1, M - 1] + [int(r) for r in rng.integers(0, M, 32)]))
+    idx = torch.tensor(rows, device=dev())
+    qa = oracle.QTensor(ca[idx].cpu().numpy(), sa[idx].cpu().numpy(), 1.0)
+    qb = oracle.QTensor(cb.cpu().numpy(), sb.cpu().numpy(), 1.0)
+    ref, absdot = oracle.gemm_f64(qa, qb)
+    fro, nw = gemm_errors(c[idx].cpu().numpy(), ref, absdot)
+    print(f"  rows {len(rows)} frobenius {fro:.3e} normwise {nw:.3e}")
+    assert fro <= GEMM_TOL and nw <= GEMM_TOL
+
