@@ -119,3 +119,11 @@ def random_nvfp4_parts(n, k, seed, device="cpu", max_scale_code=0x7E):
         0, max_scale_code + 1, generator=g)
     return codes, scales
 
+
+def uniform_bf16(shape, seed, device="cpu"):
+    """Uniform [-1, 1) values rounded to bfloat16, drawn with a seeded torch generator on
+    `device` (for inputs too large to build on the host)."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    x = torch.empty(shape, dtype=torch.float32, device=device).uniform_(-1.0, 1.0, generator=g)
+    return x.to(torch.bfloat16)
+

@@ -161,6 +161,36 @@ def test_dequantize_matches_oracle(nv, oracle, out_dtype, shape, pad):
                        ref.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32))
 
 
+# ------------------------------------------------------------------ beyond 2 GiB
+def test_quantize_input_over_2gib(nv, oracle):
+    """A bf16 input of 2 GiB + 512 KiB (rowwise and columnwise copies).  A planted 7.0 in
+    row 0 fixes the tensor maximum; the oracle quantizes row group 0 together with each
+    checked group (both sides of the 2^31-byte offset, the last group, random groups), so
+    its tensor scale is the device's, and both copies of the checked group must match."""
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    M, K = (1 << 16) + 16, 16384                  # input bytes: 2 M K = 2^31 + 524288
+    print(f"quantize a {2 * M * K} byte bf16 input, {M}x{K}", flush=True)
+    x = synthetic.uniform_bf16((M, K), 31, device=dev())
+    x[0, 5] = 7.0
+    p = nv.quant_params(rowwise=True, colwise=True)
+    r, c = nv.nvfp4_quantize(x, p)
+    torch.cuda.synchronize()
+    edge = (1 << 31) // (2 * K)                   # first row that starts past 2^31 bytes
+    rng = np.random.default_rng(32)
+    groups = sorted(set([edge // 16 - 1, edge // 16, M // 16 - 1] +
+                        [int(gi) for gi in rng.integers(1, M // 16, 3)]))
+    head = x[:16].float().cpu().numpy()
+    for gi in groups:
+        rows = slice(16 * gi, 16 * gi + 16)
+        orow, ocol = oracle.quantize(np.concatenate([head, x[rows].float().cpu().numpy()]),
+                                     colwise=True)
+        assert r.gscale.item() == np.float32(orow.sg) and c.gscale.item() == np.float32(ocol.sg)
+        assert np.array_equal(r.codes[rows].cpu().numpy(), orow.codes[16:])
+        assert np.array_equal(r.scales[rows].cpu().numpy(), orow.scales[16:])
+        assert np.array_equal(c.codes[:, 8 * gi:8 * gi + 8].cpu().numpy(), ocol.codes[:, 8:16])
+        assert np.array_equal(c.scales[:, gi:gi + 1].cpu().numpy(), ocol.scales[:, 1:2])
+
+
 # ------------------------------------------------------------------ full-size tensors
 def test_full_size_activation_rowcol(nv, oracle):
     from nvfp4_block_scaled_quantize_amd import synthetic
