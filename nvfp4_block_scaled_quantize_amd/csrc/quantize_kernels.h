@@ -737,8 +737,11 @@ __device__ __forceinline__ void lora_step(const QArgs& a, const uint4 (&xv)[4], 
     __syncthreads();
 }
 
+// Three workgroups per CU (at most 168 VGPRs): the third wave per SIMD hides more of each
+// step's load latency than the few scratch round trips of the ping-pong registers cost
+// (X 8192x3072 rank 64: 55.8 -> 53.6 us; dY 8192x9216: 172 -> 163 us, outputs identical).
 template <int H, int NQ>
-__global__ __launch_bounds__(kThreads) void k_amax_lora(QArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void k_amax_lora(QArgs a) {
     constexpr bool RHT_ROW = H & 1, RHT_COL = (H >> 1) & 1;
     // [2 buffers][NQ*16 rows][16 chunks], chunk ^ (row & 15): the next step's slice is
     // written into one buffer while the MFMAs read the other
