@@ -79,14 +79,6 @@ __device__ __forceinline__ uint32_t e4m3_encode(float s) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(s, 448.0f), 0.0f, 0, false) & 0xFFu;
 }
 
-// The codes of two scales from one conversion.
-__device__ __forceinline__ void e4m3_encode2(float s0, float s1, uint32_t& c0, uint32_t& c1) {
-    const uint32_t w =
-        (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(s0, 448.0f), fminf(s1, 448.0f), 0, false);
-    c0 = w & 0xFFu;
-    c1 = (w >> 8) & 0xFFu;
-}
-
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
     uint32_t e = (c >> 3) & 15u, m = c & 7u;
     if (e == 0) return (float)m * 0.001953125f;
@@ -123,11 +115,6 @@ template <int SEL>
 __device__ __forceinline__ float2v fp4x2_to_f32(uint32_t w) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
 }
-template <int SEL>
-__device__ __forceinline__ half2v fp4x2_to_f16(uint32_t w) {
-    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
-}
-
 // ---------------------------------------------------------------- misc
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
