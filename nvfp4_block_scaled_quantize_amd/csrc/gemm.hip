@@ -72,11 +72,15 @@ struct GArgs {
     const float* d;       // C = alpha * product + beta * D (the EpiAxpby kernels)
     int64_t ldd;
     float alpha, beta;
+    float* part;          // EpiPart: [kparts][triangle tiles][256][256] raw accumulators
+    int kparts;
 };
 
 // Epilogue variants: plain product; plus the LoRA-SVD low-rank term; alpha * product +
 // beta * D (the Newton-Schulz updates).
-enum { EpiPlain = 0, EpiLora = 1, EpiAxpby = 2 };
+// EpiPart: the raw accumulators of one K-part of an upper-triangle tile of A A^T go to a
+// partial buffer (k_syrk_reduce sums the parts and mirrors the result).
+enum { EpiPlain = 0, EpiLora = 1, EpiAxpby = 2, EpiPart = 3 };
 
 // Packed tile layout: row r holds 64 bytes as four 16-byte chunks; chunk q sits at slot
 // q ^ (r/4 mod 4), which keeps both the staging stores (four lanes per row) and the
@@ -209,6 +213,34 @@ __device__ __forceinline__ void store_tile(const GArgs& g, const float16v (&acc)
     }
 }
 
+// The raw accumulators of the tile into its 256 x 256 slot of the partial buffer (row-major),
+// in the row order of store_tile.
+__device__ __forceinline__ void store_part(float* slot, const float16v (&acc)[4][4], int wm, int wn,
+                                           int h, int li) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float* rowp = slot + (wm * 128 + 4 * h + i * 32 + 8 * (r >> 2) + (r & 3)) * GBN +
+                          wn * 128 + li;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rowp[j * 32] = acc[i][j][r];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Upper-triangle tile t (row-major over tm <= tn) of a T x T tile grid.
+__device__ __forceinline__ void tri_tile(int t, int T, int& tm, int& tn) {
+    int r = 0, rem = t;
+    while (rem >= T - r) {
+        rem -= T - r;
+        ++r;
+    }
+    tm = r;
+    tn = r + rem;
+}
+
 // LoRA-SVD up-projection in the epilogue (Full-Stack FP4 sec. 3.2 eq. (1), Appendix 9: the
 // low-rank branch shares the GEMM's output tile).  After the main loop the stage buffers are
 // free: the workgroup copies its 256 rows of T and of L, 64 rank entries at a time, into
@@ -308,6 +340,8 @@ __device__ __forceinline__ void finish_tile(const GArgs& g, uint8_t* lds, float1
         store_tile(g, acc, m0, n0, wm, wn, h, li, 1.0f);
     } else if constexpr (EPI == EpiAxpby) {
         store_tile_axpby(g, acc, m0, n0, wm, wn, h, li);
+    } else if constexpr (EPI == EpiPart) {
+        store_part(g.part + ((int64_t)blockIdx.x << 16), acc, wm, wn, h, li);
     } else {
         store_tile(g, acc, m0, n0, wm, wn, h, li, *g.asg * *g.bsg);
     }
@@ -577,6 +611,7 @@ struct DmaCtx {
     const uint8_t* lds;
     int64_t m0, n0;
     int t, wid, wm, wn, h, li, nst;
+    int s0;   // first K stage of this workgroup (EpiPart: its K-part)
     uint32_t kbytes, kblocks;
 };
 
@@ -617,8 +652,8 @@ __device__ __forceinline__ void piped_stage(const DmaCtx& c, int s, HalfFrags& l
     const int last = s + 2 < c.nst ? s + 2 : c.nst - 1;   // last stage issued so far
     wait_meet(last - (s + 1));
     if (s + 3 < c.nst)
-        dma_stage(c.g, c.rs, c.lds0 + (s % kDmaStages) * kStageBytes, c.m0, c.n0, s + 3, c.t, c.wid,
-                  c.kbytes, c.kblocks);
+        dma_stage(c.g, c.rs, c.lds0 + (s % kDmaStages) * kStageBytes, c.m0, c.n0, c.s0 + s + 3, c.t,
+                  c.wid, c.kbytes, c.kblocks);
     const uint8_t* nxt = c.lds + ((s + 1) % kDmaStages) * kStageBytes;
     uint32_t nsa[4], nsb[4];
     read_half(nxt, 0, c.wm, c.wn, c.h, c.li, lo);
@@ -654,7 +689,19 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
     c.wm = c.wid >> 1;
     c.wn = c.wid & 1;
     int tm, tn;
-    tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+    const int nst_all = (int)((g.K + GBK - 1) / GBK);
+    c.s0 = 0;
+    c.nst = nst_all;
+    if constexpr (EPI == EpiPart) {
+        // workgroup = K-part kp of upper-triangle tile t: blockIdx = kp * ntri + t
+        const int ntri = g.tiles_m * (g.tiles_m + 1) / 2;
+        const int kp = blockIdx.x / ntri;
+        tri_tile(blockIdx.x - kp * ntri, g.tiles_m, tm, tn);
+        c.s0 = (int)((int64_t)kp * nst_all / g.kparts);
+        c.nst = (int)((int64_t)(kp + 1) * nst_all / g.kparts) - c.s0;
+    } else {
+        tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+    }
     c.m0 = (int64_t)tm * GBM;
     c.n0 = (int64_t)tn * GBN;
     c.h = lane >> 5;
@@ -667,13 +714,13 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
     c.rs.bs = make_rsrc(g.bs, (uint32_t)(g.N * c.kblocks));
     c.lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
     c.lds = lds;
-    c.nst = (int)((g.K + GBK - 1) / GBK);
 
     float16v acc[4][4];
     zero_acc(acc);
     const int pre = c.nst < kDmaStages ? c.nst : kDmaStages;
     for (int j = 0; j < pre; ++j)
-        dma_stage(g, c.rs, c.lds0 + j * kStageBytes, c.m0, c.n0, j, c.t, c.wid, c.kbytes, c.kblocks);
+        dma_stage(g, c.rs, c.lds0 + j * kStageBytes, c.m0, c.n0, c.s0 + j, c.t, c.wid, c.kbytes,
+                  c.kblocks);
     wait_meet(pre - 1);
     HalfFrags lo, hi;
     uint32_t sa[4], sb[4];
@@ -686,6 +733,91 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
     decode_slot<0>(lo, p, av, bv);
     for (int s = 0; s < c.nst; ++s) piped_stage(c, s, lo, hi, sa, sb, p, av, bv, acc);
     finish_tile<EPI>(g, lds, acc, c.m0, c.n0, c.wm, c.wn, c.h, c.li);
+}
+
+// C = s_gA s_gB (P_0 + P_1 + ...) over the K-parts, in part order, for the upper-triangle
+// tiles of A A^T, and the same values mirrored into the tiles below the diagonal.  A
+// workgroup takes one 64 x 64 sub-block of one triangle tile: thread t sums four consecutive
+// columns of rows t/16 + 16q; an off-diagonal sub-block is transposed through LDS so the
+// mirrored rows are written whole.
+__global__ __launch_bounds__(256) void k_syrk_reduce(const float* part, int ntri, int kparts, int T,
+                                                     const float* asg, const float* bsg, float* c,
+                                                     int64_t ldc) {
+    __shared__ float tr[64][65];
+    const int t = threadIdx.x, tile = blockIdx.x >> 4, sb = blockIdx.x & 15;
+    int tm, tn;
+    tri_tile(tile, T, tm, tn);
+    const int br = (sb >> 2) * 64, bc = (sb & 3) * 64, cl = (t & 15) * 4;
+    const float scale = *asg * *bsg;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int rl = (t >> 4) + 16 * q;
+        const int64_t off = (int64_t)(br + rl) * GBN + bc + cl;
+        float4 sum = *(const float4*)(part + ((int64_t)tile << 16) + off);
+        for (int kp = 1; kp < kparts; ++kp) {
+            const float4 p = *(const float4*)(part + ((int64_t)(kp * ntri + tile) << 16) + off);
+            sum.x = sum.x + p.x; sum.y = sum.y + p.y; sum.z = sum.z + p.z; sum.w = sum.w + p.w;
+        }
+        sum.x = sum.x * scale; sum.y = sum.y * scale; sum.z = sum.z * scale; sum.w = sum.w * scale;
+        *(float4*)(c + ((int64_t)tm * GBM + br + rl) * ldc + (int64_t)tn * GBN + bc + cl) = sum;
+        tr[rl][cl] = sum.x; tr[rl][cl + 1] = sum.y; tr[rl][cl + 2] = sum.z; tr[rl][cl + 3] = sum.w;
+    }
+    if (tm == tn) return;   // uniform: the diagonal tiles hold both halves already
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int xr = (t >> 4) + 16 * q;   // row of the mirrored sub-block = column here
+        const float4 m = make_float4(tr[cl][xr], tr[cl + 1][xr], tr[cl + 2][xr], tr[cl + 3][xr]);
+        *(float4*)(c + ((int64_t)tn * GBN + bc + xr) * ldc + (int64_t)tm * GBM + br + cl) = m;
+    }
+}
+
+// K-parts for A A^T with m a multiple of 256: as many as fill one round of the 256 CUs with
+// the triangle's tiles, each K-part at least four stages; 1 means no gain over the plain GEMM.
+static int syrk_kparts(int64_t m, int64_t k) {
+    if (m <= 0 || m % GBM || k <= 0 || k % 64) return 1;
+    const int64_t T = m / GBM, ntri = T * (T + 1) / 2, nst = (k + GBK - 1) / GBK;
+    int64_t kp = 256 / ntri;
+    if (kp > nst / 4) kp = nst / 4;
+    return kp > 1 ? (int)kp : 1;
+}
+
+size_t syrk_part_bytes(int64_t m, int64_t k) {
+    const int kp = syrk_kparts(m, k);
+    if (kp <= 1) return 0;
+    const int64_t T = m / GBM;
+    return (size_t)kp * (size_t)(T * (T + 1) / 2) * GBM * GBN * sizeof(float);
+}
+
+// C = s_gA^2 A A^T (m x m, FP32) for one NVFP4 copy a of an m x k matrix: the upper-triangle
+// tiles with K split into parts on the direct path, then k_syrk_reduce.  Returns
+// NVFP4_ERR_MODE when the shape or alignment does not allow it (the caller then takes the
+// plain GEMM).  part: syrk_part_bytes(m, k) bytes, 16-byte aligned.
+int syrk_splitk(const nvfp4_qtensor* a, int64_t m, int64_t k, float* c, int64_t ldc, float* part,
+                size_t part_bytes, hipStream_t st) {
+    const int kparts = syrk_kparts(m, k);
+    if (kparts <= 1 || !part || part_bytes < syrk_part_bytes(m, k)) return NVFP4_ERR_MODE;
+    if (((uintptr_t)a->codes & 15) || ((uintptr_t)a->scales & 3) || ((uintptr_t)c & 15) ||
+        ((uintptr_t)part & 15) || ldc % 4 || ldc < m || m * (k / 2) >= (int64_t)kOutOfRange)
+        return NVFP4_ERR_MODE;
+    GArgs g;
+    g.ac = a->codes; g.as = a->scales; g.asg = a->gscale;
+    g.bc = a->codes; g.bs = a->scales; g.bsg = a->gscale;
+    g.M = m; g.N = m; g.K = k; g.c = c; g.ldc = ldc;
+    g.lt = nullptr; g.lb = nullptr; g.lr = 0;
+    g.d = nullptr; g.ldd = 0; g.alpha = 1.0f; g.beta = 0.0f;
+    g.part = part;
+    g.kparts = kparts;
+    const int T = (int)(m / GBM), ntri = T * (T + 1) / 2;
+    g.tiles_m = T;
+    g.tiles_n = T;
+    if (hipFuncSetAttribute((const void*)k_gemm_dma<EpiPart>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kGemmDmaLds) != hipSuccess)
+        return NVFP4_ERR_HIP;
+    k_gemm_dma<EpiPart><<<(unsigned)(kparts * ntri), GThreads, kGemmDmaLds, st>>>(g);
+    k_syrk_reduce<<<(unsigned)(ntri * 16), 256, 0, st>>>(part, ntri, kparts, T, a->gscale, a->gscale,
+                                                        c, ldc);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
 }  // namespace nvfp4
@@ -720,6 +852,8 @@ static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M
     g.ldd = d ? ldd : 0;
     g.alpha = alpha;
     g.beta = beta;
+    g.part = nullptr;
+    g.kparts = 1;
     const int epi = d ? EpiAxpby : (lr > 0 ? EpiLora : EpiPlain);
     const int64_t tiles_m = (M + GBM - 1) / GBM, tiles_n = (N + GBN - 1) / GBN;
     g.tiles_m = (int)tiles_m;

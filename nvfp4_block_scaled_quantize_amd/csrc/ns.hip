@@ -12,7 +12,16 @@
 // Every quantization is nearest-even with 4/6 scaling (the pages'), 1x16 / 16x1 blocks, and
 // one random Hadamard H per iteration (the seed).  The coefficients are the caller's: the
 // pages take shape-specialised ones from Root and do not print them.
+#include <hip/hip_runtime.h>
 #include "nvfp4.h"
+
+namespace nvfp4 {
+// gemm.hip: A A^T on the triangle tiles with K split into parts, then a reduction that
+// mirrors (NVFP4_ERR_MODE when the shape does not allow it)
+size_t syrk_part_bytes(int64_t m, int64_t k);
+int syrk_splitk(const nvfp4_qtensor* a, int64_t m, int64_t k, float* c, int64_t ldc, float* part,
+                size_t part_bytes, hipStream_t st);
+}  // namespace nvfp4
 
 namespace {
 
@@ -42,6 +51,8 @@ struct NsBuffers {
     float* b;
     void* qws;
     size_t qws_bytes;
+    float* part;          // partial products of A = qX qX^T (none when it is not split)
+    size_t part_bytes;
     size_t total;
 };
 
@@ -59,6 +70,8 @@ NsBuffers ns_layout(uint8_t* ws, int64_t m, int64_t n, const nvfp4_quant_params*
     const size_t w2 = nvfp4_quantize_workspace_bytes(m, m, p);
     L.qws_bytes = w1 > w2 ? w1 : w2;
     L.qws = c.take(L.qws_bytes);
+    L.part_bytes = nvfp4::syrk_part_bytes(m, n);
+    L.part = L.part_bytes ? (float*)c.take(L.part_bytes) : nullptr;
     L.total = c.off;
     return L;
 }
@@ -104,8 +117,10 @@ extern "C" int nvfp4_ns_step(float* x, int64_t m, int64_t n, float a, float b, f
     if ((rc = nvfp4_quantize(x, NVFP4_F32, m, n, n, &pxa, &L.qx, &L.qxc, L.qws, L.qws_bytes,
                              stream)) != NVFP4_OK)
         return rc;
-    // A = qX qX^T
-    if ((rc = nvfp4_gemm(&L.qx, &L.qx, m, m, n, L.a, m, stream)) != NVFP4_OK) return rc;
+    // A = qX qX^T: the triangle tiles split along K when that fills the device, else the GEMM
+    rc = nvfp4::syrk_splitk(&L.qx, m, n, L.a, m, L.part, L.part_bytes, (hipStream_t)stream);
+    if (rc == NVFP4_ERR_MODE) rc = nvfp4_gemm(&L.qx, &L.qx, m, m, n, L.a, m, stream);
+    if (rc != NVFP4_OK) return rc;
     // qA, qA'
     if ((rc = nvfp4_quantize(L.a, NVFP4_F32, m, m, m, &pxa, &L.qa, &L.qac, L.qws, L.qws_bytes,
                              stream)) != NVFP4_OK)

@@ -62,7 +62,9 @@ def exact_step(x, a, b, c):
     return a * x + b * (A @ x) + c * (A @ (A @ x))
 
 
-@pytest.mark.parametrize("m,n", [(32, 64), (64, 192), (96, 288), (288, 544)])
+# (256, 1024) and (512, 2048): A = qX qX^T is formed on the triangle tiles with K split into
+# 2 and 4 parts, then reduced and mirrored; the other shapes take the plain GEMM
+@pytest.mark.parametrize("m,n", [(32, 64), (64, 192), (96, 288), (288, 544), (256, 1024), (512, 2048)])
 @pytest.mark.parametrize("abc", [(1.5, -0.5, 0.0), (2.0, -1.5, 0.5)])
 def test_ns_step_matches_oracle(nv, oracle, m, n, abc):
     print(f"ns_step {m}x{n} coefficients {abc}", flush=True)
