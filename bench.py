@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="write profiles/ffn3b_step_kernel_stats.txt from a rocprofv3 "
                          "--kernel-trace --stats folder of one bench run")
+    ap.add_argument("--mfma-summary", metavar="DIR",
+                    help="write profiles/gemm_mfma_busy.txt from a rocprofv3 --pmc GRBM_GUI_ACTIVE "
+                         "SQ_VALU_MFMA_BUSY_CYCLES --kernel-trace folder of one bench step")
     ap.add_argument("--counter-summary", nargs=4, metavar="DIR",
                     help="write profiles/hbm_counters.txt from rocprofv3 --pmc folders: "
                          "FETCH_SIZE and WRITE_SIZE of one bench step, then of --copy-calibration")
@@ -225,8 +228,53 @@ def counter_summary(dirs):
     print("\n".join(lines))
 
 
+def mfma_summary(d):
+    """Write profiles/gemm_mfma_busy.txt from a rocprofv3 --pmc GRBM_GUI_ACTIVE
+    SQ_VALU_MFMA_BUSY_CYCLES --kernel-trace folder of `bench.py --steps 1 --warmup 0
+    --no-cpu-baseline`: per GEMM call of the step, the duration under counter collection, the
+    effective clock (GRBM_GUI_ACTIVE over the eight XCDs / duration) and the fraction of SIMD
+    cycles the matrix cores were busy (SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles))."""
+    import csv
+    import glob as _glob
+    agg, name = {}, {}
+    for r in csv.DictReader(open(_glob.glob(os.path.join(d, "*counter_collection.csv"))[0])):
+        k = int(r["Dispatch_Id"])
+        agg.setdefault(k, {}).setdefault(r["Counter_Name"], 0.0)
+        agg[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        name[k] = r["Kernel_Name"]
+    dur = {}
+    for r in csv.DictReader(open(_glob.glob(os.path.join(d, "*kernel_trace.csv"))[0])):
+        dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    ids = [k for k in sorted(agg) if "nvfp4::" in name[k]]
+    lines = ["# Matrix-core busy fraction and effective clock of the step's GEMMs (rocprofv3 --pmc)",
+             "# commands (from the repository root, cd /tmp && TMPDIR=/tmp first):",
+             "#   rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES --kernel-trace --output-format csv \\",
+             "#       -d <m> -o bench -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
+             "#   python3 bench.py --mfma-summary <m>",
+             "# clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs",
+             "# x GRBM_GUI_ACTIVE / 8); durations are longer than uncounted ones (collection overhead)",
+             f"# {'call':16s} {'kernel':28s} {'us':>8s} {'clock_GHz':>10s} {'mfma_busy':>10s}"]
+    kinds = dict(STEP_ORDER)
+    for key, idx in split_step([name[k] for k in ids])[:len(STEP_ORDER)]:
+        if kinds[key] != "gemm":
+            continue
+        for i in idx:
+            k = ids[i]
+            cyc = agg[k].get("GRBM_GUI_ACTIVE", 0.0) / 8
+            t = dur.get(k, float("nan"))
+            busy = agg[k].get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (1024 * cyc) if cyc else float("nan")
+            lines.append(f"{key:18s} {name[k].split('(')[0].replace('void nvfp4::', ''):28s} {t * 1e6:8.1f} "
+                         f"{cyc / t / 1e9:10.2f} {busy:10.3f}")
+    out = os.path.join(ROOT, "profiles", "gemm_mfma_busy.txt")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
+        return
     if args.counter_summary:
         counter_summary(args.counter_summary)
         return
