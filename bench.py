@@ -534,7 +534,7 @@ def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream, ite
     (X quantize with the L1 down-projection fused, FFN-up GEMM with the L2 up-projection
     fused, and for dX the dY quantize with L2^T and the dgrad GEMM with L1^T); the
     QKV-projection GEMM of the 3B model; a plain device copy for the device's achievable HBM
-    bandwidth."""
+    bandwidth; and, as context only, the platform's dense f16 GEMM on the FFN-up shape."""
     qkv = synthetic.qkv()
     Xq, Wqkv = qkv["X"].to(dev), qkv["W"].to(dev)
     p46x = nv.quant_params(rowwise=True, colwise=True, rht_col=True, seed=SEED_WGRAD, scale46=True)
@@ -571,6 +571,10 @@ def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream, ite
     wsns = torch.empty(nv.load_library().nvfp4_ns_step_workspace_bytes(HIDDEN, FFN), dtype=torch.uint8,
                        device=dev)
     Yl = torch.empty((TOKENS, FFN), dtype=torch.float32, device=dev)
+    g16 = torch.Generator(device=dev).manual_seed(SEED_QADAMW + 9)
+    a16 = torch.randn((TOKENS, HIDDEN), generator=g16, device=dev, dtype=torch.float16)
+    b16 = torch.randn((HIDDEN, FFN), generator=g16, device=dev, dtype=torch.float16)   # K-major, contiguous
+    c16 = torch.empty((TOKENS, FFN), dtype=torch.float16, device=dev)
     dXl = torch.empty((TOKENS, HIDDEN), dtype=torch.float32, device=dev)
     cases = {
         "quant_X_row+colRHT_4/6": (lambda: nv.nvfp4_quantize(X, p46x, qx[0], qx[1], qx[2]),
@@ -604,6 +608,14 @@ def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream, ite
         "gemm_qkv_8192x6144x3072": (lambda: nv.nvfp4_gemm(qa, qb, out=C),
                                     qbytes(M, K) + qbytes(N, K) + 4 * M * N, 2 * M * N * K),
         "hbm_copy_256MiB": (lambda: dst.copy_(src), 2 * (256 << 20), 0),
+        # the FFN-up GEMM timed like the next line (back to back), for a like-for-like view
+        "gemm_ffn_up_back_to_back": (lambda: nv.nvfp4_gemm(qx[0], qw[0], out=Yl), 0,
+                                     2 * TOKENS * FFN * HIDDEN),
+        # context, not part of the path: the platform library's dense f16 GEMM (torch.matmul,
+        # hipBLASLt) on the FFN-up shape with contiguous operands, the practical ceiling of
+        # the f16 datapath on this part
+        "context_f16_matmul_8192x9216x3072": (lambda: torch.matmul(a16, b16, out=c16), 0,
+                                              2 * TOKENS * FFN * HIDDEN),
     }
     res = {}
     for name, (fn, nbytes, flops) in cases.items():
