@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--mfma-summary", metavar="DIR",
                     help="write profiles/gemm_mfma_busy.txt from a rocprofv3 --pmc GRBM_GUI_ACTIVE "
                          "SQ_VALU_MFMA_BUSY_CYCLES --kernel-trace folder of one bench step")
+    ap.add_argument("--valu-summary", metavar="DIR",
+                    help="write profiles/valu_busy.txt from a rocprofv3 --pmc GRBM_GUI_ACTIVE "
+                         "SQ_INSTS_VALU SQ_ACTIVE_INST_VALU --kernel-trace folder of one bench step")
     ap.add_argument("--counter-summary", nargs=4, metavar="DIR",
                     help="write profiles/hbm_counters.txt from rocprofv3 --pmc folders: "
                          "FETCH_SIZE and WRITE_SIZE of one bench step, then of --copy-calibration")
@@ -270,8 +273,69 @@ def mfma_summary(d):
     print("\n".join(lines))
 
 
+# input elements of each non-GEMM call of the step
+CALL_ELEMS = {"quant_X_row+colRHT": TOKENS * HIDDEN, "quant_Wup_2d": FFN * HIDDEN,
+              "quant_H_row": TOKENS * FFN, "quant_Wdown_2d": HIDDEN * FFN,
+              "quant_dY_rowSR+colRHTSR": TOKENS * FFN, "qadamw_encode": FFN * HIDDEN,
+              "qadamw_decode": FFN * HIDDEN, "qadamw_step_Wup": FFN * HIDDEN,
+              "dequant_Wup": FFN * HIDDEN}
+
+
+def valu_summary(d):
+    """Write profiles/valu_busy.txt from a rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_INSTS_VALU
+    SQ_ACTIVE_INST_VALU --kernel-trace folder of `bench.py --steps 1 --warmup 0
+    --no-cpu-baseline`.  Per kernel of each non-GEMM call of the step:
+      valu/elem   vector instructions per input element, SQ_INSTS_VALU x 64 lanes / elements;
+      issue_us    their issue time at 2 cycles per wave64 instruction on each of the 1024
+                  SIMDs at the 2.4 GHz peak clock (the rate of fp32 adds and integer adds with
+                  two or more waves per SIMD on gfx950; 64-bit integer products take about 4
+                  cycles, square roots and reciprocals about 8, and one wave alone issues at
+                  most every 4-5 cycles);
+      issue/us    the share of the kernel's time those issue cycles fill."""
+    import csv
+    import glob as _glob
+    agg, name = {}, {}
+    for r in csv.DictReader(open(_glob.glob(os.path.join(d, "*counter_collection.csv"))[0])):
+        k = int(r["Dispatch_Id"])
+        agg.setdefault(k, {}).setdefault(r["Counter_Name"], 0.0)
+        agg[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        name[k] = r["Kernel_Name"]
+    dur = {}
+    for r in csv.DictReader(open(_glob.glob(os.path.join(d, "*kernel_trace.csv"))[0])):
+        dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    ids = [k for k in sorted(agg) if "nvfp4::" in name[k]]
+    clk, cyc = 2.4e9, 2
+    lines = ["# Vector-ALU work of the step's quantize, optimizer-state and decode kernels (rocprofv3 --pmc)",
+             "# commands (from the repository root, cd /tmp && TMPDIR=/tmp first):",
+             "#   rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_ACTIVE_INST_VALU --kernel-trace \\",
+             "#       --output-format csv -d <v> -o bench -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
+             "#   python3 bench.py --valu-summary <v>",
+             "# valu/elem = SQ_INSTS_VALU x 64 / input elements; issue_us = SQ_INSTS_VALU x 2 cycles / 1024 SIMDs",
+             "# / 2.4 GHz (fp32-add rate; 64-bit integer products ~4 cycles, sqrt/rcp ~8); issue/us = issue_us / us.",
+             "# Durations are under counter collection, somewhat longer than uncounted ones.",
+             f"# {'call':24s} {'kernel':24s} {'us':>7s} {'valu/elem':>10s} {'issue_us':>9s} {'issue/us':>9s}"]
+    kinds = dict(STEP_ORDER)
+    for key, idx in split_step([name[k] for k in ids])[:len(STEP_ORDER)]:
+        if kinds[key] == "gemm":
+            continue
+        for i in idx:
+            k = ids[i]
+            t = dur.get(k, float("nan"))
+            insts = agg[k].get("SQ_INSTS_VALU", 0.0)
+            issue = insts * cyc / 1024 / clk
+            kern = name[k].split("(")[0].replace("void ", "").replace("nvfp4::", "")
+            lines.append(f"{key:26s} {kern:24s} {t * 1e6:7.1f} {insts * 64 / CALL_ELEMS[key]:10.1f} "
+                         f"{issue * 1e6:9.1f} {issue / t:9.2f}")
+    out = os.path.join(ROOT, "profiles", "valu_busy.txt")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.valu_summary:
+        valu_summary(args.valu_summary)
+        return
     if args.mfma_summary:
         mfma_summary(args.mfma_summary)
         return
