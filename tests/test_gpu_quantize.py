@@ -61,8 +61,8 @@ MODES = {
 SHAPES = [(16, 16), (48, 80), (128, 256), (272, 400), (528, 144)]
 
 
-def run_case(nv, oracle, x, mode, seed):
-    kw = MODES[mode]
+def run_case(nv, oracle, x, mode, seed, kw=None):
+    kw = MODES[mode] if kw is None else kw
     p = nv.quant_params(seed=seed, **kw)
     print(f"quantize case {tuple(x.shape)} {x.dtype} {mode} seed={seed:#x}", flush=True)
     gr, gc = nv.nvfp4_quantize(x.to(dev()), p)
@@ -229,3 +229,35 @@ def test_full_size_wgrad_operands(nv, oracle):
     t = synthetic.wgrad()
     run_case(nv, oracle, t["dY"], "wgrad_dy", synthetic.RHT_SEED_WGRAD)
     run_case(nv, oracle, t["X"], "wgrad_x", synthetic.RHT_SEED_WGRAD)
+
+
+# The five quantize calls of the benchmarked 3B FFN step, with its tensors, options and seeds
+# (8192 tokens, hidden 3072, FFN 9216), compared whole.
+BENCH_QUANT = {
+    "X_row+colRHT": ("ffn", "X", dict(rowwise=True, colwise=True, rht_col=True), True),
+    "Wup_2d": ("ffn", "W_up", dict(rowwise=True, colwise=True, block2d=True), False),
+    "H_row": ("ffn", "H", dict(rowwise=True), False),
+    "Wdown_2d": ("ffn", "W_down", dict(rowwise=True, block2d=True), False),
+    "dY_rowSR+colRHTSR": ("wgrad", "dY", dict(rowwise=True, colwise=True, round_row=1, round_col=1,
+                                              rht_col=True), True),
+}
+
+
+@pytest.mark.parametrize("call", list(BENCH_QUANT))
+def test_full_size_step_calls(nv, oracle, call):
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    src, name, kw, seeded = BENCH_QUANT[call]
+    x = getattr(synthetic, src)()[name]
+    run_case(nv, oracle, x, call, synthetic.RHT_SEED_WGRAD if seeded else 0, kw=kw)
+
+
+def test_full_size_dequantize_wup(nv, oracle):
+    """The step's decode: W_up's rowwise 16x16 copy (9216 x 3072) to FP32, every element."""
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    w = synthetic.ffn()["W_up"]
+    print("dequantize full-size W_up 9216x3072", flush=True)
+    orow, _ = oracle.quantize(w.float().numpy(), rowwise=True, colwise=True, block2d=True)
+    out = nv.nvfp4_dequantize(to_gpu_qtensor(nv, orow))
+    torch.cuda.synchronize()
+    ref = torch.from_numpy(oracle.dequantize(orow))
+    assert torch.equal(out.cpu().view(torch.int32), ref.view(torch.int32))
