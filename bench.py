@@ -78,8 +78,9 @@ FAMILY = {"gemm": "gemm", "quant": "quant", "qadamw_encode": "qadamw", "qadamw_d
           "qadamw_step": "qadamw", "dequant": "quant"}
 # kernels each call of the step launches, in order (name prefixes; '?' marks optional)
 CALL_KERNELS = {"quant": ["?k_amax", "k_encode|k_quant"], "gemm": ["k_gemm"],
-                "qadamw_encode": ["k_qv_pass1", "k_qv_pass2"], "qadamw_decode": ["k_qv_decode"],
-                "qadamw_step": ["k_qs_pass1", "k_qs_pass2"],
+                "qadamw_encode": ["k_qv_pass1", "k_max_partials", "k_qv_pass2"],
+                "qadamw_decode": ["k_qv_decode"],
+                "qadamw_step": ["k_qs_pass1", "k_max_partials", "k_qs_pass2"],
                 "dequant": ["k_dequant"]}
 
 

@@ -12,9 +12,9 @@
 // 16k .. 16k+15 of a wave, so the tile sum is an in-register pairwise tree over the
 // row followed by xor-shuffles 1, 2, 4, 8 over the 16 row sums -- the same adjacent-
 // pair tree in the same order.  A workgroup (4 waves) covers 16 rows x 256 columns.
-// Encoding needs the amax of the whole transformed residual first, so it is two
-// kernels like the quantizer (per-workgroup partial maxima, reduced in every
-// workgroup of the second pass).
+// Encoding needs the amax of the whole transformed residual first, so it is two passes
+// like the quantizer: per-workgroup partial maxima, reduced once by k_max_partials, then
+// the encode.
 #include "nvfp4.h"
 #include "device_common.h"
 #include "quantize_kernels.h"   // encode8_rne, encode8_sr, sse8_rne (the quantizer's block encoders)
@@ -33,7 +33,8 @@ struct QVArgs {
     uint8_t* codes;
     uint8_t* scales;
     float* sg;
-    float* partial;
+    float* partial;      // [nblocks] per-workgroup maxima of the first pass
+    const float* amax;   // [1] their maximum (k_max_partials)
     int tiles_c;   // workgroups along columns
     int nblocks;   // workgroups
 };
@@ -129,6 +130,38 @@ __device__ __forceinline__ float block_max1(float a, float* red) {
     return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+// The tensor maxima from the first pass's per-workgroup partials: one workgroup reads the
+// `arrays` (1 or 2) arrays of n partials once and writes their maxima to out[0 .. arrays-1].
+// The second pass then reads those instead of every workgroup re-reading all n partials.
+// Each thread issues its loads of a round (8 per array) before using any of them, so a round
+// costs one memory latency.  The maximum is exact: the reduction order does not change it.
+constexpr int kMaxThreads = 1024;
+__global__ __launch_bounds__(kMaxThreads) void k_max_partials(const float* partial, int n,
+                                                             int arrays, float* out) {
+    __shared__ float red[2][kMaxThreads / 64];
+    float x = 0.0f, y = 0.0f;
+    for (int i0 = threadIdx.x; i0 < n; i0 += 8 * kMaxThreads) {
+        float px[8], py[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * kMaxThreads;
+            px[u] = i < n ? partial[i] : 0.0f;
+            py[u] = (arrays > 1 && i < n) ? partial[n + i] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) { x = fmaxf(x, px[u]); y = fmaxf(y, py[u]); }
+    }
+    x = wave_max(x);
+    y = wave_max(y);
+    if ((threadIdx.x & 63) == 0) { red[0][threadIdx.x >> 6] = x; red[1][threadIdx.x >> 6] = y; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kMaxThreads / 64; ++w) { x = fmaxf(x, red[0][w]); y = fmaxf(y, red[1][w]); }
+        out[0] = x;
+        if (arrays > 1) out[1] = y;
+    }
+}
+
 __global__ __launch_bounds__(QVThreads) void k_qv_pass1(QVArgs a) {
     __shared__ float red[4];
     int64_t r, c;
@@ -148,12 +181,8 @@ __global__ __launch_bounds__(QVThreads) void k_qv_pass1(QVArgs a) {
 }
 
 __global__ __launch_bounds__(QVThreads) void k_qv_pass2(QVArgs a) {
-    __shared__ float red[4];
     __shared__ float rtab[128];   // element reciprocal per scale code
-    float am = 0.0f;
-    for (int i = threadIdx.x; i < a.nblocks; i += QVThreads) am = fmaxf(am, a.partial[i]);
-    am = block_max1(am, red);
-    const float sg = uniform_f(sg_from_amax(am));
+    const float sg = uniform_f(sg_from_amax(a.amax[0]));
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.sg = sg;
     if (threadIdx.x < 128) {
         const uint32_t t = threadIdx.x;
@@ -292,7 +321,8 @@ struct QSArgs {
     float lr, b1, b2, eps, wd, cg, bias1, bias2;
     uint32_t mk0, mk1, sk0, sk1, vk0, vk1;
     int v_use_signs;
-    float* partial;   // [2][nblocks]: m and v residual maxima per workgroup
+    float* partial;      // [2][nblocks]: m and v residual maxima per workgroup
+    const float* amax;   // [2]: their maxima (k_max_partials)
     int tiles_c, nblocks;
 };
 
@@ -408,15 +438,8 @@ __global__ __launch_bounds__(QVThreads) void k_qs_pass1(QSArgs a) {
 // fifth wave keeps the SIMDs issuing more of the time: 163 -> 156 us at 9216 x 3072, same
 // output.  Six waves (80 VGPRs) spilled more and lost.
 __global__ __launch_bounds__(QVThreads, 5) void k_qs_pass2(QSArgs a) {
-    __shared__ float red[8];
     __shared__ float rtab[2][128];   // element reciprocal per scale code: m, v
-    float am = 0.0f, av = 0.0f;
-    for (int i = threadIdx.x; i < a.nblocks; i += QVThreads) {
-        am = fmaxf(am, a.partial[i]);
-        av = fmaxf(av, a.partial[a.nblocks + i]);
-    }
-    block_max2(am, av, red);
-    const float sgm = uniform_f(sg_from_amax(am)), sgv = uniform_f(sg_from_amax(av));
+    const float sgm = uniform_f(sg_from_amax(a.amax[0])), sgv = uniform_f(sg_from_amax(a.amax[1]));
     if (blockIdx.x == 0 && threadIdx.x == 0) { *a.msgo = sgm; *a.vsgo = sgv; }
     {
         const uint32_t t = threadIdx.x & 127;
@@ -507,9 +530,15 @@ static int64_t qv_blocks(int64_t rows, int64_t cols, int* tiles_c) {
     return (rows / 16) * tc;
 }
 
+// Workspace: `arrays` arrays of per-workgroup partial maxima, then (16-byte aligned) their
+// `arrays` maxima.
+static size_t partials_floats(int64_t rows, int64_t cols, int arrays) {
+    return ((size_t)qv_blocks(rows, cols, nullptr) * arrays + 3) & ~(size_t)3;
+}
+
 extern "C" size_t qadamw_v_workspace_bytes(int64_t rows, int64_t cols) {
     if (rows <= 0 || cols <= 0) return 0;
-    return (size_t)qv_blocks(rows, cols, nullptr) * sizeof(float);
+    return (partials_floats(rows, cols, 1) + 4) * sizeof(float);
 }
 
 extern "C" int qadamw_v_encode(const float* v, int64_t rows, int64_t cols, uint64_t seed,
@@ -533,8 +562,10 @@ extern "C" int qadamw_v_encode(const float* v, int64_t rows, int64_t cols, uint6
     a.use_signs = use_signs != 0;
     a.mu = mu; a.codes = q->codes; a.scales = q->scales; a.sg = q->gscale;
     a.partial = (float*)ws;
+    a.amax = (float*)ws + partials_floats(rows, cols, 1);
     a.nblocks = (int)qv_blocks(rows, cols, &a.tiles_c);
     k_qv_pass1<<<a.nblocks, QVThreads, 0, st>>>(a);
+    k_max_partials<<<1, kMaxThreads, 0, st>>>(a.partial, a.nblocks, 1, (float*)a.amax);
     k_qv_pass2<<<a.nblocks, QVThreads, 0, st>>>(a);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
@@ -564,7 +595,7 @@ extern "C" int qadamw_v_decode(const uint16_t* mu, const nvfp4_qtensor* q, int64
 
 extern "C" size_t qadamw_step_workspace_bytes(int64_t rows, int64_t cols) {
     if (rows <= 0 || cols <= 0) return 0;
-    return (size_t)qv_blocks(rows, cols, nullptr) * 2 * sizeof(float);
+    return (partials_floats(rows, cols, 2) + 4) * sizeof(float);
 }
 
 extern "C" int qadamw_step(float* w, const void* g, int g_dtype, int64_t rows, int64_t cols,
@@ -605,9 +636,11 @@ extern "C" int qadamw_step(float* w, const void* g, int g_dtype, int64_t rows, i
     a.vk0 = (uint32_t)p->v_seed; a.vk1 = (uint32_t)(p->v_seed >> 32);
     a.v_use_signs = p->v_use_signs != 0;
     a.partial = (float*)ws;
+    a.amax = (float*)ws + partials_floats(rows, cols, 2);
     a.nblocks = (int)qv_blocks(rows, cols, &a.tiles_c);
     hipStream_t st = (hipStream_t)stream;
     k_qs_pass1<<<a.nblocks, QVThreads, 0, st>>>(a);
+    k_max_partials<<<1, kMaxThreads, 0, st>>>(a.partial, a.nblocks, 2, (float*)a.amax);
     k_qs_pass2<<<a.nblocks, QVThreads, 0, st>>>(a);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }

@@ -452,11 +452,19 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
         }
     }
 
-    // tensor scales from the per-tile partial maxima
+    // tensor scales from the per-tile partial maxima; a round's loads (4 per copy) are all
+    // issued before any is used
     float mr = 0.0f, mc = 0.0f;
-    for (int i = t; i < a.npart; i += kThreads) {
-        mr = fmaxf(mr, a.partial[i]);
-        mc = fmaxf(mc, a.partial[a.npart + i]);
+    for (int i0 = t; i0 < a.npart; i0 += 4 * kThreads) {
+        float pr[4], pc[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * kThreads;
+            pr[u] = i < a.npart ? a.partial[i] : 0.0f;
+            pc[u] = i < a.npart ? a.partial[a.npart + i] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { mr = fmaxf(mr, pr[u]); mc = fmaxf(mc, pc[u]); }
     }
     block_max2(mr, mc, red);
     const float sg_r = uniform_f(sg_from_amax(mr)), sg_c = uniform_f(sg_from_amax(mc));
