@@ -241,12 +241,38 @@ __device__ __forceinline__ void tri_tile(int t, int T, int& tm, int& tn) {
     tn = r + rem;
 }
 
+// ---------------------------------------------------------------- direct global -> LDS loads
+
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor of a raw byte buffer: base, no stride, num_records bytes, the data
+// format word of untyped 32-bit buffer access.
+__device__ __forceinline__ int4v make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    return int4v{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+
+// Direct loads.  They are written as assembly so that the compiler does not track them:
+// its own bookkeeping would otherwise wait for every pending direct load before each LDS
+// read, which would serialise the three-stage pipeline.  The kernel waits for them
+// explicitly (dma_wait_barrier); it issues no other vector-memory loads in the loop, so
+// the compiler's own waits can only wait longer than needed, never shorter.
+__device__ __forceinline__ void dma16(int4v rsrc, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(int4v rsrc, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
 // LoRA-SVD up-projection in the epilogue (Full-Stack FP4 sec. 3.2 eq. (1), Appendix 9: the
 // low-rank branch shares the GEMM's output tile).  After the main loop the stage buffers are
 // free: the workgroup copies its 256 rows of T and of L, 64 rank entries at a time, into
-// LDS (one round trip instead of one per MFMA operand), then each accumulator block is
-// scaled by s_gA s_gB into a temporary that BF16 MFMAs 32x32x16 (FP32 accumulate) take as C,
-// written back in place.  LDS rows hold 8 chunks of 16 bytes, chunk c at c ^ (row mod 8),
+// LDS (one round trip instead of one per MFMA operand).  The accumulators are scaled by
+// s_gA s_gB in place, and per 16 rank entries each wave reads its 4 T and 4 L fragments
+// and issues its 16 BF16 MFMAs 32x32x16 (FP32 accumulate) on them.  LDS rows hold 8 chunks
+// of 16 bytes, chunk c at c ^ (row mod 8),
 // so the fragment reads (16 bytes of 32 consecutive rows per half-wave) spread over the
 // banks.  Lane (li, h) supplies row li of the block and rank entries 8h..8h+7 of a step.
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
@@ -256,6 +282,29 @@ constexpr int kLoraLdsRow = kLoraChunk * 2;       // bytes per staged row
 __device__ __forceinline__ void stage_lora(const GArgs& g, uint8_t* lds, int64_t m0, int64_t n0,
                                            int64_t k0, int kc) {
     // kc rank entries (a multiple of 16) from k0, rows of T then rows of L
+    if (kc == kLoraChunk && (uint64_t)g.M * g.lr * 2 < kOutOfRange &&
+        (uint64_t)g.N * g.lr * 2 < kOutOfRange) {
+        // A full chunk by direct loads: 64 KB in 64 loads of 1 KB, 16 per wave, all in
+        // flight at once.  Load S fills LDS bytes [1024 S, +1024): 8 rows of one matrix,
+        // lane l taking the global chunk whose swizzled position is l mod 8.  Rows past M or
+        // N read zeros (offset past the buffer's end).
+        const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+        const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+        const int4v rt = make_rsrc(g.lt, (uint32_t)(g.M * g.lr * 2));
+        const int4v rl = make_rsrc(g.lb, (uint32_t)(g.N * g.lr * 2));
+#pragma unroll
+        for (int i = 0; i < 2 * GBM * kLoraLdsRow / 1024 / 4; ++i) {
+            const int S = i * 4 + wid, which = S / (GBM * kLoraLdsRow / 1024);
+            const int row = (S % (GBM * kLoraLdsRow / 1024)) * 8 + (lane >> 3);
+            const int ch = (lane & 7) ^ (row & 7);
+            const int64_t grow = (which ? n0 : m0) + row;
+            const uint32_t off = grow < (which ? g.N : g.M)
+                                     ? (uint32_t)((grow * g.lr + k0 + ch * 8) * 2) : kOutOfRange;
+            dma16(which ? rl : rt, lds0 + (uint32_t)S * 1024, off);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        return;
+    }
     const int chunks = kc / 8;                    // 16-byte chunks per row
     for (int q = threadIdx.x; q < 2 * GBM * chunks; q += GThreads) {
         const int which = q / (GBM * chunks), rem = q % (GBM * chunks);
@@ -283,25 +332,26 @@ __device__ __forceinline__ void lora_epilogue(const GArgs& g, uint8_t* lds, floa
         __syncthreads();   // every wave is done with the stage buffers (or the previous chunk)
         stage_lora(g, lds, m0, n0, k0, kc);
         __syncthreads();
+        if (k0 == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float16v c;
-                if (k0 == 0) {
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) c[r] = acc[i][j][r] * scale;
-                } else {
-                    c = acc[i][j];
-                }
-                for (int s = 0; s < kc; s += 16) {
-                    const bf16x8v a = lds_frag(lds, 0, ra + 32 * i, s / 8 + h);
-                    const bf16x8v b = lds_frag(lds, 1, rb + 32 * j, s / 8 + h);
-                    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-                }
-                acc[i][j] = c;
-            }
-            __builtin_amdgcn_sched_barrier(0);
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] * scale;
+        }
+        // per 16 rank entries: the wave's 4 A and 4 B fragments, then its 16 products
+        for (int s = 0; s < kc; s += 16) {
+            bf16x8v a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = lds_frag(lds, 0, ra + 32 * i, s / 8 + h);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = lds_frag(lds, 1, rb + 32 * j, s / 8 + h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     }
 }
@@ -461,29 +511,6 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm(GArgs g) {
 }
 
 // ---------------------------------------------------------------- direct staging path
-
-typedef int int4v __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor of a raw byte buffer: base, no stride, num_records bytes, the data
-// format word of untyped 32-bit buffer access.
-__device__ __forceinline__ int4v make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t b = (uint64_t)base;
-    return int4v{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
-}
-
-// Direct loads.  They are written as assembly so that the compiler does not track them:
-// its own bookkeeping would otherwise wait for every pending direct load before each LDS
-// read, which would serialise the three-stage pipeline.  The kernel waits for them
-// explicitly (dma_wait_barrier); it issues no other vector-memory loads in the loop, so
-// the compiler's own waits can only wait longer than needed, never shorter.
-__device__ __forceinline__ void dma16(int4v rsrc, uint32_t lds_addr, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(int4v rsrc, uint32_t lds_addr, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
-}
 
 struct Rsrc4 {
     int4v ac, as, bc, bs;
