@@ -65,3 +65,13 @@ def test_qadamw_tiny_values(nv, oracle):
     v[40:56, 256:272] = 3e-33                         # a whole tile of them
     check(nv, oracle, v, 0x5EED5, 1)
 
+
+
+def test_qadamw_many_partials(nv, oracle):
+    """144000 x 16: 9000 first-pass workgroups, so the tensor maximum is reduced from more
+    partials than one round of the reduction's loads covers (8192); the largest value sits in
+    the last tile."""
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    v = synthetic.lognormal((144000, 16), 77)
+    v[-1, 3] = float(v.max()) * 4.0
+    check(nv, oracle, v, 0x5EED5, 1)

@@ -124,3 +124,13 @@ def test_step_refuses_aliased_states(nv):
     p = nv.qadamw_step_params(**HP)
     with pytest.raises(nv.Nvfp4Error):
         nv.qadamw_step(w, w.clone(), q, mu, v, p, m_out=q)
+
+
+def test_step_many_partials(nv, oracle):
+    """144000 x 16: 9000 first-pass workgroups (more partial maxima than one round of the
+    reduction's loads covers), the largest gradient in the last tile."""
+    R, C = 144000, 16
+    w, qm, mu, qv = start_state(oracle, R, C, 31)
+    g = grad(R, C, 32, False)
+    g[-1, 7] = np.float32(np.abs(g).max() * 8.0)
+    check_step(nv, oracle, w, g, qm, mu, qv, 0x53520400, False)
