@@ -433,10 +433,10 @@ __global__ __launch_bounds__(QVThreads) void k_qs_pass1(QSArgs a) {
     }
 }
 
-// Five waves per SIMD: 96 VGPRs and two spilled dwords instead of 100 VGPRs at four.  The
-// pass is long dependent arithmetic chains (decodes, square roots, divisions, Philox), and a
-// fifth wave keeps the SIMDs issuing more of the time: 163 -> 156 us at 9216 x 3072, same
-// output.  Six waves (80 VGPRs) spilled more and lost.
+// Five waves per SIMD (96 VGPRs, no spills) instead of four: the pass is long dependent
+// arithmetic chains (decodes, square roots, divisions, Philox), and a fifth wave keeps the
+// SIMDs issuing more of the time (about 2% at 9216 x 3072, same output).  Six waves (80
+// VGPRs) spill and lose 7%.
 __global__ __launch_bounds__(QVThreads, 5) void k_qs_pass2(QSArgs a) {
     __shared__ float rtab[2][128];   // element reciprocal per scale code: m, v
     const float sgm = uniform_f(sg_from_amax(a.amax[0])), sgv = uniform_f(sg_from_amax(a.amax[1]));
