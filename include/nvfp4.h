@@ -30,8 +30,10 @@
  *     pages give no padding rule); every other extent may be any size >= 0.
  *   - Input values must be finite.  Tensors whose largest magnitude is below
  *     2^-96 give unspecified (but in-bounds) codes.
- *   - Calls on one stream are ordered; the library holds no state, so calls on
- *     different streams may run concurrently on distinct buffers.
+ *   - Calls on one stream are ordered.  The library holds no state apart from the
+ *     scratch array of nvfp4_quantize_noalloc, so calls on different streams may run
+ *     concurrently on distinct buffers (except two nvfp4_quantize_noalloc calls on one
+ *     device).
  *
  * Quantized tensor layout (one "copy"): an n x k matrix quantized along its
  * rows has
@@ -53,7 +55,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 5
+#define NVFP4_ABI_VERSION 6
 
 enum nvfp4_status {
     NVFP4_OK = 0,
@@ -131,6 +133,23 @@ size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols, const nvfp4_qu
 int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
                    const nvfp4_quant_params* p, const nvfp4_qtensor* row_out,
                    const nvfp4_qtensor* col_out, void* ws, size_t ws_bytes, void* stream);
+
+/* nvfp4_quantize without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments, results and errors are those of nvfp4_quantize with the same x, p and copies.
+ * The per-workgroup partial maxima go to a file-scope device array of
+ * NVFP4_NOALLOC_SCRATCH_BYTES (6 KiB) instead of `ws`; each device holds its own copy from
+ * the first call on it until the process ends.  Every shape fits (the first pass never has
+ * more than 768 workgroups); a larger need would give NVFP4_ERR_WORKSPACE.  The call uses
+ * the array of the current device (hipGetDevice), so `stream` must belong to it.  The call
+ * allocates nothing: the array's address is looked up once per device on the first call.
+ * Calls that overlap in time on one device share that array and race: order them on one
+ * stream (or synchronise between streams).  nvfp4_quantize with its own workspace has no
+ * such restriction. */
+#define NVFP4_NOALLOC_SCRATCH_BYTES 6144
+int nvfp4_quantize_noalloc(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                           const nvfp4_quant_params* p, const nvfp4_qtensor* row_out,
+                           const nvfp4_qtensor* col_out, void* stream);
 
 /* nvfp4_quantize with the LoRA-SVD down-projection fused into its first pass:
  *   lora_t[rows][rank] = BF16(beta * x lora_a^T)   (nearest-even from the FP32 sum)

@@ -33,7 +33,7 @@ EXPORTED = ["nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantiz
             "qadamw_step", "nvfp4_gemm_lora", "nvfp4_quantize_lora_workspace_bytes",
             "nvfp4_quantize_lora", "nvfp4_requantize_cols_workspace_bytes",
             "nvfp4_requantize_cols", "nvfp4_gemm_axpby", "nvfp4_ns_step_workspace_bytes",
-            "nvfp4_ns_step"]
+            "nvfp4_ns_step", "nvfp4_quantize_noalloc"]
 
 
 class Nvfp4Error(RuntimeError):
@@ -62,7 +62,7 @@ class QTensorC(ctypes.Structure):
 
 
 _lib = None
-ABI_VERSION = 5   # NVFP4_ABI_VERSION of include/nvfp4.h this binding matches
+ABI_VERSION = 6   # NVFP4_ABI_VERSION of include/nvfp4.h this binding matches
 
 
 def load_library(path: Optional[str] = None):
@@ -82,6 +82,9 @@ def load_library(path: Optional[str] = None):
     lib.nvfp4_quantize.restype = ctypes.c_int
     lib.nvfp4_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, P(QuantParams),
                                    P(QTensorC), P(QTensorC), vp, sz, vp]
+    lib.nvfp4_quantize_noalloc.restype = ctypes.c_int
+    lib.nvfp4_quantize_noalloc.argtypes = [vp, ctypes.c_int, i64, i64, i64, P(QuantParams),
+                                           P(QTensorC), P(QTensorC), vp]
     lib.nvfp4_dequantize.restype = ctypes.c_int
     lib.nvfp4_dequantize.argtypes = [P(QTensorC), i64, i64, ctypes.c_int, vp, i64, vp]
     lib.nvfp4_gemm.restype = ctypes.c_int
@@ -214,6 +217,30 @@ def nvfp4_quantize(x, params, row_out=None, col_out=None, workspace=None):
                             _ptr(workspace), workspace.numel(), _stream(dev))
     _check(rc)
     return (row_out if params.rowwise else None), (col_out if params.colwise else None)
+
+
+def nvfp4_quantize_noalloc(x, params, row_out, col_out=None):
+    """nvfp4_quantize into caller-allocated copies with no workspace: the library keeps the
+    partial maxima in its per-device scratch array (calls on one device must not overlap)."""
+    lib = load_library()
+    _require_cuda(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise Nvfp4Error("x must be a 2-D tensor with unit column stride")
+    if x.dtype == torch.bfloat16:
+        dt = NVFP4_BF16
+    elif x.dtype == torch.float32:
+        dt = NVFP4_F32
+    else:
+        raise Nvfp4Error(f"unsupported dtype {x.dtype}")
+    R, C = x.shape
+    rc_ = row_out.c() if params.rowwise else None
+    cc_ = col_out.c() if params.colwise else None
+    with torch.cuda.device(x.device):
+        _check(lib.nvfp4_quantize_noalloc(_ptr(x), dt, R, C, x.stride(0), ctypes.byref(params),
+                                          ctypes.byref(rc_) if rc_ is not None else None,
+                                          ctypes.byref(cc_) if cc_ is not None else None,
+                                          _stream(x.device)))
+    return row_out, col_out
 
 
 def nvfp4_dequantize(q, out_dtype=torch.float32, out=None):

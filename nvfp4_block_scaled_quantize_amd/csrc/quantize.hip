@@ -3,6 +3,8 @@
 // work decomposition); their specialisations are compiled in quantize_launch_*.hip.
 #include "quantize_kernels.h"
 
+#include <mutex>
+
 namespace nvfp4 {
 
 __global__ void k_fill_scale_one(float* a, float* b) {
@@ -97,11 +99,24 @@ static int64_t quant_tiles(int64_t rows, int64_t cols, int* tiles_c) {
     return tr * tc;
 }
 
+// Workgroups of the k_amax pass: one wave per 16 x 512 wave tile, four per workgroup, at most
+// about one round of resident workgroups (each then loops), never more than the encode's
+// tiles.  Each writes one partial maximum per copy.
+constexpr int64_t kMaxAmaxParts = 768;
+static int64_t amax_parts(int64_t rows, int64_t cols) {
+    const int64_t wtiles = (rows / 16) * ((cols + kAmaxWaveCols - 1) / kAmaxWaveCols);
+    int64_t np = (wtiles + 3) / 4;
+    if (np > kMaxAmaxParts) np = kMaxAmaxParts;
+    const int64_t nt = quant_tiles(rows, cols, nullptr);
+    if (np > nt) np = nt;
+    return np > 0 ? np : 1;
+}
+
 extern "C" size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols,
                                                  const nvfp4_quant_params* p) {
     (void)p;
     if (rows <= 0 || cols <= 0) return 0;
-    return (size_t)quant_tiles(rows, cols, nullptr) * 2 * sizeof(float);
+    return (size_t)amax_parts(rows, cols) * 2 * sizeof(float);
 }
 
 static int check_qtensor(const nvfp4_qtensor* q) {
@@ -136,10 +151,39 @@ extern "C" size_t nvfp4_quantize_lora_workspace_bytes(int64_t rows, int64_t cols
            (size_t)(sp.parts * rows * rank) * sizeof(float);
 }
 
+// ---------------------------------------------------------------- allocation-free variant
+// The partial maxima of nvfp4_quantize_noalloc go to this file-scope device array instead of
+// a caller workspace.  Every device holds its own copy until the process ends.  In host code
+// the name is only a host-side stand-in: the device address of the current device's copy is
+// taken once per device with hipGetSymbolAddress and kept in g_scratch_ptr.  Nothing in it
+// needs clearing: k_amax writes every partial that k_encode reads.
+static __device__ __align__(256) float scratch[2 * kMaxAmaxParts];
+static_assert(sizeof(scratch) == NVFP4_NOALLOC_SCRATCH_BYTES, "scratch size of the header");
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static int scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return NVFP4_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return NVFP4_OK;
+}
+
+// use_scratch: the partial maxima go to the current device's copy of `scratch` (ws and
+// ws_bytes are ignored).
 static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
                          const nvfp4_quant_params* p, const nvfp4_qtensor* row_out,
                          const nvfp4_qtensor* col_out, const uint16_t* lora_a, int64_t rank,
-                         float beta, uint16_t* lora_t, void* ws, size_t ws_bytes, void* stream) {
+                         float beta, uint16_t* lora_t, void* ws, size_t ws_bytes, void* stream,
+                         bool use_scratch = false) {
     if (!p) return NVFP4_ERR_NULL;
     if (dtype != NVFP4_F32 && dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
     if (rows < 0 || cols < 0 || rows % 16 || cols % 16 || ld_x < cols) return NVFP4_ERR_SHAPE;
@@ -171,6 +215,11 @@ static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, i
     if (!aligned(x, 16) || (ld_x * esize) % 16) return NVFP4_ERR_ALIGN;
     const size_t need = lora_t ? nvfp4_quantize_lora_workspace_bytes(rows, cols, rank)
                                : nvfp4_quantize_workspace_bytes(rows, cols, p);
+    if (use_scratch) {
+        if (lora_t || need > sizeof(scratch)) return NVFP4_ERR_WORKSPACE;
+        if ((rc = scratch_of_current_device(&ws)) != NVFP4_OK) return rc;
+        ws_bytes = sizeof(scratch);
+    }
     if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
     if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
 
@@ -218,13 +267,8 @@ static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, i
         a.lora_parts = (int)sp.parts;
         a.lora_kp = sp.kp;
         a.lora_beta = beta;
-    } else {   // k_amax: one wave per 16 x 512 wave tile, four per workgroup, at most about one
-        // round of resident workgroups (each then loops), never more than ntiles
-        const int64_t wtiles = (rows / 16) * ((cols + kAmaxWaveCols - 1) / kAmaxWaveCols);
-        int64_t np = (wtiles + 3) / 4;
-        if (np > 768) np = 768;
-        if (np > a.ntiles) np = a.ntiles;
-        a.npart = (int)(np > 0 ? np : 1);
+    } else {
+        a.npart = (int)amax_parts(rows, cols);
     }
     const int f = a.sr_row | (a.sr_col << 1) | (a.rht_row << 2) | (a.rht_col << 3);
     if (a.is_bf16)
@@ -240,6 +284,14 @@ extern "C" int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t co
                               void* stream) {
     return quantize_impl(x, dtype, rows, cols, ld_x, p, row_out, col_out, nullptr, 0, 0.0f,
                          nullptr, ws, ws_bytes, stream);
+}
+
+extern "C" int nvfp4_quantize_noalloc(const void* x, int dtype, int64_t rows, int64_t cols,
+                                      int64_t ld_x, const nvfp4_quant_params* p,
+                                      const nvfp4_qtensor* row_out, const nvfp4_qtensor* col_out,
+                                      void* stream) {
+    return quantize_impl(x, dtype, rows, cols, ld_x, p, row_out, col_out, nullptr, 0, 0.0f,
+                         nullptr, nullptr, 0, stream, true);
 }
 
 __global__ void k_fill_u16(uint16_t* p, int64_t n, uint16_t v) {
@@ -283,7 +335,7 @@ void launch_requant_cols(int f, const QArgs& a, hipStream_t st) {
 
 extern "C" size_t nvfp4_requantize_cols_workspace_bytes(int64_t rows, int64_t cols) {
     if (rows <= 0 || cols <= 0) return 0;
-    return (size_t)quant_tiles(rows, cols, nullptr) * 2 * sizeof(float);
+    return (size_t)amax_parts(rows, cols) * 2 * sizeof(float);
 }
 
 extern "C" int nvfp4_requantize_cols(const nvfp4_qtensor* row_in, int64_t rows, int64_t cols,
@@ -341,13 +393,7 @@ extern "C" int nvfp4_requantize_cols(const nvfp4_qtensor* row_in, int64_t rows, 
     a.lora_parts = 0;
     a.lora_kp = 0;
     a.lora_beta = 0.0f;
-    {
-        const int64_t wtiles = (rows / 16) * ((cols + kAmaxWaveCols - 1) / kAmaxWaveCols);
-        int64_t np = (wtiles + 3) / 4;
-        if (np > 768) np = 768;
-        if (np > a.ntiles) np = a.ntiles;
-        a.npart = (int)(np > 0 ? np : 1);
-    }
+    a.npart = (int)amax_parts(rows, cols);
     launch_requant_cols((a.sr_col << 1) | (a.rht_col << 3), a, st);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(nv):
 
 def test_version_and_status_strings(nv):
     lib = nv.load_library()
-    assert lib.nvfp4_abi_version() == nv.ABI_VERSION == 5
+    assert lib.nvfp4_abi_version() == nv.ABI_VERSION == 6
     assert lib.nvfp4_status_string(0) == b"ok"
     for code in range(-7, 0):
         s = lib.nvfp4_status_string(code)
@@ -103,6 +103,27 @@ def test_quantize_argument_errors(nv):
                 nv.quant_params(rowwise=False, colwise=True, block2d=True, rht_col=True)]:
         assert call(x, 1, 32, 32, 32, ctypes.byref(bad), ctypes.byref(q), ctypes.byref(q), ws,
                     1 << 20, None) == -5
+
+
+def test_quantize_noalloc_argument_errors(nv):
+    """The allocation-free variant validates like nvfp4_quantize before it looks up its
+    scratch array, so none of these touches a device."""
+    lib = nv.load_library()
+    p = nv.quant_params(rowwise=True)
+    q = _qt(FAKE)
+    x = ctypes.c_void_p(FAKE + 0x80000)
+    call = lambda *a: lib.nvfp4_quantize_noalloc(*a)
+    assert call(x, 1, 20, 32, 32, ctypes.byref(p), ctypes.byref(q), None, None) == -2
+    assert call(x, 7, 32, 32, 32, ctypes.byref(p), ctypes.byref(q), None, None) == -4
+    assert call(x, 1, 32, 32, 32, None, ctypes.byref(q), None, None) == -1
+    assert call(None, 1, 32, 32, 32, ctypes.byref(p), ctypes.byref(q), None, None) == -1
+    assert call(ctypes.c_void_p(FAKE + 0x80008), 1, 32, 32, 32, ctypes.byref(p), ctypes.byref(q),
+                None, None) == -3
+    bad = nv.quant_params(block2d=True, scale46=True)
+    assert call(x, 1, 32, 32, 32, ctypes.byref(bad), ctypes.byref(q), None, None) == -5
+    # the scratch array holds the partial maxima of any shape (at most 768 per copy)
+    for shape in [(16, 16), (8192, 3072), (65552, 16384), (1 << 20, 1 << 14)]:
+        assert lib.nvfp4_quantize_workspace_bytes(*shape, ctypes.byref(p)) <= 6144
 
 
 def test_gemm_and_dequantize_argument_errors(nv):
