@@ -28,8 +28,12 @@
  *     the caller's next synchronisation.
  *   - Matrices are row-major.  Block dimensions must be multiples of 16 (the
  *     pages give no padding rule); every other extent may be any size >= 0.
- *   - Input values must be finite.  Tensors whose largest magnitude is below
- *     2^-96 give unspecified (but in-bounds) codes.
+ *   - Input values must be finite; any finite values are quantized as described, down
+ *     to tensors of subnormal values.  Elements are scaled by the correctly rounded
+ *     reciprocal of fl(s s_g), kept at binary32 precision; where its exponent exceeds
+ *     binary32's range (fl(s s_g) < about 2^-128, only for tensor maxima below about
+ *     2^-107) it is carried as R 2^-64 with the 2^64 restored in the E2M1 conversion.
+ *     The GEMM's stated accuracy assumes s_gA s_gB is a normal binary32.
  *   - Calls on one stream are ordered.  The library holds no state apart from the
  *     scratch array of nvfp4_quantize_noalloc, so calls on different streams may run
  *     concurrently on distinct buffers (except two nvfp4_quantize_noalloc calls on one
@@ -241,7 +245,12 @@ int nvfp4_gemm_axpby(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, 
  * The call enqueues three quantizes and three GEMMs.  When m is a multiple of 256, A (which
  * is symmetric) is formed on its upper-triangle tiles with K split into parts, then summed
  * in part order and mirrored; the workspace then also holds those partial products
- * (58.5 MB for m = 3072, n = 9216). */
+ * (58.5 MB for m = 3072, n = 9216).
+ * After the call (once the stream reaches it) the workspace holds the iteration's
+ * intermediates, each starting at the previous one's end rounded up to 256 bytes, from
+ * offset 0: qX (codes [m][n/2], scales [m][n/16], s_g float), qX' ([n][m/2], [n][m/16],
+ * s_g), A (FP32 [m][m]), qA, qA' (each [m][m/2], [m][m/16], s_g), B (FP32 [m][m]), qB
+ * ([m][m/2], [m][m/16], s_g); the rest is scratch. */
 size_t nvfp4_ns_step_workspace_bytes(int64_t m, int64_t n);
 int nvfp4_ns_step(float* x, int64_t m, int64_t n, float a, float b, float c, uint64_t seed,
                   int32_t scale46, void* ws, size_t ws_bytes, void* stream);

@@ -86,12 +86,15 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
 }
 
 // ---------------------------------------------------------------- E2M1 element
-// Two binary32 values -> two E2M1 codes (nearest-even, saturating at 6, sign copied),
-// written into byte `sel` of `old`.  The hardware conversion at scale 1.0 equals that
-// rounding for every finite binary32 input (checked exhaustively on gfx950).
+// Two binary32 values -> two E2M1 codes (nearest-even, saturating at 6, sign copied) of
+// a / cs and b / cs, written into byte `sel` of `old`.  The scale operand cs is a power of
+// two (the conversion uses only its exponent); the division by it is exact.  At cs = 1 the
+// hardware conversion equals that rounding for every finite binary32 input, and at
+// cs = 2^-64 it equals the conversion of a 2^64 at cs = 1 wherever that is finite (both
+// checked exhaustively on gfx950).
 template <int SEL>
-__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b) {
-    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b, float cs = 1.0f) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, cs, SEL);
 }
 
 // Stochastic rounding of one value v = x * rcp to an E2M1 code with 16 random bits r16: the
@@ -105,9 +108,11 @@ __device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b) {
 // bits 0..3, bits 4..7 zero): the compiler does not carry the builtin's first operand into
 // the bytes the instruction leaves alone.  (A GPU test compares the conversion with the
 // plain rule for every finite binary32 value.)
-__device__ __forceinline__ uint32_t cvt_fp4_sr(float v, uint32_t seed) {
+// cs: the power-of-two scale operand, as for cvt_fp4x2 (v / cs is rounded; checked against
+// v 2^64 at cs = 1 for cs = 2^-64).
+__device__ __forceinline__ uint32_t cvt_fp4_sr(float v, uint32_t seed, float cs = 1.0f) {
     const float2v p = {v, 0.0f};
-    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, seed, 1.0f, 0);
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, seed, cs, 0);
 }
 
 // Decode the two E2M1 codes in byte SEL of w to binary32 (exact).
@@ -170,6 +175,33 @@ __device__ __forceinline__ float div_rn_by(float a, float b, float rb) {
     const float q = a * rb;
     const float r = __builtin_fmaf(-q, b, a);
     return __builtin_fmaf(r, rb, q);
+}
+
+// Correctly rounded square roots of 16 non-negative finite values, in place.  The hardware
+// estimate v_sqrt_f32 is within one ulp for inputs of at least 2^-96; the root is then s,
+// or s - ulp when (s - ulp) s >= x, or s + ulp when (s + ulp) s < x (residuals by fma,
+// exact), which is also right for x = 0.  This is the library square root's own sequence
+// for that range, without its rescaling of tiny inputs and its special-value checks.  When
+// any lane of the wave holds a value in (0, 2^-96), the whole wave takes sqrtf instead.
+__device__ __forceinline__ void sqrt16_rn(float y[16]) {
+    // bits - 1 of a value in (0, 2^-96) is below that of 2^-96; 0 wraps to the top
+    uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mn = min(mn, __float_as_uint(y[i]) - 1u);
+    if (__builtin_amdgcn_ballot_w64(mn < 0x0F7FFFFFu) != 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] = sqrtf(y[i]);
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float x = y[i], s = __builtin_amdgcn_sqrtf(x);
+        const float sm = __uint_as_float(__float_as_uint(s) - 1u);
+        const float sp = __uint_as_float(__float_as_uint(s) + 1u);
+        float r = __builtin_fmaf(-sm, s, x) <= 0.0f ? sm : s;
+        r = __builtin_fmaf(-sp, s, x) > 0.0f ? sp : r;
+        y[i] = r;
+    }
 }
 
 __device__ __forceinline__ float wave_max(float v) {

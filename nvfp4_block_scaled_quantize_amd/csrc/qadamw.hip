@@ -39,33 +39,6 @@ struct QVArgs {
     int nblocks;   // workgroups
 };
 
-// Correctly rounded square roots of 16 non-negative finite values, in place.  The hardware
-// estimate v_sqrt_f32 is within one ulp for inputs of at least 2^-96; the root is then s,
-// or s - ulp when (s - ulp) s >= x, or s + ulp when (s + ulp) s < x (residuals by fma,
-// exact), which is also right for x = 0.  This is the library square root's own sequence
-// for that range, without its rescaling of tiny inputs and its special-value checks.  When
-// any lane of the wave holds a value in (0, 2^-96), the whole wave takes sqrtf instead.
-__device__ __forceinline__ void sqrt16_rn(float y[16]) {
-    // bits - 1 of a value in (0, 2^-96) is below that of 2^-96; 0 wraps to the top
-    uint32_t mn = 0xFFFFFFFFu;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mn = min(mn, __float_as_uint(y[i]) - 1u);
-    if (__builtin_amdgcn_ballot_w64(mn < 0x0F7FFFFFu) != 0) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) y[i] = sqrtf(y[i]);
-        return;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float x = y[i], s = __builtin_amdgcn_sqrtf(x);
-        const float sm = __uint_as_float(__float_as_uint(s) - 1u);
-        const float sp = __uint_as_float(__float_as_uint(s) + 1u);
-        float r = __builtin_fmaf(-sm, s, x) <= 0.0f ? sm : s;
-        r = __builtin_fmaf(-sp, s, x) > 0.0f ? sp : r;
-        y[i] = r;
-    }
-}
-
 __device__ __forceinline__ float tree16_row(const float y[16]) {
     float t[8], u[4], w[2];
 #pragma unroll
@@ -184,12 +157,10 @@ __global__ __launch_bounds__(QVThreads) void k_qv_pass2(QVArgs a) {
     __shared__ float rtab[128];   // element reciprocal per scale code
     const float sg = uniform_f(sg_from_amax(a.amax[0]));
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.sg = sg;
-    if (threadIdx.x < 128) {
-        const uint32_t t = threadIdx.x;
-        rtab[t] = t ? __fdiv_rn(1.0f, e4m3_value(t) * sg) : 0.0f;
-    }
+    const bool tiny = tiny_scale(sg);
+    if (threadIdx.x < 128) rtab[threadIdx.x] = recip_entry(threadIdx.x, sg, tiny);
     __syncthreads();
-    const CopyScale csc{sg, __fdiv_rn(1.0f, sg), sg >= 0x1p-92f, rtab};
+    const CopyScale csc{sg, __fdiv_rn(1.0f, sg), sg >= 0x1p-92f, rtab, conv_scale(tiny)};
 
     int64_t r, c;
     bool valid;
@@ -201,16 +172,10 @@ __global__ __launch_bounds__(QVThreads) void k_qv_pass2(QVArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(e[i]));
     const uint32_t scode = csc.code(bm, 6.0f, kRcp6);
-    const float rcp = csc.rcp(scode);
-    uint32_t lo = 0, hi = 0;
-    lo = cvt_fp4x2<0>(lo, e[0] * rcp, e[1] * rcp);
-    lo = cvt_fp4x2<1>(lo, e[2] * rcp, e[3] * rcp);
-    lo = cvt_fp4x2<2>(lo, e[4] * rcp, e[5] * rcp);
-    lo = cvt_fp4x2<3>(lo, e[6] * rcp, e[7] * rcp);
-    hi = cvt_fp4x2<0>(hi, e[8] * rcp, e[9] * rcp);
-    hi = cvt_fp4x2<1>(hi, e[10] * rcp, e[11] * rcp);
-    hi = cvt_fp4x2<2>(hi, e[12] * rcp, e[13] * rcp);
-    hi = cvt_fp4x2<3>(hi, e[14] * rcp, e[15] * rcp);
+    float u[16];
+    csc.scale8(&e[0], scode, 1.0f, &u[0]);
+    csc.scale8(&e[8], scode, 1.0f, &u[8]);
+    const uint32_t lo = encode8_rne(&u[0], csc.cs), hi = encode8_rne(&u[8], csc.cs);
     if (valid) {
         *(uint2*)(a.codes + r * (a.cols / 2) + c / 2) = make_uint2(lo, hi);
         a.scales[r * (a.cols / 16) + c / 16] = (uint8_t)scode;
@@ -441,14 +406,15 @@ __global__ __launch_bounds__(QVThreads, 5) void k_qs_pass2(QSArgs a) {
     __shared__ float rtab[2][128];   // element reciprocal per scale code: m, v
     const float sgm = uniform_f(sg_from_amax(a.amax[0])), sgv = uniform_f(sg_from_amax(a.amax[1]));
     if (blockIdx.x == 0 && threadIdx.x == 0) { *a.msgo = sgm; *a.vsgo = sgv; }
+    const bool tiny_m = tiny_scale(sgm), tiny_v = tiny_scale(sgv);
     {
         const uint32_t t = threadIdx.x & 127;
-        const float sg = threadIdx.x < 128 ? sgm : sgv;
-        rtab[threadIdx.x >> 7][t] = t ? __fdiv_rn(1.0f, e4m3_value(t) * sg) : 0.0f;
+        const bool mrow = threadIdx.x < 128;
+        rtab[threadIdx.x >> 7][t] = recip_entry(t, mrow ? sgm : sgv, mrow ? tiny_m : tiny_v);
     }
     __syncthreads();
-    const CopyScale msc{sgm, __fdiv_rn(1.0f, sgm), sgm >= 0x1p-92f, rtab[0]};
-    const CopyScale vsc{sgv, __fdiv_rn(1.0f, sgv), sgv >= 0x1p-92f, rtab[1]};
+    const CopyScale msc{sgm, __fdiv_rn(1.0f, sgm), sgm >= 0x1p-92f, rtab[0], conv_scale(tiny_m)};
+    const CopyScale vsc{sgv, __fdiv_rn(1.0f, sgv), sgv >= 0x1p-92f, rtab[1], conv_scale(tiny_v)};
 
     int64_t r, c;
     bool valid;
@@ -490,15 +456,20 @@ __global__ __launch_bounds__(QVThreads, 5) void k_qs_pass2(QSArgs a) {
         uint32_t sc = msc.code(bm, 6.0f, kRcp6);
         const uint32_t sc4 = msc.code(bm, 4.0f, 0.25f);
         const float s6 = e4m3_value(sc), s4 = e4m3_value(sc4);
-        const float q6 = msc.rcp(sc), q4 = msc.rcp(sc4);
         uint32_t t0, t1, t2, t3;
-        const float e6 = sse8_rne(&y[0], s6, q6, sgm, t0) + sse8_rne(&y[8], s6, q6, sgm, t1);
-        const float e4 = sse8_rne(&y[0], s4, q4, sgm, t2) + sse8_rne(&y[8], s4, q4, sgm, t3);
+        float u[16];
+        msc.scale8(&y[0], sc, 1.0f, &u[0]);
+        msc.scale8(&y[8], sc, 1.0f, &u[8]);
+        const float e6 = sse8_rne(&y[0], &u[0], s6, sgm, msc.cs, t0) + sse8_rne(&y[8], &u[8], s6, sgm, msc.cs, t1);
+        msc.scale8(&y[0], sc4, 1.0f, &u[0]);
+        msc.scale8(&y[8], sc4, 1.0f, &u[8]);
+        const float e4 = sse8_rne(&y[0], &u[0], s4, sgm, msc.cs, t2) + sse8_rne(&y[8], &u[8], s4, sgm, msc.cs, t3);
         sc = e4 < e6 ? sc4 : sc;
-        const float rcp = e4 < e6 ? q4 : q6;
+        msc.scale8(&y[0], sc, 1.0f, &u[0]);
+        msc.scale8(&y[8], sc, 1.0f, &u[8]);
         const uint64_t g0 = ((uint64_t)r * (uint64_t)a.cols + (uint64_t)c) >> 3;
-        const uint32_t lo = encode8_sr(&y[0], rcp, sr_words(g0, 0u, a.sk0, a.sk1));
-        const uint32_t hi = encode8_sr(&y[8], rcp, sr_words(g0 + 1, 0u, a.sk0, a.sk1));
+        const uint32_t lo = encode8_sr(&u[0], sr_words(g0, 0u, a.sk0, a.sk1), msc.cs);
+        const uint32_t hi = encode8_sr(&u[8], sr_words(g0 + 1, 0u, a.sk0, a.sk1), msc.cs);
         if (valid) {
             *(uint2*)(a.mco + r * (a.cols / 2) + c / 2) = make_uint2(lo, hi);
             a.mso[r * (a.cols / 16) + c / 16] = (uint8_t)sc;
@@ -511,8 +482,10 @@ __global__ __launch_bounds__(QVThreads, 5) void k_qs_pass2(QSArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(e[i]));
         const uint32_t sc = vsc.code(bm, 6.0f, kRcp6);
-        const float rcp = vsc.rcp(sc);
-        const uint32_t lo = encode8_rne(&e[0], rcp), hi = encode8_rne(&e[8], rcp);
+        float u[16];
+        vsc.scale8(&e[0], sc, 1.0f, &u[0]);
+        vsc.scale8(&e[8], sc, 1.0f, &u[8]);
+        const uint32_t lo = encode8_rne(&u[0], vsc.cs), hi = encode8_rne(&u[8], vsc.cs);
         if (valid) {
             *(uint2*)(a.vco + r * (a.cols / 2) + c / 2) = make_uint2(lo, hi);
             a.vso[r * (a.cols / 16) + c / 16] = (uint8_t)sc;

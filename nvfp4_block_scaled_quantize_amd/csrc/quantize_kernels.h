@@ -319,29 +319,31 @@ __global__ __launch_bounds__(kThreads) void k_amax(QArgs a) {
     }
 }
 
-// Codes for 8 values (one dword), nearest-even.
-__device__ __forceinline__ uint32_t encode8_rne(const float w[8], float rcp) {
+// Codes for 8 scaled values u (one dword), nearest-even: of u / cs, cs a power of two (1,
+// or 2^-64 for the scaled values of a tiny copy; see CopyScale).
+__device__ __forceinline__ uint32_t encode8_rne(const float u[8], float cs) {
     uint32_t r = 0;
-    r = cvt_fp4x2<0>(r, w[0] * rcp, w[1] * rcp);
-    r = cvt_fp4x2<1>(r, w[2] * rcp, w[3] * rcp);
-    r = cvt_fp4x2<2>(r, w[4] * rcp, w[5] * rcp);
-    r = cvt_fp4x2<3>(r, w[6] * rcp, w[7] * rcp);
+    r = cvt_fp4x2<0>(r, u[0], u[1], cs);
+    r = cvt_fp4x2<1>(r, u[2], u[3], cs);
+    r = cvt_fp4x2<2>(r, u[4], u[5], cs);
+    r = cvt_fp4x2<3>(r, u[6], u[7], cs);
     return r;
 }
 
-// Codes for 8 values (one dword), stochastic, with the 4 Philox words of their group:
-// element 2b takes the low half of word b, element 2b + 1 the high half.  Each conversion
-// leaves its code in byte 0 of its result; byte permutes gather the even codes into the
-// bytes of one dword and the odd ones into another, which is shifted into the high nibbles.
-__device__ __forceinline__ uint32_t encode8_sr(const float w[8], float rcp, const U4& rw) {
-    const uint32_t c0 = cvt_fp4_sr(w[0] * rcp, rw.x << 16);
-    const uint32_t c1 = cvt_fp4_sr(w[1] * rcp, rw.x & 0xFFFF0000u);
-    const uint32_t c2 = cvt_fp4_sr(w[2] * rcp, rw.y << 16);
-    const uint32_t c3 = cvt_fp4_sr(w[3] * rcp, rw.y & 0xFFFF0000u);
-    const uint32_t c4 = cvt_fp4_sr(w[4] * rcp, rw.z << 16);
-    const uint32_t c5 = cvt_fp4_sr(w[5] * rcp, rw.z & 0xFFFF0000u);
-    const uint32_t c6 = cvt_fp4_sr(w[6] * rcp, rw.w << 16);
-    const uint32_t c7 = cvt_fp4_sr(w[7] * rcp, rw.w & 0xFFFF0000u);
+// Codes for 8 scaled values (one dword), stochastic (of u / cs, as encode8_rne), with the 4
+// Philox words of their group: element 2b takes the low half of word b, element 2b + 1 the
+// high half.  Each conversion leaves its code in byte 0 of its result; byte permutes gather
+// the even codes into the bytes of one dword and the odd ones into another, which is
+// shifted into the high nibbles.
+__device__ __forceinline__ uint32_t encode8_sr(const float u[8], const U4& rw, float cs) {
+    const uint32_t c0 = cvt_fp4_sr(u[0], rw.x << 16, cs);
+    const uint32_t c1 = cvt_fp4_sr(u[1], rw.x & 0xFFFF0000u, cs);
+    const uint32_t c2 = cvt_fp4_sr(u[2], rw.y << 16, cs);
+    const uint32_t c3 = cvt_fp4_sr(u[3], rw.y & 0xFFFF0000u, cs);
+    const uint32_t c4 = cvt_fp4_sr(u[4], rw.z << 16, cs);
+    const uint32_t c5 = cvt_fp4_sr(u[5], rw.z & 0xFFFF0000u, cs);
+    const uint32_t c6 = cvt_fp4_sr(u[6], rw.w << 16, cs);
+    const uint32_t c7 = cvt_fp4_sr(u[7], rw.w & 0xFFFF0000u, cs);
     // selector bytes 0..3 pick bytes of the second operand, 4..7 of the first, 0x0C gives 0
     const uint32_t ev = __builtin_amdgcn_perm(c2, c0, 0x0C0C0400u) |
                         __builtin_amdgcn_perm(c6, c4, 0x04000C0Cu);
@@ -350,13 +352,13 @@ __device__ __forceinline__ uint32_t encode8_sr(const float w[8], float rcp, cons
     return ev | (od << 4);
 }
 
-// 4/6 adaptive block scaling: squared error of 8 values quantized nearest-even with block
-// scale s (reciprocal rcp = RN(1 / fl(s s_g))), as the fma chain over the values in order of
-// e_i^2, e_i = fma(-(v_i s), s_g, w_i) (v_i the signed decoded code; v_i s is exact).  Also
-// returns the 8 codes.
-__device__ __forceinline__ float sse8_rne(const float w[8], float s, float rcp, float sg,
-                                          uint32_t& codes) {
-    codes = encode8_rne(w, rcp);
+// 4/6 adaptive block scaling: squared error of 8 values w quantized nearest-even with block
+// scale s (u: the values scaled by it), as the fma chain over the values in order of e_i^2,
+// e_i = fma(-(v_i s), s_g, w_i) (v_i the signed decoded code; v_i s is exact).  Also returns
+// the 8 codes.
+__device__ __forceinline__ float sse8_rne(const float w[8], const float u[8], float s, float sg,
+                                          float cs, uint32_t& codes) {
+    codes = encode8_rne(u, cs);
     const float2v p[4] = {fp4x2_to_f32<0>(codes), fp4x2_to_f32<1>(codes), fp4x2_to_f32<2>(codes),
                           fp4x2_to_f32<3>(codes)};
     float acc = 0.0f;
@@ -367,12 +369,6 @@ __device__ __forceinline__ float sse8_rne(const float w[8], float s, float rcp, 
         acc = __builtin_fmaf(e, e, acc);
     }
     return acc;
-}
-
-// The same with the scale given as its E4M3 code.
-__device__ __forceinline__ float sse8_rne(const float w[8], uint32_t sc, float sg, uint32_t& codes) {
-    const float s = e4m3_value(sc);
-    return sse8_rne(w, s, sc ? __fdiv_rn(1.0f, s * sg) : 0.0f, sg, codes);
 }
 
 __device__ __forceinline__ float sg_from_amax(float amax) {
@@ -389,11 +385,21 @@ constexpr float kRcp6 = 1.0f / 6.0f;     // RN(1/6)
 //    least about 2^-80.6).  Then every block whose code can be nonzero has normal
 //    operands and quotients, where the corrected division is exact; blocks with quotients
 //    below 2^-12 get code 0 either way.  Smaller tensor scales take the plain divisions;
-//  * the reciprocal of each of the 128 codes is computed once per workgroup into LDS.
+//  * the reciprocal of each of the 128 codes is computed once per workgroup into LDS;
+//  * the reciprocal is kept at binary32 precision where its exponent leaves binary32's
+//    range: when fl(s s_g) is below about 2^-128 (possible only when s_g < 2^-119), its
+//    reciprocal R overflows.  For such a copy (`tiny`, uniform) the table holds
+//    R 2^-64 = RN(1 / (fl(s s_g) 2^64)) for every code (the scalings are exact, and every
+//    entry and every nonzero scaled element x R 2^-64 is then a normal number), and the
+//    E2M1 conversions, which divide by the power of two given as their scale operand, take
+//    2^-64: the code is that of fl(x (R 2^-64)) 2^64 = fl(x R).  Where R is finite this is
+//    the binary32 product itself.
+constexpr float kTinyShift = 0x1p64f;
 struct CopyScale {
     float sg, rsg;
     bool fast;
     const float* rtab;
+    float cs;   // scale operand of the E2M1 conversions: 1, or 2^-64 for a tiny copy
     __device__ __forceinline__ uint32_t code(float am, float k, float rk) const {
         float z;
         if (fast)
@@ -403,7 +409,28 @@ struct CopyScale {
         return e4m3_encode(z);
     }
     __device__ __forceinline__ float rcp(uint32_t c) const { return rtab[c]; }
+    // The scaled values of 8 elements of a block with scale code c (see above); rscale is
+    // 1/4 where the rotation's factor is folded into the reciprocal (never in a tiny copy).
+    __device__ __forceinline__ void scale8(const float w[8], uint32_t c, float rscale,
+                                           float u[8]) const {
+        const float r = rtab[c] * rscale;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = w[e] * r;
+    }
 };
+
+// Whether the reciprocals of a copy with tensor scale sg leave binary32's range: that of
+// the smallest nonzero block scale 2^-9, the largest, is infinite.
+__device__ __forceinline__ bool tiny_scale(float sg) {
+    return __builtin_isinf(__fdiv_rn(1.0f, 0x1p-9f * sg));
+}
+// The E2M1 conversions' scale operand for a copy (see CopyScale).
+__device__ __forceinline__ float conv_scale(bool tiny) { return tiny ? 1.0f / kTinyShift : 1.0f; }
+// Table entry for scale code c (0 for the zero scale).
+__device__ __forceinline__ float recip_entry(uint32_t c, float sg, bool tiny) {
+    const float d = e4m3_value(c) * sg;
+    return c ? __fdiv_rn(1.0f, tiny ? d * kTinyShift : d) : 0.0f;
+}
 
 __device__ __forceinline__ float uniform_f(float v) {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
@@ -472,14 +499,14 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
         if (a.rowwise) *a.rsg = sg_r;
         if (a.colwise) *a.csg = sg_c;
     }
+    const bool tiny_r = tiny_scale(sg_r), tiny_c = tiny_scale(sg_c);
     if (t < 128) {
-        const float s = e4m3_value(t);
-        rtab[0][t] = t ? __fdiv_rn(1.0f, s * sg_r) : 0.0f;
-        rtab[1][t] = t ? __fdiv_rn(1.0f, s * sg_c) : 0.0f;
+        rtab[0][t] = recip_entry(t, sg_r, tiny_r);
+        rtab[1][t] = recip_entry(t, sg_c, tiny_c);
     }
     __syncthreads();
-    const CopyScale rsc{sg_r, __fdiv_rn(1.0f, sg_r), sg_r >= 0x1p-92f, rtab[0]};
-    const CopyScale csc{sg_c, __fdiv_rn(1.0f, sg_c), sg_c >= 0x1p-92f, rtab[1]};
+    const CopyScale rsc{sg_r, __fdiv_rn(1.0f, sg_r), sg_r >= 0x1p-92f, rtab[0], conv_scale(tiny_r)};
+    const CopyScale csc{sg_c, __fdiv_rn(1.0f, sg_c), sg_c >= 0x1p-92f, rtab[1], conv_scale(tiny_c)};
     const bool fold_r = RHT_ROW && !a.scale46 && sg_r >= 0x1p-92f && sg_r <= 0x1p110f;
     const bool fold_c = RHT_COL && !a.scale46 && sg_c >= 0x1p-92f && sg_c <= 0x1p110f;
     const uint32_t signs =
@@ -522,8 +549,11 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
                     // both lanes form the same (elements 0..7) + (elements 8..15) sum
                     const uint32_t sc4 = rsc.code(am, 4.0f, 0.25f);
                     uint32_t c6, c4;
-                    float e6 = sse8_rne(w, e4m3_value(scode), rsc.rcp(scode), sg_r, c6);
-                    float e4 = sse8_rne(w, e4m3_value(sc4), rsc.rcp(sc4), sg_r, c4);
+                    float u[8];
+                    rsc.scale8(w, scode, 1.0f, u);
+                    float e6 = sse8_rne(w, u, e4m3_value(scode), sg_r, rsc.cs, c6);
+                    rsc.scale8(w, sc4, 1.0f, u);
+                    float e4 = sse8_rne(w, u, e4m3_value(sc4), sg_r, rsc.cs, c4);
                     e6 += xor1(e6);
                     e4 += xor1(e4);
                     const bool use4 = e4 < e6;
@@ -532,13 +562,19 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
                     have = true;
                 }
             }
-            const float rcp = rsc.rcp(scode) * rscale;
             uint32_t codes;
-            if (!SR_ROW) {
-                codes = have ? rcodes : encode8_rne(w, rcp);
-            } else {
+            if (SR_ROW) {
                 const uint64_t g = ((uint64_t)(r0 + i) * (uint64_t)a.cols + (uint64_t)c0) >> 3;
-                codes = encode8_sr(w, rcp, sr_words(g, 0u, a.k0, a.k1));
+                const U4 rw = sr_words(g, 0u, a.k0, a.k1);
+                float u[8];
+                rsc.scale8(w, scode, rscale, u);
+                codes = encode8_sr(u, rw, rsc.cs);
+            } else if (!have) {
+                float u[8];
+                rsc.scale8(w, scode, rscale, u);
+                codes = encode8_rne(u, rsc.cs);
+            } else {
+                codes = rcodes;
             }
             if (valid) {
                 *(uint32_t*)(cbase + i * rpitch) = codes;
@@ -574,10 +610,16 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
                 if (a.scale46) {
                     const uint32_t sc4 = csc.code(am, 4.0f, 0.25f);
                     const float s6 = e4m3_value(scode), s4 = e4m3_value(sc4);
-                    const float q6 = csc.rcp(scode), q4 = csc.rcp(sc4);
                     uint32_t l6, h6, l4, h4;
-                    const float e6 = sse8_rne(&w[0], s6, q6, sg_c, l6) + sse8_rne(&w[8], s6, q6, sg_c, h6);
-                    const float e4 = sse8_rne(&w[0], s4, q4, sg_c, l4) + sse8_rne(&w[8], s4, q4, sg_c, h4);
+                    float u[8];
+                    csc.scale8(&w[0], scode, 1.0f, u);
+                    float e6 = sse8_rne(&w[0], u, s6, sg_c, csc.cs, l6);
+                    csc.scale8(&w[8], scode, 1.0f, u);
+                    e6 = e6 + sse8_rne(&w[8], u, s6, sg_c, csc.cs, h6);
+                    csc.scale8(&w[0], sc4, 1.0f, u);
+                    float e4 = sse8_rne(&w[0], u, s4, sg_c, csc.cs, l4);
+                    csc.scale8(&w[8], sc4, 1.0f, u);
+                    e4 = e4 + sse8_rne(&w[8], u, s4, sg_c, csc.cs, h4);
                     const bool use4 = e4 < e6;
                     scode = use4 ? sc4 : scode;
                     rlo = use4 ? l4 : l6;
@@ -585,15 +627,25 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
                     have = true;
                 }
             }
-            const float rcp = csc.rcp(scode) * rscale;
             uint32_t lo, hi;
-            if (!SR_COL) {
-                lo = have ? rlo : encode8_rne(&w[0], rcp);
-                hi = have ? rhi : encode8_rne(&w[8], rcp);
-            } else {
+            if (SR_COL) {
                 const uint64_t g = ((uint64_t)(c0 + j) * (uint64_t)a.rows + (uint64_t)r0) >> 3;
-                lo = encode8_sr(&w[0], rcp, sr_words(g, 1u, a.k0, a.k1));
-                hi = encode8_sr(&w[8], rcp, sr_words(g + 1, 1u, a.k0, a.k1));
+                float u[8];
+                const U4 rlo_w = sr_words(g, 1u, a.k0, a.k1);
+                csc.scale8(&w[0], scode, rscale, u);
+                lo = encode8_sr(u, rlo_w, csc.cs);
+                const U4 rhi_w = sr_words(g + 1, 1u, a.k0, a.k1);
+                csc.scale8(&w[8], scode, rscale, u);
+                hi = encode8_sr(u, rhi_w, csc.cs);
+            } else if (!have) {
+                float u[8];
+                csc.scale8(&w[0], scode, rscale, u);
+                lo = encode8_rne(u, csc.cs);
+                csc.scale8(&w[8], scode, rscale, u);
+                hi = encode8_rne(u, csc.cs);
+            } else {
+                lo = rlo;
+                hi = rhi;
             }
             const int cl = pc * 8 + j;
             ccodes_lds[cl][pr ^ pc] = make_uint2(lo, hi);

@@ -63,6 +63,7 @@ def _load():
                                                P, P]),
         "or_qadamw_v_encode": (ctypes.c_int, [P, i64, i64, u64, ctypes.c_int, P, P, P, P]),
         "or_qadamw_v_decode": (ctypes.c_int, [P, P, P, f32, i64, i64, u64, ctypes.c_int, P]),
+        "or_scale46_disagreements": (ctypes.c_int, [P, i64, i64, ctypes.c_int, u64, P, P, P]),
         "or_num_threads": (ctypes.c_int, []),
         "or_set_num_threads": (None, [ctypes.c_int]),
         "or_lora_down": (ctypes.c_int, [P, i64, i64, P, i64, f32, P, P, P]),
@@ -209,6 +210,22 @@ def quantize(x, rowwise=True, colwise=False, block2d=False, round_row=RNE, round
         col = quantize_rows(np.ascontiguousarray(x.T), block2d, round_col, rht_col, seed,
                             copy_id=1, scale46=scale46)
     return row, col
+
+
+def scale46_disagreements(x, rht=False, seed=0):
+    """For the rows of x (rotated when rht), the number of 1x16 blocks whose 4/6 choice
+    differs between the binary32 squared errors the method compares and the same errors in
+    binary64, and the number of blocks whose binary64 errors tie exactly (a measurement of
+    the evaluation-order convention, not part of the method), and the largest relative gap
+    |e4 - e6| / max(e4, e6) of the binary64 errors among the differing blocks."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    n, k = x.shape
+    differ, ties, gap = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_double(0.0)
+    _check(_load().or_scale46_disagreements(_ptr(x), n, k, int(rht), int(seed),
+                                            ctypes.byref(differ), ctypes.byref(ties),
+                                            ctypes.byref(gap)),
+           "scale46_disagreements")
+    return differ.value, ties.value, gap.value
 
 
 def dequantize(q):

@@ -242,6 +242,21 @@ static int all_finite(const float* x, int64_t count)
     return 1;
 }
 
+/* Element scaling u = |x| / (s s_g) ([FS4] sec. 2: x_hat = x_E2M1 s s_g).  Reading
+ * ([NVP] sec. 2, "reciprocal scale"): one correctly rounded reciprocal R of d = fl(s s_g) per
+ * block, kept at binary32 precision, and u = fl(|x| R).  Where R's exponent leaves binary32's
+ * range (d below about 2^-128, which needs a tensor maximum below about 2^-107), R is held
+ * as R 2^-64 = fl(1 / (d 2^64)): scaling d up by 2^64 is exact, and both that reciprocal
+ * (at most 2^85, as d >= 2^-149) and |x| R 2^-64 (at least 2^-85 for x != 0) are normal, so
+ * fl(|x| (R 2^-64)) 2^64 = fl(|x| R). */
+static float scale_element(float x, float d)
+{
+    float rcp = 1.0f / d;
+    if (!isinf(rcp))
+        return fabsf(x) * rcp;
+    return (fabsf(x) * (1.0f / (d * 0x1p64f))) * 0x1p64f;
+}
+
 /* 4/6 adaptive block scaling.  [FS4] sec. 3 (and the introduction's list of
  * primitives) applies "4/6 scaling" to every NVFP4 quantization and the related-work
  * paragraph describes it as MSE-optimal adaptive block scaling; the rule itself is not
@@ -258,15 +273,31 @@ static float block_sse_rne(const float* y, uint8_t scode, float sg)
 {
     float part[2] = {0.0f, 0.0f};
     float s = (float)or_e4m3_value(scode);
-    float rcp = scode ? 1.0f / (s * sg) : 0.0f;
     for (int i = 0; i < 16; ++i) {
-        int mag = scode ? or_e2m1_rne(fabsf(y[i]) * rcp) : 0;
+        int mag = scode ? or_e2m1_rne(scale_element(y[i], s * sg)) : 0;
         float v = (float)or_e2m1_value(mag);
         if (signbit(y[i])) v = -v;
         float e = fmaf(-(v * s), sg, y[i]);
         part[i / 8] = fmaf(e, e, part[i / 8]);
     }
     return part[0] + part[1];
+}
+
+/* Measurement, not part of the method: the same squared error in binary64 (each error
+ * y - v s s_g exact, its square and the sum rounded to 53 bits), to count how often the
+ * binary32 evaluation order above decides a 4/6 choice differently. */
+static double block_sse_f64(const float* y, uint8_t scode, float sg)
+{
+    double acc = 0.0;
+    float s = (float)or_e4m3_value(scode);
+    for (int i = 0; i < 16; ++i) {
+        int mag = scode ? or_e2m1_rne(scale_element(y[i], s * sg)) : 0;
+        double v = or_e2m1_value(mag);
+        if (signbit(y[i])) v = -v;
+        double e = (double)y[i] - v * (double)s * (double)sg;
+        acc += e * e;
+    }
+    return acc;
 }
 
 /* Quantize already-transformed values y[n][k]. */
@@ -316,9 +347,7 @@ static void quantize_core(const float* y, int64_t n, int64_t k, int block2d, int
             if (scode == 0) {
                 mag = 0;
             } else {
-                float d = (float)or_e4m3_value(scode) * sg;
-                float rcp = 1.0f / d;
-                float u = fabsf(x) * rcp;
+                float u = scale_element(x, (float)or_e4m3_value(scode) * sg);
                 if (rounding == 1)
                     mag = or_e2m1_sr(u, or_sr_bits(seed, copy_id, (uint64_t)(r * k + c)));
                 else
@@ -355,6 +384,57 @@ int or_quantize_rows(const float* x, int64_t n, int64_t k, int block2d, int roun
     memset(codes, 0, (size_t)(n * (k / 2)));
     quantize_core(y, n, k, block2d, rounding, scale46, seed, copy_id, codes, scales, sg);
     free(y);
+    return 0;
+}
+
+/* For the rows of x (rotated first when rht), the number of 1x16 blocks whose 4/6 choice
+ * differs between the binary32 evaluation of the squared errors (the method's) and their
+ * binary64 evaluation, and the number of blocks whose binary64 errors tie exactly. */
+int or_scale46_disagreements(const float* x, int64_t n, int64_t k, int rht, uint64_t seed,
+                             int64_t* differ, int64_t* ties64, double* max_gap)
+{
+    if (n < 0 || k < 0 || k % 16 != 0) return -2;
+    if (!all_finite(x, n * k)) return -8;
+    float* y = (float*)malloc(sizeof(float) * (size_t)(n * k > 0 ? n * k : 1));
+    if (!y) return -9;
+    memcpy(y, x, sizeof(float) * (size_t)(n * k));
+    if (rht) {
+        float sgn[16];
+        or_rht_signs(seed, sgn);
+        for (int64_t r = 0; r < n; ++r)
+            for (int64_t c = 0; c < k; c += 16)
+                or_rht16_forward(&y[r * k + c], sgn);
+    }
+    float amax_t = 0.0f;
+    for (int64_t i = 0; i < n * k; ++i)
+        if (fabsf(y[i]) > amax_t) amax_t = fabsf(y[i]);
+    float sg = amax_t / 2688.0f;
+    if (sg == 0.0f) sg = 1.0f;
+    int64_t nd = 0, nt = 0;
+    double gap = 0.0;   /* largest |e4 - e6| / max(e4, e6) (binary64) where the choices differ */
+    #pragma omp parallel for schedule(static) reduction(+:nd, nt) reduction(max:gap)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t b = 0; b < k / 16; ++b) {
+            const float* blk = &y[r * k + b * 16];
+            float amax_b = 0.0f;
+            for (int i = 0; i < 16; ++i)
+                if (fabsf(blk[i]) > amax_b) amax_b = fabsf(blk[i]);
+            uint8_t s6 = or_e4m3_encode((amax_b / 6.0f) / sg);
+            uint8_t s4 = or_e4m3_encode((amax_b / 4.0f) / sg);
+            int use4_32 = block_sse_rne(blk, s4, sg) < block_sse_rne(blk, s6, sg);
+            double e6 = block_sse_f64(blk, s6, sg), e4 = block_sse_f64(blk, s4, sg);
+            int use4_64 = e4 < e6;
+            if (use4_32 != use4_64) {
+                ++nd;
+                double g = fabs(e4 - e6) / (e4 > e6 ? e4 : e6);
+                if (g > gap) gap = g;
+            }
+            if (e4 == e6 && s4 != s6) ++nt;
+        }
+    free(y);
+    *differ = nd;
+    *ties64 = nt;
+    *max_gap = gap;
     return 0;
 }
 

@@ -137,6 +137,11 @@ int or_qadamw_step(float* w, const float* g, int64_t R, int64_t C,
                    uint16_t* mu_out, uint8_t* v_codes_out, uint8_t* v_scales_out, float* v_sg_out,
                    float* m_new_out, float* v_new_out);
 
+/* Measurement (not part of the method): blocks whose 4/6 choice differs between the binary32
+ * and the binary64 evaluation of the squared errors; exact binary64 ties; the largest relative
+ * gap between the two binary64 errors among the differing blocks. */
+int or_scale46_disagreements(const float* x, int64_t n, int64_t k, int rht, uint64_t seed,
+                             int64_t* differ, int64_t* ties64, double* max_gap);
 int or_num_threads(void);
 void or_set_num_threads(int n);
 

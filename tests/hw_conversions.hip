@@ -13,6 +13,9 @@
 //    floor(frac * 2^16) + r16 >= 2^16" (frac: the position between the two grid
 //    neighbours, in binary64; saturation at 6, sign copied).  Every finite binary32 with a
 //    hashed r16, and every r16 for the multiples of 1/256 in [0, 8) of both signs.
+//  * The same two E2M1 conversions with the scale operand 2^-64 (which the kernels pass for
+//    tensors whose block-scale reciprocals leave binary32's range) against the conversion
+//    of x 2^64 at scale 1.0, for every finite binary32 x with |x| < 2^64 (x 2^64 exact).
 // Nothing here is shared with the library's kernels.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -103,15 +106,34 @@ __global__ void k_check_sr_thresholds(unsigned long long* bad, uint32_t* first) 
         *first = __float_as_uint(x);
 }
 
-// Runs the checks; returns 0 and fills counts[0..2] (mismatches: E4M3, E2M1 nearest-even,
-// E2M1 stochastic) and first[0..2] (first mismatching input bits), or a HIP error code.
+// every finite x with |x| < 2^64: the conversions at scale 2^-64 equal those of x 2^64 at 1.0
+__global__ void k_check_scaled(uint64_t lo, uint32_t n, unsigned long long* bad, uint32_t* first) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t bits = (uint32_t)(lo + i);
+    if (((bits >> 23) & 0xFFu) >= 127u + 64u) return;    // |x| >= 2^64, inf and NaN
+    const float x = __uint_as_float(bits);
+    const float xs = x * 0x1p64f;                         // exact
+    const uint32_t rne = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x, 0.0f, 0x1p-64f, 0) & 0xFu;
+    const uint32_t rne1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, xs, 0.0f, 1.0f, 0) & 0xFu;
+    const uint32_t r16 = (bits * 0x9E3779B1u) >> 16;
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 p = {x, 0.0f}, ps = {xs, 0.0f};
+    const uint32_t sr = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, r16 << 16, 0x1p-64f, 0) & 0xFFu;
+    const uint32_t sr1 = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, ps, r16 << 16, 1.0f, 0) & 0xFFu;
+    if ((rne != rne1 || sr != sr1) && atomicAdd(bad, 1ull) == 0ull) *first = bits;
+}
+
+// Runs the checks; returns 0 and fills counts[0..3] (mismatches: E4M3, E2M1 nearest-even,
+// E2M1 stochastic, the two E2M1 conversions at scale 2^-64) and first[0..3] (first
+// mismatching input bits), or a HIP error code.
 extern "C" int hwcheck_run(unsigned long long* counts, uint32_t* first) {
     unsigned long long* d_bad = nullptr;
     uint32_t* d_first = nullptr;
-    if (hipMalloc(&d_bad, 3 * sizeof(unsigned long long)) != hipSuccess) return 1;
-    if (hipMalloc(&d_first, 3 * sizeof(uint32_t)) != hipSuccess) return 1;
-    (void)hipMemset(d_bad, 0, 3 * sizeof(unsigned long long));
-    (void)hipMemset(d_first, 0, 3 * sizeof(uint32_t));
+    if (hipMalloc(&d_bad, 4 * sizeof(unsigned long long)) != hipSuccess) return 1;
+    if (hipMalloc(&d_first, 4 * sizeof(uint32_t)) != hipSuccess) return 1;
+    (void)hipMemset(d_bad, 0, 4 * sizeof(unsigned long long));
+    (void)hipMemset(d_first, 0, 4 * sizeof(uint32_t));
     const uint32_t chunk = 1u << 28;
     const uint32_t nonneg = 0x7F800000u;   // every non-negative finite pattern
     for (uint32_t lo = 0; lo < nonneg; lo += chunk) {
@@ -123,9 +145,11 @@ extern "C" int hwcheck_run(unsigned long long* counts, uint32_t* first) {
     for (uint64_t lo = 0; lo < (1ull << 32); lo += chunk)
         k_check_sr_all<<<chunk / 256, 256>>>(lo, chunk, d_bad + 2, d_first + 2);
     k_check_sr_thresholds<<<(1u << 28) / 256, 256>>>(d_bad + 2, d_first + 2);
+    for (uint64_t lo = 0; lo < (1ull << 32); lo += chunk)
+        k_check_scaled<<<chunk / 256, 256>>>(lo, chunk, d_bad + 3, d_first + 3);
     int rc = hipDeviceSynchronize() == hipSuccess ? 0 : 2;
-    (void)hipMemcpy(counts, d_bad, 3 * sizeof(unsigned long long), hipMemcpyDeviceToHost);
-    (void)hipMemcpy(first, d_first, 3 * sizeof(uint32_t), hipMemcpyDeviceToHost);
+    (void)hipMemcpy(counts, d_bad, 4 * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+    (void)hipMemcpy(first, d_first, 4 * sizeof(uint32_t), hipMemcpyDeviceToHost);
     (void)hipFree(d_bad);
     (void)hipFree(d_first);
     return rc;

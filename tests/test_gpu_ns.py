@@ -5,18 +5,25 @@ nvfp4_gemm_axpby: C = alpha A B^T + beta D with oracle-quantized operands; toler
 |C - (alpha C64 + beta D)| <= 1e-5 (|alpha| sum_k |a b| + |beta d|) per element, as the
 plain GEMM's plus the one rounding of beta d.
 
-nvfp4_ns_step: the quantize stages are bit-exact on oracle inputs (the quantize tests); the
-whole iteration feeds GEMM outputs (FP32, accumulated in another order than the oracle's
-binary64) into the next quantization, so an element at a rounding boundary can take the
-neighbouring code.  The check: relative Frobenius distance between the GPU's and the
-oracle's X' at most 2e-3 (well below the step's NVFP4 error of several percent), and both
-equally close to the exact (unquantized) step.
+nvfp4_ns_step, stage by stage: the step leaves its intermediates in the workspace (at the
+offsets include/nvfp4.h documents), and each stage is checked against the oracle on the
+GPU's own input to that stage -- qX, qX' bit-exact from X; A against the binary64 product
+of qX at the GEMM tolerance (the triangle split-K path for m a multiple of 256); qA, qA'
+bit-exact from the GPU's A; B against b A + c qA qA' (binary64) at the alpha/beta GEMM
+tolerance; qB bit-exact from the GPU's B; X' against a X + qB qX' likewise.  The full-size
+3072 x 9216 step is checked the same way on sampled entries plus full rows and columns.
+
+The whole iteration, run separately on the oracle, feeds its own binary64 GEMM outputs into
+the next quantization, so an element at a rounding boundary can take the neighbouring code;
+end to end the two are compared through the relative Frobenius distance of X' (at most
+2e-3, well below the step's NVFP4 error of several percent), both equally close to the
+exact (unquantized) step.
 """
 import numpy as np
 import pytest
 import torch
 
-from gpu_util import dev, to_gpu_qtensor
+from gpu_util import GEMM_TOL, assert_copy_equal, dev, to_gpu_qtensor
 
 pytestmark = pytest.mark.gpu
 
@@ -111,3 +118,116 @@ def test_ns_full_size_orthogonalises(nv):
     gram = (x @ x.T - torch.eye(3072, device=dev())).abs().max().item()
     print(f"  max |X X^T - I|: {gram0:.3f} -> {gram:.3f}")
     assert gram0 > 0.5 and gram < 0.25
+
+
+# ------------------------------------------------------------------ stage by stage
+def al256(n):
+    return (n + 255) & ~255
+
+
+def ns_intermediates(nv, ws, m, n):
+    """The intermediates nvfp4_ns_step leaves in its workspace, in the documented order:
+    qX, qX', A, qA, qA', B, qB, each piece 256-byte aligned after the previous one."""
+    off = 0
+
+    def take(nbytes):
+        nonlocal off
+        t = ws[off:off + nbytes]
+        off += al256(nbytes)
+        return t
+
+    def copy(r, c):
+        codes = take(r * c // 2).view(r, c // 2)
+        scales = take(r * c // 16).view(r, c // 16)
+        return nv.QTensor(codes, scales, take(4).view(torch.float32))
+
+    qx, qxc = copy(m, n), copy(n, m)
+    A = take(m * m * 4).view(torch.float32).view(m, m)
+    qa, qac = copy(m, m), copy(m, m)
+    B = take(m * m * 4).view(torch.float32).view(m, m)
+    qb = copy(m, m)
+    return qx, qxc, A, qa, qac, B, qb
+
+
+def check_product(what, got, ref, absdot, extra):
+    """|got - ref| <= GEMM_TOL (sum |a b| + |extra|) per entry (ref and the bound in
+    binary64), and the relative Frobenius error at most GEMM_TOL."""
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
+    bound = GEMM_TOL * (absdot + np.abs(extra)) + 1e-30
+    fro = np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-300)
+    print(f"  {what}: max err/bound {np.max(err / bound):.3f}, frobenius {fro:.2e}")
+    assert np.all(err <= bound), f"{what}: {(err > bound).sum()} entries outside the bound"
+    assert fro <= GEMM_TOL
+
+
+def run_stagewise(nv, oracle, x, abc, seed, sampled):
+    a, b, c = abc
+    m, n = x.shape
+    ws = torch.empty(nv.load_library().nvfp4_ns_step_workspace_bytes(m, n), dtype=torch.uint8,
+                     device=dev())
+    xg = torch.from_numpy(x.copy()).to(dev())
+    nv.nvfp4_ns_step(xg, a, b, c, seed=seed, workspace=ws)
+    torch.cuda.synchronize()
+    qx, qxc, A, qa, qac, B, qb = ns_intermediates(nv, ws, m, n)
+    rng = np.random.default_rng(seed)
+
+    def entries(rows, cols):
+        if not sampled:
+            return None
+        em = list(rng.integers(0, rows, 4096)) + [0] * cols + [rows - 1] * cols + list(range(rows)) * 2
+        en = list(rng.integers(0, cols, 4096)) + list(range(cols)) * 2 + [0] * rows + [cols - 1] * rows
+        return np.array(em), np.array(en)
+
+    def product(qa_, qb_, idx):
+        if idx is None:
+            return oracle.gemm_f64(qa_, qb_)
+        return oracle.gemm_f64_entries(qa_, qb_, *idx)
+
+    def pick(t, idx):
+        t = t.cpu().numpy() if isinstance(t, torch.Tensor) else t
+        return t if idx is None else t[idx]
+
+    # qX, qX' from X
+    oqx, oqxc = oracle.quantize(x, rowwise=True, colwise=True, rht_row=True, rht_col=True,
+                                seed=seed, scale46=True)
+    assert_copy_equal(qx, oqx, "qX")
+    assert_copy_equal(qxc, oqxc, "qX'")
+    # A = qX qX^T
+    idx = entries(m, m)
+    P, ad = product(oqx, oqx, idx)
+    check_product("A", pick(A, idx), P, ad, 0.0)
+    # qA, qA' from the GPU's A
+    A_np = A.cpu().numpy()
+    oqa, oqac = oracle.quantize(A_np, rowwise=True, colwise=True, rht_row=True, rht_col=True,
+                                seed=seed, scale46=True)
+    assert_copy_equal(qa, oqa, "qA")
+    assert_copy_equal(qac, oqac, "qA'")
+    # B = b A + c qA qA'
+    P, ad = product(oqa, oqac, idx)
+    bA = np.float64(np.float32(b)) * pick(A_np, idx).astype(np.float64)
+    check_product("B", pick(B, idx), np.float64(np.float32(c)) * P + bA, abs(c) * ad, bA)
+    # qB from the GPU's B
+    oqb, _ = oracle.quantize(B.cpu().numpy(), rowwise=True, rht_row=True, seed=seed, scale46=True)
+    assert_copy_equal(qb, oqb, "qB")
+    # X' = a X + qB qX'
+    idx = entries(m, n)
+    P, ad = product(oqb, oqxc, idx)
+    aX = np.float64(np.float32(a)) * pick(x, idx).astype(np.float64)
+    check_product("X'", pick(xg, idx), P + aX, ad, aX)
+
+
+# (64, 192): A by the plain GEMM; (256, 1024) and (512, 2048): A on the triangle tiles with K
+# split into 2 and 4 parts, reduced and mirrored
+@pytest.mark.parametrize("m,n", [(64, 192), (256, 1024), (512, 2048)])
+@pytest.mark.parametrize("abc", [(1.5, -0.5, 0.0), (2.0, -1.5, 0.5)])
+def test_ns_step_stagewise(nv, oracle, m, n, abc):
+    print(f"ns_step stage by stage {m}x{n} coefficients {abc}", flush=True)
+    run_stagewise(nv, oracle, wide(m, n, 7 * m + n), abc, 0x5EED4 + m, sampled=False)
+
+
+def test_ns_step_stagewise_full_size(nv, oracle):
+    """W_up's wide orientation 3072 x 9216: A by the triangle split-K path; every stage on
+    4096 sampled entries plus two full rows and two full columns."""
+    print("ns_step stage by stage full-size 3072x9216", flush=True)
+    run_stagewise(nv, oracle, wide(3072, 9216, 12), (2.0, -1.5, 0.5), 0x5EED7, sampled=True)

@@ -107,6 +107,21 @@ def test_step_tiny_second_moments(nv, oracle):
     check_step(nv, oracle, w, g, qm, mu, qv, 0x53520300, False)
 
 
+@pytest.mark.parametrize("gscale", [1e-36, 1e-41])
+def test_step_tiny_first_moments(nv, oracle, gscale):
+    """Every gradient scaled to about 1e-36 (1e-41: subnormal) from the zero state: the new
+    first moment's tensor scale is so small that the reciprocals of its small block scales
+    leave binary32's range (the extended-range reciprocal), and its elements are tiny."""
+    R, C = 64, 256
+    z = np.zeros((R, C), dtype=np.float32)
+    qm = oracle.quantize_rows(z, rounding=oracle.SR, seed=1, scale46=True)
+    mu, qv = oracle.qadamw_v_encode(z, seed=V_SEED)
+    w = np.random.default_rng(14).standard_normal((R, C)).astype(np.float32)
+    g = (grad(R, C, 15, False).astype(np.float64) * gscale).astype(np.float32)
+    g[3, 16:32] *= np.float32(1e-4)                  # blocks with much smaller scales
+    check_step(nv, oracle, w, g, qm, mu, qv, 0x53520500, False)
+
+
 def test_step_full_size(nv, oracle):
     from nvfp4_block_scaled_quantize_amd import synthetic
     R, C = 9216, 3072                      # the FFN weight's state, log-normal v as for Q-AdamW

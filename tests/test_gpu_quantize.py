@@ -57,6 +57,11 @@ MODES = {
                          scale46=True),
     "46_all": dict(rowwise=True, colwise=True, round_row=1, round_col=1, rht_row=True,
                    rht_col=True, scale46=True),
+    # both copies rotated, nearest-even (the Newton-Schulz quantization of X and A), with and
+    # without 4/6 scaling; the rowwise-rotated copy alone with 4/6 (its quantization of B)
+    "rht_both": dict(rowwise=True, colwise=True, rht_row=True, rht_col=True),
+    "46_rht_both": dict(rowwise=True, colwise=True, rht_row=True, rht_col=True, scale46=True),
+    "46_rht_row": dict(rowwise=True, rht_row=True, scale46=True),
 }
 SHAPES = [(16, 16), (48, 80), (128, 256), (272, 400), (528, 144)]
 
@@ -87,6 +92,24 @@ def test_quantize_matches_oracle(nv, oracle, dtype, shape, mode):
     seed = 0x1234 + shape[0] * 7 + shape[1]
     x = make_input(shape, seed, dtype)
     run_case(nv, oracle, x, mode, 0x5EED0000 + seed)
+
+
+# Tensor scales at the edges of the kernels' arithmetic shortcuts: s_g < 2^-92 takes the plain
+# divisions for the block scales; s_g > 2^110 (or < 2^-92) keeps the rotation's factor 1/4
+# out of the element reciprocal; below that the element reciprocal of small block scales
+# overflows binary32 and the elements are divided by the scale instead; 2^-130 makes every
+# input subnormal.  The largest input 2^125 keeps every butterfly sum below 2^128.
+EXTREME_MODES = ["rowcol", "rht_row", "wgrad_x", "rht_both", "dgrad_and_wgrad", "all",
+                 "46_rowcol", "46_rht_both", "46_all"]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("log2_amax", [125, -85, -100, -110, -120, -130])
+@pytest.mark.parametrize("mode", EXTREME_MODES)
+def test_extreme_tensor_scales(nv, oracle, dtype, log2_amax, mode):
+    x = make_input((272, 400), 0x3E3 + log2_amax, torch.float32)
+    x = x / x.abs().max() * 2.0 ** log2_amax
+    run_case(nv, oracle, x.to(dtype), mode, 0x5EED0000 + log2_amax)
 
 
 def test_rne_ties_and_neighbours(nv, oracle):

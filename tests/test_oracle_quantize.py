@@ -104,17 +104,40 @@ def test_zero_and_negative_zero_tensor(oracle):
     assert np.all(oracle.dequantize(row) == 0.0)
 
 
-def test_rne_reconstruction_error_is_half_a_step(oracle):
+# log2 of the tensor maximum: None keeps 3 N(0,1); 125 is near the top of binary32; from
+# -110 down the reciprocal of small block scales overflows binary32 (the elements are then
+# divided by the scale), and at -130 every input is subnormal
+@pytest.mark.parametrize("log2_amax", [None, 125, -100, -110, -120, -130])
+def test_rne_reconstruction_error_is_half_a_step(oracle, log2_amax):
     rng = np.random.default_rng(11)
     x = rng.standard_normal((32, 128)).astype(np.float32) * 3
+    x[5, 16:32] = 0.0
+    x[6, 17] = -0.0
+    x[7, 32:48] *= 1e-5          # blocks whose E4M3 scale is small or subnormal
+    x[8, 48:64] *= 4e-6
+    x[9, 64:80] *= 3e-5
+    if log2_amax is not None:
+        x = (x.astype(np.float64) / np.abs(x).max() * 2.0 ** log2_amax).astype(np.float32)
     row, _ = oracle.quantize(x)
     deq = dequant64(oracle, row)
-    d = np.repeat(scale_value(row.scales), 16, axis=1) * row.sg
-    u = np.abs(x) / d
+    s = np.repeat(scale_value(row.scales), 16, axis=1)
+    d64 = s * np.float64(row.sg)                                   # exact s s_g
+    d32 = (s.astype(np.float32) * np.float32(row.sg)).astype(np.float64)   # binary32 fl(s s_g)
+    u = np.abs(x) / np.where(d32 > 0, d32, 1.0)
     pos = np.array([oracle.e2m1_value(c) for c in range(8)])
     step = np.interp(u, pos[:-1], np.diff(pos), right=2.0)
-    # half a local step of the grid times the block's decode scale (+ scale-rounding slack)
-    assert np.all(np.abs(deq - x) <= (step / 2 * d) * 1.01 + 1e-12)
+    # half a local step of the grid (or the overshoot past 6 where a rounded-down scale
+    # saturates) times the block's decode scale, plus the roundings of the scaled element
+    # and of fl(s s_g) (the latter only matters where it is subnormal)
+    err = np.abs(deq - x)
+    bound = (np.maximum(step / 2, u - 6) + 6 * 2.0 ** -23) * d32 * 1.0001 + 6 * np.abs(d32 - d64)
+    nz = s > 0
+    assert np.all(err[nz] <= bound[nz])
+    # a zero block scale: (amax_b / 6) / s_g rounded to E4M3 below half its smallest step 2^-9
+    assert np.all(deq[~nz] == 0)
+    # (amax_b / 6 is rounded once in binary32, by at most 2^-150 where it is subnormal)
+    assert np.all(np.abs(x[~nz]) <= 6 * (2.0 ** -10 * np.float64(row.sg) * 1.0001 + 2.0 ** -150))
+    assert np.all(deq[x == 0] == 0)                                # zeros stay zero
 
 
 def test_dequantize_matches_independent_decode(oracle):
