@@ -550,11 +550,40 @@ def main():
         "kernels": kernels,
     }
 
+    out["qadamw_v_error"] = qadamw_error(nv, torch, v, v_out)
     out["kernels_isolated"] = isolated(torch, dev, calls, work, stream)
     out["extras"] = extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, synthetic, ffn)
     print(json.dumps(out))
+
+
+def qadamw_error(nv, torch, v, v_hat):
+    """Reconstruction error of the Q-AdamW second moment (v 9216 x 3072, the step's GPU
+    encode and decode) beside direct NVFP4 1x16 RNE quantization of the same v (GPU
+    quantize and dequantize): Rel. MSE = MSE(v - v_hat) / mean(v^2) (Full-Stack FP4 sec. 3.2's
+    definition), the median, 99th percentile and mean of |v_hat - v| / v, the fraction of
+    elements decoded as 0, and the Rel. MSE of sqrt(v), the quantity the update divides by.
+    Measurement only (binary64 on the device), outside the timed region."""
+    q, _ = nv.nvfp4_quantize(v, nv.quant_params(rowwise=True))
+    v_direct = nv.nvfp4_dequantize(q)
+    v64 = v.double().flatten()
+    n = v64.numel()
+
+    def metrics(vh):
+        vh = vh.double().flatten()
+        e = vh - v64
+        rel = (e.abs() / v64).sort().values
+        se = vh.clamp(min=0).sqrt() - v64.sqrt()
+        return {"rel_mse": float((e * e).mean() / (v64 * v64).mean()),
+                "median_rel_err": float(rel[n // 2]),
+                "p99_rel_err": float(rel[min(n - 1, (99 * n) // 100)]),
+                "mean_rel_err": float(rel.mean()),
+                "zero_fraction": float((vh == 0).double().mean()),
+                "rel_mse_sqrt_v": float((se * se).mean() / v64.mean())}
+
+    return {"workload": "v fp32 9216x3072 log-normal exp(-18 + 3 N(0,1))",
+            "pipeline": metrics(v_hat), "direct_nvfp4": metrics(v_direct)}
 
 
 def isolated(torch, dev, calls, work, stream, reps=10):
