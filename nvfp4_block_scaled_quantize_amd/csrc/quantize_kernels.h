@@ -464,34 +464,31 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
     const bool valid = r0 < a.rows && c0 < a.cols;
     const int half = pc & 1;
 
-    // the patch loads go out first and land while the tensor scales are formed
-    Patch<IN> P;
-    load_patch(P, a, r0, c0, valid);
-
-    // LoRA-SVD down-projection: T = BF16(beta * sum of the K-part partials, in part order)
-    if (a.lora_t) {
-        const int64_t total = a.rows * a.lora_r;
-        for (int64_t e = (int64_t)blockIdx.x * kThreads + t; e < total;
-             e += (int64_t)gridDim.x * kThreads) {
-            float sum = 0.0f;
-            for (int q = 0; q < a.lora_parts; ++q) sum += a.lora_part[q * total + e];
-            a.lora_t[e] = (uint16_t)f32_to_bf16_rne(sum * a.lora_beta);
-        }
+    // A first round of the partial maxima (up to 768 per copy, three per thread) is loaded
+    // before the patch: vector loads complete in issue order, so the wait for these leaves
+    // the patch loads in flight, and the rowwise encode below can start on the first rows of
+    // the patch while the later ones are still arriving.
+    float pmr[3], pmc[3];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+        const int i = min(t + kThreads * u, a.npart - 1);
+        pmr[u] = a.partial[i];
+        pmc[u] = a.partial[a.npart + i];
     }
+    // A lane past the tensor's edge (whole 16-row groups and 8-column halves of whole 16-column
+    // blocks, so its pair and its column blocks are past it too) encodes the tensor's first
+    // patch and stores nothing.  Its loads are not skipped: a branch around them would make
+    // the compiler wait for all of them before the first use of the partials.
+    Patch<IN> P;
+    load_patch(P, a, valid ? r0 : 0, valid ? c0 : 0, true);
 
-    // tensor scales from the per-tile partial maxima; a round's loads (4 per copy) are all
-    // issued before any is used
-    float mr = 0.0f, mc = 0.0f;
-    for (int i0 = t; i0 < a.npart; i0 += 4 * kThreads) {
-        float pr[4], pc[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = i0 + u * kThreads;
-            pr[u] = i < a.npart ? a.partial[i] : 0.0f;
-            pc[u] = i < a.npart ? a.partial[a.npart + i] : 0.0f;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) { mr = fmaxf(mr, pr[u]); mc = fmaxf(mc, pc[u]); }
+    // tensor scales from the per-tile partial maxima: the first round loaded above (indices
+    // past the last partial read the last one again, which leaves the maximum unchanged),
+    // then any beyond 768 (the LoRA first pass can have more workgroups)
+    float mr = fmaxf(fmaxf(pmr[0], pmr[1]), pmr[2]), mc = fmaxf(fmaxf(pmc[0], pmc[1]), pmc[2]);
+    for (int i = t + 3 * kThreads; i < a.npart; i += kThreads) {
+        mr = fmaxf(mr, a.partial[i]);
+        mc = fmaxf(mc, a.partial[a.npart + i]);
     }
     block_max2(mr, mc, red);
     const float sg_r = uniform_f(sg_from_amax(mr)), sg_c = uniform_f(sg_from_amax(mc));
@@ -511,6 +508,19 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
     const bool fold_c = RHT_COL && !a.scale46 && sg_c >= 0x1p-92f && sg_c <= 0x1p110f;
     const uint32_t signs =
         (RHT_ROW || RHT_COL) ? __builtin_amdgcn_readfirstlane(rht_sign_bits(a.k0, a.k1)) : 0u;
+
+    // LoRA-SVD down-projection: T = BF16(beta * sum of the K-part partials, in part order)
+    // (after the tensor scales, so that this uniform branch does not stand between the
+    // loads above and their first use)
+    if (a.lora_t) {
+        const int64_t total = a.rows * a.lora_r;
+        for (int64_t e = (int64_t)blockIdx.x * kThreads + t; e < total;
+             e += (int64_t)gridDim.x * kThreads) {
+            float sum = 0.0f;
+            for (int q = 0; q < a.lora_parts; ++q) sum += a.lora_part[q * total + e];
+            a.lora_t[e] = (uint16_t)f32_to_bf16_rne(sum * a.lora_beta);
+        }
+    }
 
     uint32_t scode2d = 0;
     if (a.block2d) {  // one scale per 16x16 tile = this patch and its neighbour's
