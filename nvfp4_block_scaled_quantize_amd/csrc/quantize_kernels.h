@@ -143,30 +143,62 @@ template <> struct Patch<0> {
     }
 };
 
-// A rowwise NVFP4 copy decoded to binary32, fl(fl(v s) s_g) (v s is exact): the input of
-// the columnwise copy in Full-Stack FP4 eq. (2), Q_16x1(H^T Q_1x16(X)).  A patch row's 8
-// columns are one 4-byte group of codes inside one 16-element block.
-template <> struct Patch<2> : Patch<0> {
+// A rowwise NVFP4 copy, the input of the columnwise copy in Full-Stack FP4 eq. (2),
+// Q_16x1(H^T Q_1x16(X)).  A patch row's 8 columns are one 4-byte group of codes inside one
+// 16-element block; the patch keeps those code words and the rows' block scales (32 VGPRs)
+// and decodes an element where it is used: fl(fl(v s) s_g), v s being exact.
+template <> struct Patch<2> {
+    uint32_t p[16];   // 8 E2M1 codes per row, element e in bits 4e..4e+3
+    float s[16];      // the row's block scale
+    float sg;         // the copy's tensor scale
     __device__ __forceinline__ void load_q(const QArgs& a, int64_t r0, int64_t c0, bool valid) {
+        sg = *a.in_sg;
         if (!valid) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) p[i][e] = 0.0f;
+            for (int i = 0; i < 16; ++i) { p[i] = 0u; s[i] = 0.0f; }
             return;
         }
-        const float sg = *a.in_sg;
         const int64_t cp = a.cols / 2, sp = a.cols / 16;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const uint32_t w = *(const uint32_t*)(a.in_codes + (r0 + i) * cp + c0 / 2);
-            const float s = e4m3_value(a.in_scales[(r0 + i) * sp + c0 / 16]);
-            const float2v q0 = fp4x2_to_f32<0>(w), q1 = fp4x2_to_f32<1>(w);
-            const float2v q2 = fp4x2_to_f32<2>(w), q3 = fp4x2_to_f32<3>(w);
-            const float v[8] = {q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) p[i][e] = (v[e] * s) * sg;
+            p[i] = *(const uint32_t*)(a.in_codes + (r0 + i) * cp + c0 / 2);
+            s[i] = e4m3_value(a.in_scales[(r0 + i) * sp + c0 / 16]);
         }
+    }
+    // the two decoded codes of byte k of row i (k a constant once the callers' loops unroll)
+    __device__ __forceinline__ float2v pair(int i, int k) const {
+        switch (k) {
+            case 0: return fp4x2_to_f32<0>(p[i]);
+            case 1: return fp4x2_to_f32<1>(p[i]);
+            case 2: return fp4x2_to_f32<2>(p[i]);
+            default: return fp4x2_to_f32<3>(p[i]);
+        }
+    }
+    __device__ __forceinline__ float at(int i, int e) const {
+        const float2v q = pair(i, e >> 1);
+        return ((e & 1) ? q.y : q.x) * s[i] * sg;
+    }
+    // negating a decoded value is flipping its code's sign bit (bit 3 of the nibble)
+    __device__ __forceinline__ void flip(int i, int h, uint32_t m) {   // m as for bfloat16
+        p[i] ^= (((m >> 15) & 1u) << (8 * h + 3)) | ((m >> 31) << (8 * h + 7));
+    }
+    static __device__ __forceinline__ uint32_t pair_mask(uint32_t b_even, uint32_t b_odd) {
+        return (b_even << 15) | (b_odd << 31);
+    }
+    // max |x|: per row from the largest decoded |v| (x -> fl(fl(x s) s_g) is monotone)
+    __device__ __forceinline__ float amax() const {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float r = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float2v q = pair(i, k);
+                r = fmaxf(r, fmaxf(fabsf(q.x), fabsf(q.y)));
+            }
+            m = fmaxf(m, r * s[i] * sg);
+        }
+        return m;
     }
 };
 
@@ -216,6 +248,18 @@ __device__ __forceinline__ uint32_t col_sign_mask(uint32_t signs, int i) {
 template <int IN>
 __device__ __forceinline__ void flip_signs(Patch<IN>& P, uint32_t signs, int half, bool rows,
                                            bool cols) {
+    if constexpr (IN == 2) {   // one XOR per code word: the row signs' nibbles, then column i's
+        const uint32_t rs = rows ? (signs >> (half * 8)) & 0xFFu : 0u;
+        uint32_t rmask = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rmask |= ((rs >> e) & 1u) << (4 * e + 3);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t cm = cols ? ((signs >> i) & 1u) * 0x88888888u : 0u;
+            P.p[i] ^= rmask ^ cm;
+        }
+        return;
+    }
     uint32_t rm[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) rm[h] = rows ? row_sign_mask<IN>(signs, half, h) : 0u;
@@ -436,6 +480,14 @@ __device__ __forceinline__ float uniform_f(float v) {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
 
+// Tile of workgroup b of n (a bijection of 0..n-1): XCD b mod 8 takes the contiguous run
+// of tiles that ends where the next XCD's begins, visited from its end.
+__device__ __forceinline__ int xcd_tile(int b, int n) {
+    const int x = b & 7, k = b >> 3, q = n >> 3, rem = n & 7;
+    const int start = x * q + min(x, rem), len = q + (x < rem ? 1 : 0);
+    return start + len - 1 - k;
+}
+
 // Specialised on the input dtype and on F: bit 0 rowwise SR, bit 1 columnwise SR,
 // bit 2 rowwise Hadamard, bit 3 columnwise Hadamard.
 //
@@ -455,40 +507,67 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
     __shared__ float rtab[2][128];                        // element reciprocal per scale code
     __shared__ float red[8];
     const int t = threadIdx.x, pc = t & 15, pr = t >> 4;
-    // tiles in reverse order: the first reads are of the rows the amax pass read last, the
-    // likeliest still to be cached (1-3% on inputs that are not cache-resident)
-    const int tb = gridDim.x - 1 - blockIdx.x;
+    // Workgroups go to the 8 XCDs in turn (workgroup b to XCD b mod 8), each with its own L2.
+    // XCD x is given one contiguous run of tiles (ceil or floor of n/8), so that the tiles of
+    // one tile row, whose rowwise codes (64 of each 128 bytes) and scales (8 of each 128)
+    // share cache lines, are written through one L2.  Within a run the tiles go in reverse
+    // order: the first reads are of the rows the amax pass read last, the likeliest still to
+    // be cached.
+    const int tb = xcd_tile(blockIdx.x, gridDim.x);
     const int tile_r = tb / a.tiles_c, tile_c = tb % a.tiles_c;
     const int64_t r0 = (int64_t)tile_r * kTileRows + pr * 16;
     const int64_t c0 = (int64_t)tile_c * kTileCols + pc * 8;
     const bool valid = r0 < a.rows && c0 < a.cols;
     const int half = pc & 1;
 
-    // A first round of the partial maxima (up to 768 per copy, three per thread) is loaded
-    // before the patch: vector loads complete in issue order, so the wait for these leaves
-    // the patch loads in flight, and the rowwise encode below can start on the first rows of
-    // the patch while the later ones are still arriving.
-    float pmr[3], pmc[3];
-#pragma unroll
-    for (int u = 0; u < 3; ++u) {
-        const int i = min(t + kThreads * u, a.npart - 1);
-        pmr[u] = a.partial[i];
-        pmc[u] = a.partial[a.npart + i];
-    }
-    // A lane past the tensor's edge (whole 16-row groups and 8-column halves of whole 16-column
-    // blocks, so its pair and its column blocks are past it too) encodes the tensor's first
-    // patch and stores nothing.  Its loads are not skipped: a branch around them would make
-    // the compiler wait for all of them before the first use of the partials.
     Patch<IN> P;
-    load_patch(P, a, valid ? r0 : 0, valid ? c0 : 0, true);
-
-    // tensor scales from the per-tile partial maxima: the first round loaded above (indices
-    // past the last partial read the last one again, which leaves the maximum unchanged),
-    // then any beyond 768 (the LoRA first pass can have more workgroups)
-    float mr = fmaxf(fmaxf(pmr[0], pmr[1]), pmr[2]), mc = fmaxf(fmaxf(pmc[0], pmc[1]), pmc[2]);
-    for (int i = t + 3 * kThreads; i < a.npart; i += kThreads) {
-        mr = fmaxf(mr, a.partial[i]);
-        mc = fmaxf(mc, a.partial[a.npart + i]);
+    float mr, mc;
+    if constexpr (!RHT_ROW) {
+        // A first round of the partial maxima (up to 768 per copy, three per thread) is loaded
+        // before the patch: vector loads complete in issue order, so the wait for these leaves
+        // the patch loads in flight, and the rowwise encode below can start on the first rows
+        // of the patch while the later ones are still arriving.
+        float pmr[3], pmc[3];
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int i = min(t + kThreads * u, a.npart - 1);
+            pmr[u] = a.partial[i];
+            pmc[u] = a.partial[a.npart + i];
+        }
+        // A lane past the tensor's edge (whole 16-row groups and 8-column halves of whole
+        // 16-column blocks, so its pair and its column blocks are past it too) encodes the
+        // tensor's first patch and stores nothing.  Its loads are not skipped: a branch around
+        // them would make the compiler wait for all of them before the first use of the
+        // partials.
+        load_patch(P, a, valid ? r0 : 0, valid ? c0 : 0, true);
+        // tensor scales from the per-tile partial maxima: the first round loaded above
+        // (indices past the last partial read the last one again, which leaves the maximum
+        // unchanged), then any beyond 768 (the LoRA first pass can have more workgroups)
+        mr = fmaxf(fmaxf(pmr[0], pmr[1]), pmr[2]);
+        mc = fmaxf(fmaxf(pmc[0], pmc[1]), pmc[2]);
+        for (int i = t + 3 * kThreads; i < a.npart; i += kThreads) {
+            mr = fmaxf(mr, a.partial[i]);
+            mc = fmaxf(mc, a.partial[a.npart + i]);
+        }
+    } else {
+        // With the rowwise rotation the whole patch is sign-flipped before the first row is
+        // encoded, so nothing starts before the last patch load: the patch goes first and the
+        // partials (four loads per copy issued together) after it, the order that needs the
+        // fewest registers here.  A lane past the edge loads nothing and stores nothing.
+        load_patch(P, a, r0, c0, valid);
+        mr = 0.0f;
+        mc = 0.0f;
+        for (int i0 = t; i0 < a.npart; i0 += 4 * kThreads) {
+            float pr[4], pc[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * kThreads;
+                pr[u] = i < a.npart ? a.partial[i] : 0.0f;
+                pc[u] = i < a.npart ? a.partial[a.npart + i] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) { mr = fmaxf(mr, pr[u]); mc = fmaxf(mc, pc[u]); }
+        }
     }
     block_max2(mr, mc, red);
     const float sg_r = uniform_f(sg_from_amax(mr)), sg_c = uniform_f(sg_from_amax(mc));
@@ -522,12 +601,14 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
         }
     }
 
+    // A rowwise NVFP4 input (IN == 2) asks for the columnwise 1-D copy alone.
+    constexpr bool kRowsOrTiles = IN != 2;
     uint32_t scode2d = 0;
-    if (a.block2d) {  // one scale per 16x16 tile = this patch and its neighbour's
+    if (kRowsOrTiles && a.block2d) {  // one scale per 16x16 tile = this patch and its neighbour's
         scode2d = rsc.code(pair_max(P.amax()), 6.0f, kRcp6);
     }
 
-    if (a.rowwise) {
+    if (kRowsOrTiles && a.rowwise) {
         if (RHT_ROW) flip_signs<IN>(P, signs, half, true, false);
         const float sgn = half ? -1.0f : 1.0f;
         const int64_t rpitch = a.cols / 2, spitch = a.cols / 16;
