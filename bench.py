@@ -512,7 +512,7 @@ def main():
     q_ms = sum(kernels[n]["ms"] for n in q_names)
     up = kernels["gemm_ffn_up"]
     up_flops = work["gemm_ffn_up"][2]
-    roofline = {"bound": "mfma", "kernel": "k_gemm_dma (FFN-up 8192x9216x3072)",
+    roofline = {"bound": "mfma", "kernel": "k_gemm_sk (FFN-up 8192x9216x3072)",
                 "achieved": up["TFLOP/s"], "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(up["TFLOP/s"] / PEAK_F16_TFLOPS, 4),
                 "traffic": counters_for("gemm_ffn_up", "gemm")}

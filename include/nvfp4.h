@@ -35,9 +35,10 @@
  *     2^-107) it is carried as R 2^-64 with the 2^64 restored in the E2M1 conversion.
  *     The GEMM's stated accuracy assumes s_gA s_gB is a normal binary32.
  *   - Calls on one stream are ordered.  The library holds no state apart from the
- *     scratch array of nvfp4_quantize_noalloc, so calls on different streams may run
- *     concurrently on distinct buffers (except two nvfp4_quantize_noalloc calls on one
- *     device).
+ *     scratch array of nvfp4_quantize_noalloc and the hand-off flags of nvfp4_gemm's
+ *     balanced schedule (one 64-bit word per workgroup and device, tagged per launch), so
+ *     calls on different streams may run concurrently on distinct buffers (except two
+ *     nvfp4_quantize_noalloc calls on one device; concurrent GEMMs stay correct).
  *
  * Quantized tensor layout (one "copy"): an n x k matrix quantized along its
  * rows has
@@ -202,7 +203,13 @@ int nvfp4_dequantize(const nvfp4_qtensor* q, int64_t n, int64_t k, int out_dtype
  * stored for the GEMM).  Every product of a decoded element and its block scale is
  * exact in binary16, so the only rounding is the FP32 accumulation.
  * K must be a multiple of 16; M and N any size >= 0; codes 16-byte aligned with row pitch
- * K/2 a multiple of 16 bytes (K % 32 == 0), C 4-byte aligned. */
+ * K/2 a multiple of 16 bytes (K % 32 == 0), C 4-byte aligned.
+ * Schedule: 256 x 256 output tiles, one workgroup per compute unit at a time.  When the
+ * last round of tiles would keep at most half the units busy (and K > 128), each of its
+ * tiles is split into two K halves computed by two workgroups and summed as
+ * fl(head + tail) of the two FP32 partial accumulations; the tail half is parked in the
+ * tile's own region of C meanwhile.  Results are bitwise reproducible on a given device
+ * (they depend on its compute-unit count through this split). */
 int nvfp4_gemm(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
                int64_t K, float* c, int64_t ldc, void* stream);
 

@@ -41,6 +41,9 @@
 #include "nvfp4.h"
 #include "device_common.h"
 
+#include <atomic>
+#include <cstdlib>
+
 namespace nvfp4 {
 
 constexpr int GBM = 256, GBN = 256, GBK = 128;  // GBK in elements: 64 bytes of codes per row
@@ -74,6 +77,15 @@ struct GArgs {
     float alpha, beta;
     float* part;          // EpiPart: [kparts][triangle tiles][256][256] raw accumulators
     int kparts;
+    // balanced schedule, k_gemm_sk: whole rounds, remaining tiles (each split in two K
+    // halves), K stages per tile; launch epoch tagging the hand-off flags; longest wait for a
+    // hand-off (wall-clock ticks); sk_test != 0 makes every tail half skip its hand-off (so
+    // that the head computes it itself; for tests)
+    int sk_rounds, sk_rem;
+    int sk_nst;
+    uint64_t sk_epoch;
+    uint64_t sk_spin;
+    int sk_test;
 };
 
 // Epilogue variants: plain product; plus the LoRA-SVD low-rank term; alpha * product +
@@ -194,23 +206,50 @@ __device__ __forceinline__ void mma_stage(const Frags& f, float16v (&acc)[4][4])
 // the caches cut the FFN-up GEMM from 508 to 433 us on this part.  One block row
 // (32 rows) at a time, with a scheduling fence between block rows, so the compiler does
 // not pull all 256 accumulators into VGPRs at once.
-__device__ __forceinline__ void store_tile(const GArgs& g, const float16v (&acc)[4][4], int64_t m0,
+// ADD: each element first adds the raw partial sum that the same position of C holds (the
+// other K half of a tile split by the balanced schedule), fl(acc + p), before the scaling.
+// A block row's 64 partials are loaded before any of its stores: a load issued after
+// stores can only be waited for together with them.  FULL: the tile lies inside C, so no
+// element needs a bounds test (a test per element becomes a branch, and the compiler waits
+// for every outstanding store at each branch's end).
+template <bool ADD, bool FULL>
+__device__ __forceinline__ void store_rows(const GArgs& g, const float16v (&acc)[4][4], int64_t m0,
                                            int64_t n0, int wm, int wn, int h, int li, float scale) {
     const int64_t rbase = m0 + wm * 128 + 4 * h, cbase = n0 + wn * 128 + li;
-    const bool full = m0 + GBM <= g.M && n0 + GBN <= g.N;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        float pv[16][4];
+        if constexpr (ADD) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+                const float* rowp = g.c + row * g.ldc + cbase;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    pv[r][j] = (FULL || (row < g.M && cbase + j * 32 < g.N)) ? rowp[j * 32] : 0.0f;
+            }
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
             float* rowp = g.c + row * g.ldc + cbase;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (full || (row < g.M && cbase + j * 32 < g.N))
-                    __builtin_nontemporal_store(acc[i][j][r] * scale, rowp + j * 32);
+                if (FULL || (row < g.M && cbase + j * 32 < g.N)) {
+                    float x = acc[i][j][r];
+                    if constexpr (ADD) x = x + pv[r][j];
+                    __builtin_nontemporal_store(x * scale, rowp + j * 32);
+                }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+template <bool ADD = false>
+__device__ __forceinline__ void store_tile(const GArgs& g, const float16v (&acc)[4][4], int64_t m0,
+                                           int64_t n0, int wm, int wn, int h, int li, float scale) {
+    if (m0 + GBM <= g.M && n0 + GBN <= g.N) store_rows<ADD, true>(g, acc, m0, n0, wm, wn, h, li, scale);
+    else store_rows<ADD, false>(g, acc, m0, n0, wm, wn, h, li, scale);
 }
 
 // The raw accumulators of the tile into its 256 x 256 slot of the partial buffer (row-major),
@@ -323,8 +362,10 @@ __device__ __forceinline__ bf16x8v lds_frag(const uint8_t* lds, int which, int r
                                                         row * kLoraLdsRow + ((ch ^ (row & 7)) << 4)));
 }
 
+// add: as for store_tile, the partial held in C is added before the scaling.
 __device__ __forceinline__ void lora_epilogue(const GArgs& g, uint8_t* lds, float16v (&acc)[4][4],
-                                              int64_t m0, int64_t n0, int wm, int wn, int h, int li) {
+                                              int64_t m0, int64_t n0, int wm, int wn, int h, int li,
+                                              bool add = false) {
     const float scale = *g.asg * *g.bsg;
     const int ra = wm * 128 + li, rb = wn * 128 + li;
     for (int64_t k0 = 0; k0 < g.lr; k0 += kLoraChunk) {
@@ -333,12 +374,21 @@ __device__ __forceinline__ void lora_epilogue(const GArgs& g, uint8_t* lds, floa
         stage_lora(g, lds, m0, n0, k0, kc);
         __syncthreads();
         if (k0 == 0) {
+            const int64_t rbase = m0 + wm * 128 + 4 * h, cbase = n0 + wn * 128 + li;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] * scale;
+                    for (int r = 0; r < 16; ++r) {
+                        float x = acc[i][j][r];
+                        if (add) {
+                            const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+                            const int64_t col = cbase + j * 32;
+                            if (row < g.M && col < g.N) x = x + g.c[row * g.ldc + col];
+                        }
+                        acc[i][j][r] = x * scale;
+                    }
         }
         // per 16 rank entries: the wave's 4 A and 4 B fragments, then its 16 products
         for (int s = 0; s < kc; s += 16) {
@@ -381,19 +431,28 @@ __device__ __forceinline__ void store_tile_axpby(const GArgs& g, const float16v 
 }
 
 // The epilogue variant is a compile-time switch so that the plain kernels keep their
-// register allocation.
+// register allocation.  mode (the balanced schedule's; every other caller takes 1):
+// 0 the raw accumulators into C (a K half parked for the other half's workgroup), 1 the
+// tile's result, 2 the result of the accumulators plus the half parked in C, 3 NaN (the
+// parked half was lost).
+enum { FinPark = 0, FinResult = 1, FinAdd = 2, FinNan = 3 };
 template <int EPI>
 __device__ __forceinline__ void finish_tile(const GArgs& g, uint8_t* lds, float16v (&acc)[4][4],
-                                            int64_t m0, int64_t n0, int wm, int wn, int h, int li) {
+                                            int64_t m0, int64_t n0, int wm, int wn, int h, int li,
+                                            int mode = FinResult) {
+    const float nan = __builtin_nanf("");
     if constexpr (EPI == EpiLora) {
-        lora_epilogue(g, lds, acc, m0, n0, wm, wn, h, li);
-        store_tile(g, acc, m0, n0, wm, wn, h, li, 1.0f);
+        if (mode == FinResult || mode == FinAdd)
+            lora_epilogue(g, lds, acc, m0, n0, wm, wn, h, li, mode == FinAdd);
+        store_tile(g, acc, m0, n0, wm, wn, h, li, mode == FinNan ? nan : 1.0f);
     } else if constexpr (EPI == EpiAxpby) {
         store_tile_axpby(g, acc, m0, n0, wm, wn, h, li);
     } else if constexpr (EPI == EpiPart) {
         store_part(g.part + ((int64_t)blockIdx.x << 16), acc, wm, wn, h, li);
     } else {
-        store_tile(g, acc, m0, n0, wm, wn, h, li, *g.asg * *g.bsg);
+        const float scale = mode == FinPark ? 1.0f : (mode == FinNan ? nan : *g.asg * *g.bsg);
+        if (mode == FinAdd) store_tile<true>(g, acc, m0, n0, wm, wn, h, li, scale);
+        else store_tile(g, acc, m0, n0, wm, wn, h, li, scale);
     }
 }
 
@@ -705,16 +764,57 @@ __device__ __forceinline__ void piped_stage(const DmaCtx& c, int s, HalfFrags& l
     for (int x = 0; x < 4; ++x) { sa[x] = nsa[x]; sb[x] = nsb[x]; }
 }
 
+// Stages [c.s0, c.s0 + c.nst) of the tile at (c.m0, c.n0), c.nst >= 1, added onto acc: the
+// first three stages' direct loads, then the pipelined stages.  On return every direct load
+// has landed and every wave has passed the last stage's barrier; LDS holds nothing needed.
+__device__ __forceinline__ void run_stages(const DmaCtx& c, float16v (&acc)[4][4]) {
+    const int pre = c.nst < kDmaStages ? c.nst : kDmaStages;
+    for (int j = 0; j < pre; ++j)
+        dma_stage(c.g, c.rs, c.lds0 + j * kStageBytes, c.m0, c.n0, c.s0 + j, c.t, c.wid, c.kbytes,
+                  c.kblocks);
+    wait_meet(pre - 1);
+    HalfFrags lo, hi;
+    uint32_t sa[4], sb[4];
+    Pairs p;
+    half8v av[4], bv[4];
+    read_half(c.lds, 0, c.wm, c.wn, c.h, c.li, lo);
+    read_half(c.lds, 1, c.wm, c.wn, c.h, c.li, hi);
+    read_scales(c.lds, c.wm, c.wn, c.h, c.li, sa, sb);
+    make_pairs<0>(sa, sb, p);
+    decode_slot<0>(lo, p, av, bv);
+    for (int s = 0; s < c.nst; ++s) piped_stage(c, s, lo, hi, sa, sb, p, av, bv, acc);
+}
+
+// The thread's lane coordinates from its index t.
+__device__ __forceinline__ void set_lanes(DmaCtx& c, int t) {
+    c.t = t;
+    const int lane = t & 63;
+    c.wid = __builtin_amdgcn_readfirstlane(t >> 6);
+    c.wm = c.wid >> 1;
+    c.wn = c.wid & 1;
+    c.h = lane >> 5;
+    c.li = lane & 31;
+}
+
+// The per-workgroup constants of the direct path (tile and K range set by the caller).
+__device__ __forceinline__ void init_ctx(DmaCtx& c, const GArgs& g, uint8_t* lds) {
+    c.g = g;
+    set_lanes(c, threadIdx.x);
+    c.kbytes = (uint32_t)(g.K / 2);
+    c.kblocks = (uint32_t)(g.K / 16);
+    c.rs.ac = make_rsrc(g.ac, (uint32_t)(g.M * c.kbytes));
+    c.rs.bc = make_rsrc(g.bc, (uint32_t)(g.N * c.kbytes));
+    c.rs.as = make_rsrc(g.as, (uint32_t)(g.M * c.kblocks));
+    c.rs.bs = make_rsrc(g.bs, (uint32_t)(g.N * c.kblocks));
+    c.lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+    c.lds = lds;
+}
+
 template <int EPI>
 __global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     DmaCtx c;
-    c.g = g;
-    c.t = threadIdx.x;
-    const int lane = c.t & 63;
-    c.wid = __builtin_amdgcn_readfirstlane(c.t >> 6);
-    c.wm = c.wid >> 1;
-    c.wn = c.wid & 1;
+    init_ctx(c, g, lds);
     int tm, tn;
     const int nst_all = (int)((g.K + GBK - 1) / GBK);
     c.s0 = 0;
@@ -731,35 +831,199 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
     }
     c.m0 = (int64_t)tm * GBM;
     c.n0 = (int64_t)tn * GBN;
-    c.h = lane >> 5;
-    c.li = lane & 31;
-    c.kbytes = (uint32_t)(g.K / 2);
-    c.kblocks = (uint32_t)(g.K / 16);
-    c.rs.ac = make_rsrc(g.ac, (uint32_t)(g.M * c.kbytes));
-    c.rs.bc = make_rsrc(g.bc, (uint32_t)(g.N * c.kbytes));
-    c.rs.as = make_rsrc(g.as, (uint32_t)(g.M * c.kblocks));
-    c.rs.bs = make_rsrc(g.bs, (uint32_t)(g.N * c.kblocks));
-    c.lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
-    c.lds = lds;
 
     float16v acc[4][4];
     zero_acc(acc);
-    const int pre = c.nst < kDmaStages ? c.nst : kDmaStages;
-    for (int j = 0; j < pre; ++j)
-        dma_stage(g, c.rs, c.lds0 + j * kStageBytes, c.m0, c.n0, c.s0 + j, c.t, c.wid, c.kbytes,
-                  c.kblocks);
-    wait_meet(pre - 1);
-    HalfFrags lo, hi;
-    uint32_t sa[4], sb[4];
-    Pairs p;
-    half8v av[4], bv[4];
-    read_half(lds, 0, c.wm, c.wn, c.h, c.li, lo);
-    read_half(lds, 1, c.wm, c.wn, c.h, c.li, hi);
-    read_scales(lds, c.wm, c.wn, c.h, c.li, sa, sb);
-    make_pairs<0>(sa, sb, p);
-    decode_slot<0>(lo, p, av, bv);
-    for (int s = 0; s < c.nst; ++s) piped_stage(c, s, lo, hi, sa, sb, p, av, bv, acc);
+    run_stages(c, acc);
     finish_tile<EPI>(g, lds, acc, c.m0, c.n0, c.wm, c.wn, c.h, c.li);
+}
+
+// ---------------------------------------------------------------- balanced schedule
+// With T = q G + r tiles (0 < r <= G/2) and G resident workgroups (one per CU; the direct
+// path's LDS allows no second), a grid of one workgroup per tile ends with a round in which
+// at most half the CUs work (384 tiles on 256 CUs: two rounds for 1.5 of work), and every CU
+// writes its tile of C at the same moment.  k_gemm_sk runs the q whole rounds as before
+// (workgroup v takes tile j G + v in round j, so each XCD's L2 serves a compact block of
+// neighbouring tiles) and splits each of the r remaining tiles into two K halves: workgroup
+// 2i+1 computes the tail stages [h, nst) of tile q G + i first thing, workgroup 2i its head
+// stages [0, h) last thing.  (Workgroups numbered 2r and up have no half.)  The tail's raw
+// accumulators go into the tile's own region of C and a flag marks them ready; the head adds
+// them to its accumulators (one binary32 addition per element) and runs the epilogue,
+// overwriting them.  Workgroup v is numbered XCD-major from blockIdx (workgroups go to the 8
+// XCDs in turn), so both halves of a tile and each round's 32 tiles per XCD share an L2.
+//
+// Hand-off flags: one 64-bit word per workgroup number in g_sk_flag, tagged with the
+// launch's epoch E (distinct per launch on a device): 4E+3 the tail is writing its part,
+// 4E+1 the part is in C, 4E+2 the head has claimed the tile.  The tail reserves (compare and
+// swap from anything but 4E+2) before it writes; the head waits for 4E+1 at most
+// g.sk_spin wall-clock ticks, then claims (compare and swap from anything but 4E+3) and
+// computes the tail stages itself, after parking its own part in C.  Either way C gets
+// fl(head + tail) of the same two partial sums, bit for bit.  A tail that finds the tile
+// claimed writes nothing.  Concurrent launches on one device may overwrite each other's
+// flags; that only sends a head to the fallback.  Every wait is bounded.  The last user of a
+// flag in a launch clears it (the head once it has seen the part, the tail once it has seen
+// the claim), so replays of one captured launch, which share its epoch, start from neutral
+// flags; a launch whose hand-off timed out (kSkWriteTicks) may leave one set.
+constexpr int kSkMaxGroups = 1024;
+__device__ uint64_t g_sk_flag[kSkMaxGroups];
+constexpr uint64_t kSkWriteTicks = 100000000ull;   // 1 s at 100 MHz: a reserved tail must publish
+
+__device__ __forceinline__ int sk_virtual(int b, int G) {   // G % 8 == 0
+    return (b & 7) * (G >> 3) + (b >> 3);
+}
+
+// Tile id -> (tm, tn): groups of kGroupRows tile rows, column by column within a group.
+__device__ __forceinline__ void grouped_tile(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int group = id / (kGroupRows * tiles_n);
+    const int first = group * kGroupRows;
+    const int rows = tiles_m - first < kGroupRows ? tiles_m - first : kGroupRows;
+    const int in = id - group * kGroupRows * tiles_n;
+    tm = first + in % rows;
+    tn = in / rows;
+}
+
+// Tail side: reserve the hand-off (1) unless the head has claimed the tile (0).  The caller
+// then writes the part and publishes it.
+__device__ __forceinline__ int sk_reserve(const DmaCtx& c, int v, int* bcast) {
+    const uint64_t E = c.g.sk_epoch;
+    if (c.t == 0) {
+        int ok = 0;
+        if (!c.g.sk_test) {
+            uint64_t cur = __hip_atomic_load(&g_sk_flag[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int tries = 0; tries < 64 && cur != 4 * E + 2; ++tries)
+                if (__hip_atomic_compare_exchange_strong(&g_sk_flag[v], &cur, 4 * E + 3, __ATOMIC_RELAXED,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                    ok = 1;
+                    break;
+                }
+            // claimed: the head is done with the flag, and this is its last use in the launch
+            if (!ok && cur == 4 * E + 2)
+                __hip_atomic_store(&g_sk_flag[v], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        *bcast = ok;
+    }
+    __syncthreads();
+    const int ok = *bcast;
+    __syncthreads();
+    return ok;
+}
+
+// Head side: 1 the tail's part is in C, 2 the tile is claimed (compute the tail here), 0 the
+// tail reserved the tile and did not publish within kSkWriteTicks (cannot happen while the
+// workgroups are resident; the tile is then left as NaN).
+__device__ __forceinline__ int sk_await(const DmaCtx& c, int w, int* bcast) {
+    const uint64_t E = c.g.sk_epoch;
+    if (c.t == 0) {
+        int res = 0;
+        const uint64_t t0 = (uint64_t)wall_clock64();
+        for (;;) {
+            uint64_t cur = __hip_atomic_load(&g_sk_flag[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (cur == 4 * E + 1) {
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // pairs with the tail's release
+                // the tail is done with the flag: clear it, so that a replay of this launch
+                // (same epoch, as in a captured graph) starts from a neutral flag
+                __hip_atomic_store(&g_sk_flag[w], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                res = 1;
+                break;
+            }
+            const uint64_t dt = (uint64_t)wall_clock64() - t0;
+            if (dt > c.g.sk_spin) {
+                if (cur != 4 * E + 3) {
+                    if (__hip_atomic_compare_exchange_strong(&g_sk_flag[w], &cur, 4 * E + 2, __ATOMIC_RELAXED,
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                        res = 2;
+                        break;
+                    }
+                    continue;
+                }
+                if (dt > c.g.sk_spin + kSkWriteTicks) break;
+            }
+            __builtin_amdgcn_s_sleep(4);
+        }
+        *bcast = res;
+    }
+    __syncthreads();
+    const int res = *bcast;
+    __syncthreads();
+    return res;
+}
+
+// One segment per pass of the loop below, so that the pipelined stages, the transfers and
+// the epilogue appear once in the code (a second copy of the stages pushes the accumulators
+// out of registers).  Roles: a whole tile; a tail half (published); a head half (waits for
+// the tail); the tail stages computed by a head that claimed the tile (after which the
+// parked head half is added).
+enum { SkWhole = 0, SkTail = 1, SkHead = 2, SkFallback = 3 };
+
+// Segment `idx` of workgroup v: false past the last.
+__device__ __forceinline__ bool sk_segment(const GArgs& g, int v, int G, int idx, int& tile, int& k0,
+                                           int& k1, int& role) {
+    const int q = g.sk_rounds, r = g.sk_rem, nst = g.sk_nst, h = nst / 2;
+    const bool half = v < 2 * r, tail = half && (v & 1), head = half && !(v & 1);
+    if (tail) {
+        if (idx == 0) { tile = q * G + (v >> 1); k0 = h; k1 = nst; role = SkTail; return true; }
+        --idx;
+    }
+    if (idx < q) { tile = idx * G + v; k0 = 0; k1 = nst; role = SkWhole; return true; }
+    if (head && idx == q) { tile = q * G + (v >> 1); k0 = 0; k1 = h; role = SkHead; return true; }
+    return false;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(GThreads, 1) void k_gemm_sk(GArgs g) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    __shared__ int bcast;
+    DmaCtx c;
+    init_ctx(c, g, lds);
+    const int G = gridDim.x, v = sk_virtual(blockIdx.x, G), nst = g.sk_nst;
+    int idx = 0, role = -1, tile = 0, k0 = 0, k1 = 0;
+    for (;;) {
+        if (role != SkFallback) {
+            if (!sk_segment(g, v, G, idx++, tile, k0, k1, role)) break;
+            int tm, tn;
+            grouped_tile(tile, g.tiles_m, g.tiles_n, tm, tn);
+            c.m0 = (int64_t)tm * GBM;
+            c.n0 = (int64_t)tn * GBN;
+            c.s0 = k0;
+            c.nst = k1 - k0;
+        } else {
+            c.s0 = k1;
+            c.nst = nst - k1;
+        }
+        __syncthreads();   // the previous segment's epilogue is done with LDS
+        // Per-thread values are derived afresh for each segment: hoisted out of this loop,
+        // the stages' address arithmetic stays live through the epilogue, where it spills,
+        // and each spill reload waits for all of the tile's outstanding C stores.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        set_lanes(c, tid);
+        float16v acc[4][4];
+        zero_acc(acc);
+        run_stages(c, acc);
+        // the accumulators are touched only by finish_tile, as in k_gemm_dma: any other
+        // vector arithmetic on them splits them between register files and spills
+        int mode = FinResult, next = -1, publish = 0;
+        if (role == SkTail) {
+            publish = sk_reserve(c, v, &bcast);
+            mode = publish ? FinPark : -1;
+        } else if (role == SkHead) {
+            const int res = sk_await(c, v + 1, &bcast);
+            if (res == 1) mode = FinAdd;
+            else if (res == 2) { mode = FinPark; next = SkFallback; }
+            else mode = FinNan;
+        } else if (role == SkFallback) {
+            mode = FinAdd;
+        }
+        if (mode >= 0) finish_tile<EPI>(g, lds, acc, c.m0, c.n0, c.wm, c.wn, c.h, c.li, mode);
+        if (mode == FinPark) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part has landed
+            __syncthreads();
+            if (publish && c.t == 0)
+                __hip_atomic_store(&g_sk_flag[v], 4 * g.sk_epoch + 1, __ATOMIC_RELEASE,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        role = next;
+    }
 }
 
 // C = s_gA s_gB (P_0 + P_1 + ...) over the K-parts, in part order, for the upper-triangle
@@ -835,6 +1099,12 @@ int syrk_splitk(const nvfp4_qtensor* a, int64_t m, int64_t k, float* c, int64_t 
     g.d = nullptr; g.ldd = 0; g.alpha = 1.0f; g.beta = 0.0f;
     g.part = part;
     g.kparts = kparts;
+    g.sk_rounds = 0;
+    g.sk_rem = 0;
+    g.sk_nst = 0;
+    g.sk_epoch = 0;
+    g.sk_spin = 0;
+    g.sk_test = 0;
     const int T = (int)(m / GBM), ntri = T * (T + 1) / 2;
     g.tiles_m = T;
     g.tiles_n = T;
@@ -850,6 +1120,39 @@ int syrk_splitk(const nvfp4_qtensor* a, int64_t m, int64_t k, float* c, int64_t 
 }  // namespace nvfp4
 
 using namespace nvfp4;
+
+// Balanced schedule settings, for tests and measurements: NVFP4_GEMM_SK=0 keeps one
+// workgroup per tile; NVFP4_GEMM_SK_SPIN sets the head's wait for a tail part (wall-clock
+// ticks, 100 MHz; default 20 ms); NVFP4_GEMM_SK_TEST=1 makes every tail skip its hand-off
+// so that every split tile takes the head's fallback.
+static int env_int(const char* name, int dflt) {
+    const char* e = getenv(name);
+    return e && *e ? atoi(e) : dflt;
+}
+
+// Workgroups of the balanced schedule on the current device: its compute units rounded down
+// to a multiple of 8 (the XCD-major numbering needs whole rounds of 8), 0 if unknown.
+static int sk_groups(int* dev_out) {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cache[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+    *dev_out = dev;
+    int g = cache[dev].load();
+    if (g == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+        g = cus & ~7;
+        if (g > kSkMaxGroups) g = kSkMaxGroups;
+        cache[dev].store(g > 0 ? g : -1);
+    }
+    return g > 0 ? g : 0;
+}
+
+static uint64_t next_epoch(int dev) {
+    static std::atomic<uint64_t> epoch[64];
+    return epoch[dev & 63].fetch_add(1) + 1;
+}
 
 static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
                        int64_t K, float* c, int64_t ldc, const uint16_t* lt, const uint16_t* lb,
@@ -881,6 +1184,12 @@ static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M
     g.beta = beta;
     g.part = nullptr;
     g.kparts = 1;
+    g.sk_rounds = 0;
+    g.sk_rem = 0;
+    g.sk_nst = 0;
+    g.sk_epoch = 0;
+    g.sk_spin = 0;
+    g.sk_test = 0;
     const int epi = d ? EpiAxpby : (lr > 0 ? EpiLora : EpiPlain);
     const int64_t tiles_m = (M + GBM - 1) / GBM, tiles_n = (N + GBN - 1) / GBN;
     g.tiles_m = (int)tiles_m;
@@ -901,6 +1210,26 @@ static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M
                             direct ? kGemmDmaLds : kGemmLds) != hipSuccess)
         return NVFP4_ERR_HIP;
     hipStream_t st = (hipStream_t)stream;
+    // balanced schedule (plain epilogue): a last round at most half full and at least two K
+    // stages per tile.  The axpby epilogue keeps one workgroup per tile (D may be C, which
+    // holds the tail halves), and so does the low-rank one (in this loop its epilogue spills
+    // and runs slower than the rounds it saves)
+    int dev = 0;
+    const int G = direct && epi == EpiPlain && env_int("NVFP4_GEMM_SK", 1) ? sk_groups(&dev) : 0;
+    const int sk_nst = (int)((K + GBK - 1) / GBK), sk_rem = G > 0 ? (int)(grid % G) : 0;
+    if (G > 0 && sk_rem > 0 && 2 * sk_rem <= G && sk_nst >= 2) {
+        if (hipFuncSetAttribute((const void*)k_gemm_sk<EpiPlain>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kGemmDmaLds) != hipSuccess)
+            return NVFP4_ERR_HIP;
+        g.sk_nst = sk_nst;
+        g.sk_rounds = (int)(grid / G);
+        g.sk_rem = sk_rem;
+        g.sk_epoch = next_epoch(dev);
+        g.sk_spin = (uint64_t)env_int("NVFP4_GEMM_SK_SPIN", 2000000);
+        g.sk_test = env_int("NVFP4_GEMM_SK_TEST", 0);
+        k_gemm_sk<EpiPlain><<<G, GThreads, kGemmDmaLds, st>>>(g);
+        return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+    }
     if (direct) {
         if (epi == EpiAxpby) k_gemm_dma<EpiAxpby><<<grid, GThreads, kGemmDmaLds, st>>>(g);
         else if (epi == EpiLora) k_gemm_dma<EpiLora><<<grid, GThreads, kGemmDmaLds, st>>>(g);
