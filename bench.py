@@ -234,8 +234,9 @@ def counter_summary(dirs):
 
 def mfma_summary(d):
     """Write profiles/gemm_mfma_busy.txt from a rocprofv3 --pmc GRBM_GUI_ACTIVE
-    SQ_VALU_MFMA_BUSY_CYCLES --kernel-trace folder of `bench.py --steps 1 --warmup 0
-    --no-cpu-baseline`: per GEMM call of the step, the duration under counter collection, the
+    SQ_VALU_MFMA_BUSY_CYCLES --kernel-trace folder of `bench.py --steps 1 --warmup 1
+    --no-cpu-baseline`: per GEMM call of the last step (the first one also pays the process's
+    first launches), the duration under counter collection, the
     effective clock (GRBM_GUI_ACTIVE over the eight XCDs / duration) and the fraction of SIMD
     cycles the matrix cores were busy (SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles))."""
     import csv
@@ -253,13 +254,13 @@ def mfma_summary(d):
     lines = ["# Matrix-core busy fraction and effective clock of the step's GEMMs (rocprofv3 --pmc)",
              "# commands (from the repository root, cd /tmp && TMPDIR=/tmp first):",
              "#   rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES --kernel-trace --output-format csv \\",
-             "#       -d <m> -o bench -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
-             "#   python3 bench.py --mfma-summary <m>",
+             "#       -d <m> -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+             "#   python3 bench.py --mfma-summary <m>   (the last of the two steps)",
              "# clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs",
              "# x GRBM_GUI_ACTIVE / 8); durations are longer than uncounted ones (collection overhead)",
              f"# {'call':16s} {'kernel':28s} {'us':>8s} {'clock_GHz':>10s} {'mfma_busy':>10s}"]
     kinds = dict(STEP_ORDER)
-    for key, idx in split_step([name[k] for k in ids])[:len(STEP_ORDER)]:
+    for key, idx in split_step([name[k] for k in ids])[-len(STEP_ORDER):]:
         if kinds[key] != "gemm":
             continue
         for i in idx:
