@@ -522,6 +522,11 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
 
     Patch<IN> P;
     float mr, mc;
+    // A rowwise NVFP4 input has a 32-VGPR patch, so its columnwise SR words (64 VGPRs) can be
+    // formed up front, overlapping the Philox chains with the load latency; the bf16 and f32
+    // patches leave no room for them.
+    constexpr bool kEarlyDraws = IN == 2 && SR_COL;
+    U4 cdraw[kEarlyDraws ? 8 : 1][2];
     if constexpr (!RHT_ROW) {
         // A first round of the partial maxima (up to 768 per copy, three per thread) is loaded
         // before the patch: vector loads complete in issue order, so the wait for these leaves
@@ -540,6 +545,18 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
         // them would make the compiler wait for all of them before the first use of the
         // partials.
         load_patch(P, a, valid ? r0 : 0, valid ? c0 : 0, true);
+        if constexpr (kEarlyDraws) {
+            // the columnwise SR words of all 8 columns, formed while the loads are in flight
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint64_t gd = ((uint64_t)(c0 + j) * (uint64_t)a.rows + (uint64_t)r0) >> 3;
+                cdraw[j][0] = sr_words(gd, 1u, a.k0, a.k1);
+                cdraw[j][1] = sr_words(gd + 1, 1u, a.k0, a.k1);
+                asm volatile("" : "+v"(cdraw[j][0].x), "+v"(cdraw[j][0].y), "+v"(cdraw[j][0].z),
+                             "+v"(cdraw[j][0].w), "+v"(cdraw[j][1].x), "+v"(cdraw[j][1].y),
+                             "+v"(cdraw[j][1].z), "+v"(cdraw[j][1].w));
+            }
+        }
         // tensor scales from the per-tile partial maxima: the first round loaded above
         // (indices past the last partial read the last one again, which leaves the maximum
         // unchanged), then any beyond 768 (the LoRA first pass can have more workgroups)
@@ -720,12 +737,18 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
             }
             uint32_t lo, hi;
             if (SR_COL) {
-                const uint64_t g = ((uint64_t)(c0 + j) * (uint64_t)a.rows + (uint64_t)r0) >> 3;
                 float u[8];
-                const U4 rlo_w = sr_words(g, 1u, a.k0, a.k1);
+                U4 rlo_w, rhi_w;
+                if constexpr (kEarlyDraws) {
+                    rlo_w = cdraw[j][0];
+                    rhi_w = cdraw[j][1];
+                } else {
+                    const uint64_t g = ((uint64_t)(c0 + j) * (uint64_t)a.rows + (uint64_t)r0) >> 3;
+                    rlo_w = sr_words(g, 1u, a.k0, a.k1);
+                    rhi_w = sr_words(g + 1, 1u, a.k0, a.k1);
+                }
                 csc.scale8(&w[0], scode, rscale, u);
                 lo = encode8_sr(u, rlo_w, csc.cs);
-                const U4 rhi_w = sr_words(g + 1, 1u, a.k0, a.k1);
                 csc.scale8(&w[8], scode, rscale, u);
                 hi = encode8_sr(u, rhi_w, csc.cs);
             } else if (!have) {
