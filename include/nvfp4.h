@@ -166,8 +166,10 @@ int nvfp4_quantize_noalloc(const void* x, int dtype, int64_t rows, int64_t cols,
  * up-projection then adds lora_t times the up factor; see nvfp4_gemm_lora).  The sum over
  * cols is FP32 (BF16 matrix-core products), in a fixed order: parts of the columns summed
  * separately, then the parts in order.
- * Limits: dtype NVFP4_BF16 (else NVFP4_ERR_DTYPE); rank a multiple of 16 up to 64 and cols
- * a multiple of 128 (else NVFP4_ERR_SHAPE); ws of nvfp4_quantize_lora_workspace_bytes. */
+ * Limits: dtype NVFP4_BF16 (else NVFP4_ERR_DTYPE); rank a multiple of 16 up to 64, cols
+ * a multiple of 128, and ld_x and cols below 2^24 (the first pass addresses 64 rows of x
+ * and all of lora_a with 32-bit byte offsets) (else NVFP4_ERR_SHAPE); ws of
+ * nvfp4_quantize_lora_workspace_bytes. */
 size_t nvfp4_quantize_lora_workspace_bytes(int64_t rows, int64_t cols, int64_t rank);
 int nvfp4_quantize_lora(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
                         const nvfp4_quant_params* p, const nvfp4_qtensor* row_out,

@@ -120,6 +120,34 @@ template <int SEL>
 __device__ __forceinline__ float2v fp4x2_to_f32(uint32_t w) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
 }
+// ---------------------------------------------------------------- direct global -> LDS loads
+constexpr uint32_t kOutOfRange = 0x80000000u;   // past the end of every direct-load buffer
+
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor of a raw byte buffer: base, no stride, num_records bytes, the data
+// format word of untyped 32-bit buffer access.
+__device__ __forceinline__ int4v make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    return int4v{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+
+// Direct loads (lane l writes its 16 or 4 bytes at LDS address M0 + 16 l or M0 + 4 l; an
+// offset past num_records writes zeros).  They are written as assembly so that the compiler
+// does not track them: its own bookkeeping would otherwise wait for every pending direct
+// load before each LDS read, which would serialise a multi-stage pipeline.  Kernels wait
+// for them explicitly (s_waitcnt vmcnt, then a barrier).  The compiler's waits for other
+// vector-memory operations do not count them, so they can only wait longer than needed,
+// never shorter.
+__device__ __forceinline__ void dma16(int4v rsrc, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(int4v rsrc, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
 // ---------------------------------------------------------------- misc
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);

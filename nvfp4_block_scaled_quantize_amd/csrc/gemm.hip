@@ -56,7 +56,6 @@ constexpr int kGemmLds = kRegStages * kStageBytes;
 constexpr int kGemmDmaLds = kDmaStages * kStageBytes;
 // direct loads per wave and stage: 4 + 4 code chunks, 2 + 2 scale words
 constexpr int kDmaLoadsPerStage = 12;
-constexpr uint32_t kOutOfRange = 0x80000000u;   // past the end of every direct-path buffer
 
 struct GArgs {
     const uint8_t* ac;
@@ -280,30 +279,7 @@ __device__ __forceinline__ void tri_tile(int t, int T, int& tm, int& tn) {
     tn = r + rem;
 }
 
-// ---------------------------------------------------------------- direct global -> LDS loads
-
-typedef int int4v __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor of a raw byte buffer: base, no stride, num_records bytes, the data
-// format word of untyped 32-bit buffer access.
-__device__ __forceinline__ int4v make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t b = (uint64_t)base;
-    return int4v{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
-}
-
-// Direct loads.  They are written as assembly so that the compiler does not track them:
-// its own bookkeeping would otherwise wait for every pending direct load before each LDS
-// read, which would serialise the three-stage pipeline.  The kernel waits for them
-// explicitly (dma_wait_barrier); it issues no other vector-memory loads in the loop, so
-// the compiler's own waits can only wait longer than needed, never shorter.
-__device__ __forceinline__ void dma16(int4v rsrc, uint32_t lds_addr, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(int4v rsrc, uint32_t lds_addr, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
-}
+// ---------------------------------------------------------------- low-rank epilogue
 
 // LoRA-SVD up-projection in the epilogue (Full-Stack FP4 sec. 3.2 eq. (1), Appendix 9: the
 // low-rank branch shares the GEMM's output tile).  After the main loop the stage buffers are

@@ -126,7 +126,7 @@ static int check_qtensor(const nvfp4_qtensor* q) {
 }
 
 // LoRA first pass: 64-row blocks times K-parts of kp columns (a multiple of 128), with about
-// 768 workgroups in all.
+// 512 workgroups in all (its two LDS stages fit two workgroups per CU).
 struct LoraSplit {
     int64_t row_blocks, parts, kp;
 };
@@ -134,7 +134,7 @@ static LoraSplit lora_split(int64_t rows, int64_t cols) {
     LoraSplit s;
     s.row_blocks = (rows + kLoraRowsWG - 1) / kLoraRowsWG;
     const int64_t steps = (cols + kLoraStep - 1) / kLoraStep;
-    int64_t target = (768 + s.row_blocks - 1) / (s.row_blocks > 0 ? s.row_blocks : 1);
+    int64_t target = (512 + s.row_blocks - 1) / (s.row_blocks > 0 ? s.row_blocks : 1);
     if (target < 1) target = 1;
     const int64_t steps_per_part = (steps + target - 1) / target;
     s.kp = (steps_per_part > 0 ? steps_per_part : 1) * kLoraStep;
@@ -308,6 +308,9 @@ extern "C" int nvfp4_quantize_lora(const void* x, int dtype, int64_t rows, int64
     if (dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
     if (rank <= 0 || rank % 16 || rank > kLoraMaxRank) return NVFP4_ERR_SHAPE;
     if (rows < 0 || cols < 0 || cols % kLoraStep) return NVFP4_ERR_SHAPE;
+    // the first pass's direct loads address 64 input rows and the whole factor with 32-bit
+    // byte offsets
+    if (ld_x >= ((int64_t)1 << 24) || cols >= ((int64_t)1 << 24)) return NVFP4_ERR_SHAPE;
     if (!lora_a || !lora_t) return NVFP4_ERR_NULL;
     if (((uintptr_t)lora_a & 15) || ((uintptr_t)lora_t & 1)) return NVFP4_ERR_ALIGN;
     if (rows > 0 && cols == 0) {   // an empty contraction: T = 0

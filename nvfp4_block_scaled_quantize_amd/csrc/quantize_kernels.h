@@ -784,52 +784,66 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
 // The quantizer's first pass with the LoRA-SVD down-projection fused in (Full-Stack FP4
 // sec. 3.2 eq. (1) and Appendix 9: the down-projection X L1^T reuses the quantizer's input
 // read).  Work decomposition: a workgroup takes 64 rows (16 per wave) and one K-part of
-// lora_kp columns, in steps of 128 columns.  Lane (i, g) of a wave (i = lane mod 16,
-// g = lane / 16) loads 32 consecutive bfloat16 of row i, columns 32g .. 32g + 31 of the
-// step; these 16 registers are at once
-//  * the A operands of four BF16 MFMAs 16x16x32: k-step j takes columns 32g + 8j .. +7 as
-//    the MFMA's k-slots 8g .. 8g + 7, and the B operands (the step's 128 columns of a, one
-//    16 x 128 slice per MFMA column block, staged in LDS by the workgroup) follow the same
-//    correspondence, so every column is summed exactly once;
-//  * the input of the partial maxima of k_amax: plain and row-rotated in-register (the
-//    lane holds two whole 16-chunks of its row); for the column rotation the wave's step
-//    tile is transposed through LDS so that each lane holds 16 rows of two columns.
+// lora_kp columns, in steps of 128 columns; about two workgroups per CU.
+// Staging: each step's 64 x 128 input tile and its slice of a (rank x 128) go into one of
+// two LDS stages by direct global -> LDS loads, issued one step ahead and waited for
+// explicitly, so neither passes through registers and no step waits for loads issued in
+// the same step.  (Three stages at one workgroup per CU measured within noise of this;
+// four were slower.)  Both are stored as 16-byte chunks, chunk c of row r at r * 16 +
+// (c ^ (r mod 16)), which keeps every read below on distinct banks.  Lane (i, g) of a wave
+// (i = lane mod 16, g = lane / 16) reads
+//  * the 32 consecutive bfloat16 of its row i at columns 32g .. 32g + 31 (four chunks): the
+//    A operands of four BF16 MFMAs 16x16x32 (k-step j takes columns 32g + 8j .. +7 as the
+//    MFMA's k-slots 8g .. 8g + 7, and the B operands from the slice of a follow the same
+//    correspondence, so every column is summed exactly once), and the input of the plain
+//    and row-rotated maxima;
+//  * rows 0..15 of columns 2 lane and 2 lane + 1 of the wave's 16 x 128 block, for the
+//    column rotation.
 // The low-rank partial of each K-part goes to lora_part; k_encode sums the parts in order.
 constexpr int kLoraStep = 128;
 constexpr int kLoraRowsWG = 64;
 constexpr int kLoraMaxRank = 64;
+constexpr int kLoraStages = 2;
+constexpr int kLoraXBytes = kLoraRowsWG * kLoraStep * 2;   // one stage's input tile
 typedef __bf16 bf16x8t __attribute__((ext_vector_type(8)));
 typedef float f32x4t __attribute__((ext_vector_type(4)));
 
-// Step loads: this lane's 32 values of its row, and its share of the step's slice of a
-// (NQ 16-row blocks x 128 columns: NQ 16-byte chunks per thread, chunk q = t + 256 k).
-__device__ __forceinline__ void lora_load_x(const uint16_t* xrow, bool rvalid, int64_t c, int g,
-                                            uint4 (&xw)[4]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        xw[q] = rvalid ? *(const uint4*)(xrow + c + 32 * g + 8 * q) : make_uint4(0u, 0u, 0u, 0u);
-}
+// One stage: the input tile, then the slice of a (NQ 16-row blocks).
+__host__ __device__ constexpr int lora_stage_bytes(int nq) { return kLoraXBytes + nq * 16 * kLoraStep * 2; }
+
+// Direct loads of the step at column c into the stage at LDS address base: slot p =
+// 256 k + t of each part receives the global chunk that the layout above puts there.  Input
+// rows past the workgroup's valid rows read zeros (offset past the buffer's end).
 template <int NQ>
-__device__ __forceinline__ void lora_load_a(const QArgs& a, int64_t c, int t, uint4 (&lw)[NQ]) {
+__device__ __forceinline__ void lora_dma(const QArgs& a, int4v rx, int4v ra, uint32_t base, int64_t c,
+                                         int t, int wid, int64_t rows_here) {
 #pragma unroll
-    for (int k = 0; k < NQ; ++k) {
-        const int q = t + kThreads * k;
-        lw[k] = *(const uint4*)(a.lora_a + (int64_t)(q >> 4) * a.cols + c + (q & 15) * 8);
+    for (int k = 0; k < 4; ++k) {
+        const int p = k * kThreads + t, r = p >> 4, ch = (p & 15) ^ (r & 15);
+        const uint32_t off = r < rows_here ? (uint32_t)(((int64_t)r * a.ld + c + ch * 8) * 2) : kOutOfRange;
+        dma16(rx, base + (uint32_t)(k * kThreads + wid * 64) * 16, off);
     }
-}
-template <int NQ>
-__device__ __forceinline__ void lora_store_a(uint4* bl, int t, const uint4 (&lw)[NQ]) {
 #pragma unroll
     for (int k = 0; k < NQ; ++k) {
-        const int q = t + kThreads * k, rr = q >> 4, ch = q & 15;
-        bl[rr * 16 + (ch ^ (rr & 15))] = lw[k];
+        const int p = k * kThreads + t, rr = p >> 4, ch = (p & 15) ^ (rr & 15);
+        const uint32_t off = (uint32_t)(((int64_t)rr * a.cols + c + ch * 8) * 2);
+        dma16(ra, base + kLoraXBytes + (uint32_t)(k * kThreads + wid * 64) * 16, off);
     }
 }
 
-// The partial maxima of one step's 32 values (see k_amax_lora).
+// Wait until at most AHEAD stages of this wave's direct loads are outstanding (they complete
+// in issue order), then meet the other waves: after it the awaited stage is in LDS and every
+// wave is done with the stage about to be refilled.
+template <int NQ, int AHEAD>
+__device__ __forceinline__ void lora_wait_meet() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(AHEAD * (4 + NQ)) : "memory");
+}
+
+// The partial maxima of one step from the wave's 16 x 128 block wx in LDS; xv holds this
+// lane's four chunks of it (see k_amax_lora).
 template <int H>
 __device__ __forceinline__ void lora_step_amax(const QArgs& a, const uint4 (&xv)[4], uint32_t signs,
-                                               uint4* tw, int lane, float& mr, float& mc) {
+                                               const uint4* wx, int lane, float& mr, float& mc) {
     constexpr bool RHT_ROW = H & 1, RHT_COL = (H >> 1) & 1;
     uint32_t xw[16];
 #pragma unroll
@@ -860,17 +874,13 @@ __device__ __forceinline__ void lora_step_amax(const QArgs& a, const uint4 (&xv)
         }
     }
     if (RHT_COL) {
-        // the column rotation needs a row chunk's 16 values in one lane: the wave's 16 x 128
-        // step tile goes through its LDS area (16-byte chunk c of row r at c ^ r, conflict-free
-        // both ways) and comes back as rows 0..15 of columns 2 lane, 2 lane + 1
-        const int i = lane & 15, g = lane >> 4;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) tw[i * 16 + ((4 * g + q) ^ i)] = xv[q];
-        const uint32_t* tw32 = (const uint32_t*)tw;
+        // rows 0..15 of columns 2 lane, 2 lane + 1: dword lane of each row, whose chunk
+        // lane / 4 sits at position (lane / 4) ^ r
+        const uint32_t* w32 = (const uint32_t*)wx;
         float w0[16], w1[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const uint32_t d = tw32[r * 64 + ((((lane >> 2) ^ r) & 15) << 2) + (lane & 3)] ^
+            const uint32_t d = w32[r * 64 + ((((lane >> 2) ^ r) & 15) << 2) + (lane & 3)] ^
                                col_sign_mask(signs, r);
             w0[r] = __uint_as_float(d << 16);
             w1[r] = __uint_as_float(d & 0xFFFF0000u);
@@ -896,66 +906,51 @@ __device__ __forceinline__ void lora_step_mma(const uint4 (&xv)[4], const uint4*
     }
 }
 
-// One 128-column step: its maxima and MFMAs from (xv, bl[cur]) while the loads of the next
-// step (xn, lw) are in flight; then the next slice of a goes to the other LDS buffer.
 template <int H, int NQ>
-__device__ __forceinline__ void lora_step(const QArgs& a, const uint4 (&xv)[4], uint4 (&xn)[4],
-                                          uint4 (&lw)[NQ], uint4* bcur, uint4* bnext, bool more,
-                                          int64_t cnext, const uint16_t* xrow, bool rvalid, int t,
-                                          int i, int g, uint32_t signs, uint4* tw, int lane,
-                                          float& mr, float& mc, f32x4t (&acc)[NQ]) {
-    if (more) {
-        lora_load_x(xrow, rvalid, cnext, g, xn);
-        lora_load_a<NQ>(a, cnext, t, lw);
-    }
-    lora_step_amax<H>(a, xv, signs, tw, lane, mr, mc);
-    lora_step_mma<NQ>(xv, bcur, i, g, acc);
-    if (more) lora_store_a<NQ>(bnext, t, lw);
-    __syncthreads();
-}
-
-// Three workgroups per CU (at most 168 VGPRs): the third wave per SIMD hides more of each
-// step's load latency than the few scratch round trips of the ping-pong registers cost
-// (X 8192x3072 rank 64: 55.8 -> 53.6 us; dY 8192x9216: 172 -> 163 us, outputs identical).
-template <int H, int NQ>
-__global__ __launch_bounds__(kThreads, 3) void k_amax_lora(QArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void k_amax_lora(QArgs a) {
     constexpr bool RHT_ROW = H & 1, RHT_COL = (H >> 1) & 1;
-    // [2 buffers][NQ*16 rows][16 chunks], chunk ^ (row & 15): the next step's slice is
-    // written into one buffer while the MFMAs read the other
-    __shared__ uint4 bl[2][NQ * 16 * (kLoraStep / 8)];
-    __shared__ uint4 tws[4][16 * 16];   // per wave: the step tile for the column rotation
+    constexpr int kStage = lora_stage_bytes(NQ);
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     __shared__ float red[8];
-    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(t >> 6);
     const int i = lane & 15, g = lane >> 4;
     const int rblk = blockIdx.x / a.lora_parts, part = blockIdx.x % a.lora_parts;
-    const int64_t row = (int64_t)rblk * kLoraRowsWG + wid * 16 + i;
-    const bool rvalid = row < a.rows;
+    const int64_t row0 = (int64_t)rblk * kLoraRowsWG;
+    const int64_t rows_here = a.rows - row0 < kLoraRowsWG ? a.rows - row0 : kLoraRowsWG;
     const int64_t kb = (int64_t)part * a.lora_kp;
     const int64_t ke = kb + a.lora_kp < a.cols ? kb + a.lora_kp : a.cols;
+    const int nsteps = (int)((ke - kb) / kLoraStep);
     const uint32_t signs =
         (RHT_ROW || RHT_COL) ? __builtin_amdgcn_readfirstlane(rht_sign_bits(a.k0, a.k1)) : 0u;
-    uint4* tw = tws[wid];
-    const uint16_t* xrow = (const uint16_t*)a.x + row * a.ld;
+    const int4v rx = make_rsrc((const uint16_t*)a.x + row0 * a.ld, (uint32_t)(rows_here * a.ld * 2));
+    const int4v ra = make_rsrc(a.lora_a, (uint32_t)(a.lora_r * a.cols * 2));
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
 
     f32x4t acc[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) acc[q] = f32x4t{0.0f, 0.0f, 0.0f, 0.0f};
     float mr = 0.0f, mc = 0.0f;
 
-    uint4 x0[4], x1[4], lw[NQ];
-    lora_load_x(xrow, rvalid, kb, g, x0);
-    lora_load_a<NQ>(a, kb, t, lw);
-    lora_store_a<NQ>(bl[0], t, lw);
-    __syncthreads();
-    // two steps per trip with ping-pong buffers, so nothing is copied
-    for (int64_t c = kb; c < ke; c += 2 * kLoraStep) {
-        const bool more0 = c + kLoraStep < ke;
-        lora_step<H, NQ>(a, x0, x1, lw, bl[0], bl[1], more0, c + kLoraStep, xrow, rvalid, t, i, g,
-                         signs, tw, lane, mr, mc, acc);
-        if (!more0) break;
-        const bool more1 = c + 2 * kLoraStep < ke;
-        lora_step<H, NQ>(a, x1, x0, lw, bl[1], bl[0], more1, c + 2 * kLoraStep, xrow, rvalid, t, i,
-                         g, signs, tw, lane, mr, mc, acc);
+    constexpr int kAhead = kLoraStages - 1;   // steps whose loads are in flight ahead
+    for (int j = 0; j < kAhead && j < nsteps; ++j)
+        lora_dma<NQ>(a, rx, ra, lds0 + j * kStage, kb + j * kLoraStep, t, wid, rows_here);
+    for (int s = 0; s < nsteps; ++s) {
+        const int later = nsteps - 1 - s < kAhead - 1 ? nsteps - 1 - s : kAhead - 1;
+        if (later >= 2) lora_wait_meet<NQ, 2>();
+        else if (later == 1) lora_wait_meet<NQ, 1>();
+        else lora_wait_meet<NQ, 0>();
+        // every wave is done with step s - 1, whose stage the loads of step s + kAhead refill
+        if (s + kAhead < nsteps)
+            lora_dma<NQ>(a, rx, ra, lds0 + ((s + kAhead) % kLoraStages) * kStage,
+                         kb + (int64_t)(s + kAhead) * kLoraStep, t, wid, rows_here);
+        const uint4* xs = (const uint4*)(lds + (s % kLoraStages) * kStage);
+        const uint4* wx = xs + wid * 16 * 16;   // the wave's 16 rows
+        uint4 xv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[q] = wx[i * 16 + ((4 * g + q) ^ i)];
+        lora_step_amax<H>(a, xv, signs, wx, lane, mr, mc);
+        lora_step_mma<NQ>(xv, xs + kLoraXBytes / 16, i, g, acc);
     }
     if (RHT_ROW) mr = mr * 0.25f;
     if (RHT_COL) mc = mc * 0.25f;
@@ -966,7 +961,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_amax_lora(QArgs a) {
     for (int q = 0; q < NQ; ++q) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int64_t r = (int64_t)rblk * kLoraRowsWG + wid * 16 + 4 * g + v;
+            const int64_t r = row0 + wid * 16 + 4 * g + v;
             if (r < a.rows) a.lora_part[part * total + r * a.lora_r + 16 * q + i] = acc[q][v];
         }
     }
@@ -977,13 +972,21 @@ __global__ __launch_bounds__(kThreads, 3) void k_amax_lora(QArgs a) {
     }
 }
 
+template <int H, int NQ>
+void launch_amax_lora_nq(const QArgs& a, hipStream_t st) {
+    constexpr int bytes = kLoraStages * lora_stage_bytes(NQ);
+    static_assert(bytes <= 160 * 1024 - 64, "LDS budget");
+    (void)hipFuncSetAttribute((const void*)k_amax_lora<H, NQ>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    k_amax_lora<H, NQ><<<a.npart, kThreads, bytes, st>>>(a);
+}
+
 template <int H>
 void launch_amax_lora(const QArgs& a, hipStream_t st) {
     switch (a.lora_r / 16) {
-    case 1: k_amax_lora<H, 1><<<a.npart, kThreads, 0, st>>>(a); break;
-    case 2: k_amax_lora<H, 2><<<a.npart, kThreads, 0, st>>>(a); break;
-    case 3: k_amax_lora<H, 3><<<a.npart, kThreads, 0, st>>>(a); break;
-    default: k_amax_lora<H, 4><<<a.npart, kThreads, 0, st>>>(a); break;
+    case 1: launch_amax_lora_nq<H, 1>(a, st); break;
+    case 2: launch_amax_lora_nq<H, 2>(a, st); break;
+    case 3: launch_amax_lora_nq<H, 3>(a, st); break;
+    default: launch_amax_lora_nq<H, 4>(a, st); break;
     }
 }
 

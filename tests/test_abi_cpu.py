@@ -126,6 +126,29 @@ def test_quantize_noalloc_argument_errors(nv):
         assert lib.nvfp4_quantize_workspace_bytes(*shape, ctypes.byref(p)) <= 6144
 
 
+def test_quantize_lora_argument_errors(nv):
+    """Shape and type limits of the fused LoRA quantize, checked before anything is enqueued."""
+    lib = nv.load_library()
+    p = nv.quant_params(rowwise=True)
+    q = _qt(FAKE)
+    x = ctypes.c_void_p(FAKE + 0x80000)
+    la = ctypes.c_void_p(FAKE + 0x90000)
+    t = ctypes.c_void_p(FAKE + 0xA0000)
+    ws = ctypes.c_void_p(FAKE + 0xB0000)
+    call = lambda rows, cols, ld, rank, dtype=1: lib.nvfp4_quantize_lora(
+        x, dtype, rows, cols, ld, ctypes.byref(p), ctypes.byref(q), None, la, rank, ctypes.c_float(1.0),
+        t, ws, 1 << 30, None)
+    assert call(64, 256, 256, 64, dtype=0) == -4        # bfloat16 only
+    assert call(64, 256, 256, 24) == -2                 # rank not a multiple of 16
+    assert call(64, 256, 256, 80) == -2                 # rank above 64
+    assert call(64, 200, 200, 64) == -2                 # cols not a multiple of 128
+    assert call(64, 256, 1 << 24, 64) == -2             # row pitch past the 32-bit offsets
+    assert call(16, 1 << 24, 1 << 24, 64) == -2         # factor past the 32-bit offsets
+    # the workspace holds both copies' partial maxima and the K-parts' FP32 partials of T
+    need = lib.nvfp4_quantize_lora_workspace_bytes(8192, 9216, 64)
+    assert need >= 2 * 8192 * 64 * 4
+
+
 def test_gemm_and_dequantize_argument_errors(nv):
     lib = nv.load_library()
     a, b = _qt(FAKE), _qt(FAKE + 0x100000)
