@@ -205,50 +205,59 @@ __device__ __forceinline__ void mma_stage(const Frags& f, float16v (&acc)[4][4])
 // the caches cut the FFN-up GEMM from 508 to 433 us on this part.  One block row
 // (32 rows) at a time, with a scheduling fence between block rows, so the compiler does
 // not pull all 256 accumulators into VGPRs at once.
-// ADD: each element first adds the raw partial sum that the same position of C holds (the
-// other K half of a tile split by the balanced schedule), fl(acc + p), before the scaling.
-// A block row's 64 partials are loaded before any of its stores: a load issued after
-// stores can only be waited for together with them.  FULL: the tile lies inside C, so no
-// element needs a bounds test (a test per element becomes a branch, and the compiler waits
-// for every outstanding store at each branch's end).
-template <bool ADD, bool FULL>
+// MODE: StPlain stores acc * scale; StAdd first adds the raw partial sum that the same
+// position of C holds (the other K half of a tile split by the balanced schedule),
+// fl(acc + p) * scale; StAxpby stores fma(scale, acc, fl(beta d)) with d from D (which may be
+// C: each element of D is read by the lane that writes the same element of C, before it).
+// A block row's 64 loads are issued before any of its stores: a load issued after stores can
+// only be waited for together with them.  FULL: the tile lies inside C, so no element needs a
+// bounds test (a test per element becomes a branch, and the compiler waits for every
+// outstanding store at each branch's end).
+enum { StPlain = 0, StAdd = 1, StAxpby = 2 };
+template <int MODE, bool FULL>
 __device__ __forceinline__ void store_rows(const GArgs& g, const float16v (&acc)[4][4], int64_t m0,
                                            int64_t n0, int wm, int wn, int h, int li, float scale) {
     const int64_t rbase = m0 + wm * 128 + 4 * h, cbase = n0 + wn * 128 + li;
+    constexpr int RB = MODE == StAxpby ? 8 : 16;  // accumulator rows per batch of loads
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float pv[16][4];
-        if constexpr (ADD) {
+    for (int b = 0; b < 64; b += RB) {
+        const int i = b >> 4;
+        float pv[RB][4];
+        if constexpr (MODE != StPlain) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int r = b & 15; r < (b & 15) + RB; ++r) {
                 const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
-                const float* rowp = g.c + row * g.ldc + cbase;
+                const float* src = MODE == StAdd ? g.c + row * g.ldc + cbase : g.d + row * g.ldd + cbase;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    pv[r][j] = (FULL || (row < g.M && cbase + j * 32 < g.N)) ? rowp[j * 32] : 0.0f;
+                    pv[r - (b & 15)][j] = (FULL || (row < g.M && cbase + j * 32 < g.N)) ? src[j * 32] : 0.0f;
             }
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = b & 15; r < (b & 15) + RB; ++r) {
             const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
             float* rowp = g.c + row * g.ldc + cbase;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (FULL || (row < g.M && cbase + j * 32 < g.N)) {
-                    float x = acc[i][j][r];
-                    if constexpr (ADD) x = x + pv[r][j];
-                    __builtin_nontemporal_store(x * scale, rowp + j * 32);
+                    if constexpr (MODE == StAxpby) {
+                        rowp[j * 32] = __builtin_fmaf(scale, acc[i][j][r], g.beta * pv[r - (b & 15)][j]);
+                    } else {
+                        float x = acc[i][j][r];
+                        if constexpr (MODE == StAdd) x = x + pv[r - (b & 15)][j];
+                        __builtin_nontemporal_store(x * scale, rowp + j * 32);
+                    }
                 }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-template <bool ADD = false>
+template <int MODE = StPlain>
 __device__ __forceinline__ void store_tile(const GArgs& g, const float16v (&acc)[4][4], int64_t m0,
                                            int64_t n0, int wm, int wn, int h, int li, float scale) {
-    if (m0 + GBM <= g.M && n0 + GBN <= g.N) store_rows<ADD, true>(g, acc, m0, n0, wm, wn, h, li, scale);
-    else store_rows<ADD, false>(g, acc, m0, n0, wm, wn, h, li, scale);
+    if (m0 + GBM <= g.M && n0 + GBN <= g.N) store_rows<MODE, true>(g, acc, m0, n0, wm, wn, h, li, scale);
+    else store_rows<MODE, false>(g, acc, m0, n0, wm, wn, h, li, scale);
 }
 
 // The raw accumulators of the tile into its 256 x 256 slot of the partial buffer (row-major),
@@ -382,30 +391,6 @@ __device__ __forceinline__ void lora_epilogue(const GArgs& g, uint8_t* lds, floa
     }
 }
 
-// alpha * product + beta * D, stored as fma(fl(alpha s_gA s_gB), acc, fl(beta d)).  Each
-// element of D is read by the lane that writes the same element of C, so D may be C.
-__device__ __forceinline__ void store_tile_axpby(const GArgs& g, const float16v (&acc)[4][4],
-                                                 int64_t m0, int64_t n0, int wm, int wn, int h,
-                                                 int li) {
-    const float as = (*g.asg * *g.bsg) * g.alpha;
-    const int64_t rbase = m0 + wm * 128 + 4 * h, cbase = n0 + wn * 128 + li;
-    const bool full = m0 + GBM <= g.M && n0 + GBN <= g.N;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
-            const float* drow = g.d + row * g.ldd + cbase;
-            float* rowp = g.c + row * g.ldc + cbase;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (full || (row < g.M && cbase + j * 32 < g.N))
-                    rowp[j * 32] = __builtin_fmaf(as, acc[i][j][r], g.beta * drow[j * 32]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
 // The epilogue variant is a compile-time switch so that the plain kernels keep their
 // register allocation.  mode (the balanced schedule's; every other caller takes 1):
 // 0 the raw accumulators into C (a K half parked for the other half's workgroup), 1 the
@@ -422,12 +407,13 @@ __device__ __forceinline__ void finish_tile(const GArgs& g, uint8_t* lds, float1
             lora_epilogue(g, lds, acc, m0, n0, wm, wn, h, li, mode == FinAdd);
         store_tile(g, acc, m0, n0, wm, wn, h, li, mode == FinNan ? nan : 1.0f);
     } else if constexpr (EPI == EpiAxpby) {
-        store_tile_axpby(g, acc, m0, n0, wm, wn, h, li);
+        // alpha * product + beta * D, stored as fma(fl(alpha s_gA s_gB), acc, fl(beta d))
+        store_tile<StAxpby>(g, acc, m0, n0, wm, wn, h, li, (*g.asg * *g.bsg) * g.alpha);
     } else if constexpr (EPI == EpiPart) {
         store_part(g.part + ((int64_t)blockIdx.x << 16), acc, wm, wn, h, li);
     } else {
         const float scale = mode == FinPark ? 1.0f : (mode == FinNan ? nan : *g.asg * *g.bsg);
-        if (mode == FinAdd) store_tile<true>(g, acc, m0, n0, wm, wn, h, li, scale);
+        if (mode == FinAdd) store_tile<StAdd>(g, acc, m0, n0, wm, wn, h, li, scale);
         else store_tile(g, acc, m0, n0, wm, wn, h, li, scale);
     }
 }
