@@ -56,6 +56,10 @@ constexpr int kGemmLds = kRegStages * kStageBytes;
 constexpr int kGemmDmaLds = kDmaStages * kStageBytes;
 // direct loads per wave and stage: 4 + 4 code chunks, 2 + 2 scale words
 constexpr int kDmaLoadsPerStage = 12;
+// MFMAs per direct load in the stage's second half: the loads of the four waves, issued at
+// once, queue in the texture-address unit and hold up the waves behind them; one load per
+// two MFMAs measured best against one per MFMA or per four.
+constexpr int kDmaSpread = 2;
 
 struct GArgs {
     const uint8_t* ac;
@@ -537,36 +541,28 @@ struct Rsrc4 {
     int4v ac, as, bc, bs;
 };
 
-// Issue this wave's 12 direct loads of stage s into the LDS stage at byte address buf.
-// Load i of the codes covers LDS slots [256 i + 64 wid, +64) of the operand's tile; slot
-// p = row * 4 + q receives global chunk q ^ (row/4 mod 4) of the row, which is the layout
-// code_off describes.
-__device__ __forceinline__ void dma_stage(const GArgs& g, const Rsrc4& rs, uint32_t buf,
-                                          int64_t m0, int64_t n0, int s, int t, int wid,
-                                          uint32_t kbytes, uint32_t kblocks) {
-    const uint32_t k0b = (uint32_t)s * 64;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = i * 256 + t, row = p >> 2, q = p & 3;
-        const uint32_t off = k0b + (uint32_t)((q ^ ((row >> 2) & 3)) << 4);
-        const bool kin = off < kbytes;
-        const uint32_t va = (kin && m0 + row < g.M) ? (uint32_t)(m0 + row) * kbytes + off : kOutOfRange;
-        const uint32_t vb = (kin && n0 + row < g.N) ? (uint32_t)(n0 + row) * kbytes + off : kOutOfRange;
-        const uint32_t dst = buf + (uint32_t)(i * 256 + wid * 64) * 16;
-        dma16(rs.ac, dst, va);
-        dma16(rs.bc, dst + kStageCodeBytes, vb);
-    }
-    const uint32_t kb0 = (uint32_t)s * 8;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int j = i * 256 + t, row = j >> 1;
-        const uint32_t kb = kb0 + 4 * (j & 1);
-        const bool kin = kb < kblocks;
-        const uint32_t va = (kin && m0 + row < g.M) ? (uint32_t)(m0 + row) * kblocks + kb : kOutOfRange;
-        const uint32_t vb = (kin && n0 + row < g.N) ? (uint32_t)(n0 + row) * kblocks + kb : kOutOfRange;
-        const uint32_t dst = buf + 2 * kStageCodeBytes + (uint32_t)(i * 256 + wid * 64) * 4;
-        dma4(rs.as, dst, va);
-        dma4(rs.bs, dst + kStageScaleBytes, vb);
+// This wave's 12 direct loads of one K stage: the global offsets of its four code chunks
+// per operand (16 bytes per lane) and two scale words per operand (4 bytes per lane), and
+// the LDS stage they fill.  Load i of the codes covers LDS slots [256 i + 64 wid, +64) of
+// the operand's tile; slot p = row * 4 + q receives global chunk q ^ (row/4 mod 4) of the
+// row, which is the layout code_off describes.  A stage outside [c.s0, c.s0 + c.nst) gets
+// offsets past the end of every operand: its loads read nothing and write zeros into buf.
+struct StageLoads {
+    uint32_t ca[4], cb[4], sa[2], sb[2];
+    uint32_t buf;
+};
+
+template <int K>
+__device__ __forceinline__ void issue_load(const Rsrc4& rs, const StageLoads& L, int wid) {
+    if constexpr (K < 8) {
+        const uint32_t dst = L.buf + (uint32_t)((K >> 1) * 256 + wid * 64) * 16;
+        if constexpr (K & 1) dma16(rs.bc, dst + kStageCodeBytes, L.cb[K >> 1]);
+        else dma16(rs.ac, dst, L.ca[K >> 1]);
+    } else {
+        constexpr int i = (K - 8) >> 1;
+        const uint32_t dst = L.buf + 2 * kStageCodeBytes + (uint32_t)(i * 256 + wid * 64) * 4;
+        if constexpr (K & 1) dma4(rs.bs, dst + kStageScaleBytes, L.sb[i]);
+        else dma4(rs.as, dst, L.sa[i]);
     }
 }
 
@@ -663,11 +659,61 @@ struct DmaCtx {
     uint32_t kbytes, kblocks;
 };
 
-// Wait until this wave has at most N direct loads outstanding, then meet the other waves.
-__device__ __forceinline__ void wait_meet(int ahead) {
-    if (ahead >= 2) dma_wait_barrier<2 * kDmaLoadsPerStage>();
-    else if (ahead == 1) dma_wait_barrier<kDmaLoadsPerStage>();
-    else dma_wait_barrier<0>();
+__device__ __forceinline__ void stage_loads(const DmaCtx& c, int s, uint32_t buf, StageLoads& L) {
+    const bool live = s < c.s0 + c.nst;
+    const uint32_t k0b = (uint32_t)s * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = i * 256 + c.t, row = p >> 2, q = p & 3;
+        const uint32_t off = k0b + (uint32_t)((q ^ ((row >> 2) & 3)) << 4);
+        const bool kin = live && off < c.kbytes;
+        L.ca[i] = (kin && c.m0 + row < c.g.M) ? (uint32_t)(c.m0 + row) * c.kbytes + off : kOutOfRange;
+        L.cb[i] = (kin && c.n0 + row < c.g.N) ? (uint32_t)(c.n0 + row) * c.kbytes + off : kOutOfRange;
+    }
+    const uint32_t kb0 = (uint32_t)s * 8;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int j = i * 256 + c.t, row = j >> 1;
+        const uint32_t kb = kb0 + 4 * (j & 1);
+        const bool kin = live && kb < c.kblocks;
+        L.sa[i] = (kin && c.m0 + row < c.g.M) ? (uint32_t)(c.m0 + row) * c.kblocks + kb : kOutOfRange;
+        L.sb[i] = (kin && c.n0 + row < c.g.N) ? (uint32_t)(c.n0 + row) * c.kblocks + kb : kOutOfRange;
+    }
+    L.buf = buf;
+}
+
+// All 12 loads of a stage at once (the prologue).
+__device__ __forceinline__ void dma_stage(const DmaCtx& c, int s, uint32_t buf) {
+    StageLoads L;
+    stage_loads(c, s, buf, L);
+    static_for<0, 12>([&](auto K) { issue_load<K>(c.rs, L, c.wid); });
+}
+
+// Two halves of decode8: code pairs 2Q and 2Q + 1 of w into elements 4Q .. 4Q + 3 of o.
+template <int Q>
+__device__ __forceinline__ void decode4(uint32_t w, half2v s2, half8v& o) {
+    const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2 * Q) * s2;
+    const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2 * Q + 1) * s2;
+    o[4 * Q] = p0.x; o[4 * Q + 1] = p0.y; o[4 * Q + 2] = p1.x; o[4 * Q + 3] = p1.y;
+}
+
+// A slot's 16 MFMAs on (av, bv), each followed by a quarter of one operand's decode of slot
+// T into (an, bn) and by X(k), in a scheduling region of its own: memory instructions
+// placed in X are spread over the slot instead of issued as a burst.
+template <int T, class Fx>
+__device__ __forceinline__ void mma_slot_steps(const half8v (&av)[4], const half8v (&bv)[4],
+                                               float16v (&acc)[4][4], const HalfFrags& f,
+                                               const Pairs& p, half8v (&an)[4], half8v (&bn)[4],
+                                               Fx&& X) {
+    static_for<0, 16>([&](auto K) {
+        constexpr int k = K, d = k >> 1, q = k & 1;
+        acc[k >> 2][k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[k >> 2], bv[k & 3],
+                                                                    acc[k >> 2][k & 3], 0, 0, 0);
+        if constexpr (d < 4) decode4<q>(dword_of(f.a[d], T & 3), p.a[d], an[d]);
+        else decode4<q>(dword_of(f.b[d - 4], T & 3), p.b[d - 4], bn[d - 4]);
+        X(K);
+        __builtin_amdgcn_sched_barrier(0);
+    });
 }
 
 // Stage s.  On entry lo, hi, sa, sb hold stage s, p the scale pairs of its block 0 and
@@ -696,26 +742,40 @@ __device__ __forceinline__ void piped_stage(const DmaCtx& c, int s, HalfFrags& l
     // carries the next stage's slot 0, and that half becomes VALU-bound.
 #pragma unroll
     for (int x = 0; x < 4; ++x) asm volatile("" : "+v"(av[x]), "+v"(bv[x]));
-    // lo is dead: stage s + 1 must be in LDS (its loads were issued two stages ago)
-    const int last = s + 2 < c.nst ? s + 2 : c.nst - 1;   // last stage issued so far
-    wait_meet(last - (s + 1));
-    if (s + 3 < c.nst)
-        dma_stage(c.g, c.rs, c.lds0 + (s % kDmaStages) * kStageBytes, c.m0, c.n0, c.s0 + s + 3, c.t,
-                  c.wid, c.kbytes, c.kblocks);
+    // Stage s + 3 refills this stage's buffer (out of range past the segment's last stage).
+    StageLoads L;
+    stage_loads(c, c.s0 + s + 3, c.lds0 + (s % kDmaStages) * kStageBytes, L);
+    // lo is dead: stage s + 1 must be in LDS (its loads were issued two stages ago, those
+    // of stage s + 2 may be in flight), and every wave is done with this stage's buffer
+    dma_wait_barrier<kDmaLoadsPerStage>();
     const uint8_t* nxt = c.lds + ((s + 1) % kDmaStages) * kStageBytes;
     uint32_t nsa[4], nsb[4];
-    read_half(nxt, 0, c.wm, c.wn, c.h, c.li, lo);
-    read_scales(nxt, c.wm, c.wn, c.h, c.li, nsa, nsb);
-    decode_slot<5>(hi, p, an, bn);
-    mma_slot(av, bv, acc);
-    pace<4>();
+    // Slots 4 to 6: each MFMA with a quarter of the next slot's decode; the 12 loads of stage
+    // s + 3 go one per kDmaSpread MFMAs from slot 4's first MFMA on, and the reads of the
+    // next stage's lo and scale words two per MFMA over the second half of slot 4.
+    const auto extra = [&](auto J, auto K) {
+        constexpr int g = J * 16 + K;
+        if constexpr (g % kDmaSpread == 0 && g / kDmaSpread < kDmaLoadsPerStage)
+            issue_load<g / kDmaSpread>(c.rs, L, c.wid);
+        if constexpr (J == 0 && K >= 8) {
+            constexpr int x = (K - 8) & 3;
+            const int ra = c.wm * 128 + x * 32 + c.li, rb = c.wn * 128 + x * 32 + c.li;
+            if constexpr (K < 12) {
+                lo.a[x] = *(const uint4*)(nxt + code_off(ra, 2 * c.h));
+                lo.b[x] = *(const uint4*)(nxt + kStageCodeBytes + code_off(rb, 2 * c.h));
+            } else {
+                nsa[x] = *(const uint32_t*)(nxt + 2 * kStageCodeBytes + ra * 8 + 4 * c.h);
+                nsb[x] = *(const uint32_t*)(nxt + 2 * kStageCodeBytes + kStageScaleBytes + rb * 8 + 4 * c.h);
+            }
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    mma_slot_steps<5>(av, bv, acc, hi, p, an, bn, [&](auto K) { extra(I0{}, K); });
     make_pairs<3>(sa, sb, p);
-    decode_slot<6>(hi, p, av, bv);
-    mma_slot(an, bn, acc);
-    pace<5>();
-    decode_slot<7>(hi, p, an, bn);
-    mma_slot(av, bv, acc);
-    pace<4>();
+    mma_slot_steps<6>(an, bn, acc, hi, p, av, bv, [&](auto K) { extra(I1{}, K); });
+    mma_slot_steps<7>(av, bv, acc, hi, p, an, bn, [&](auto K) { extra(I2{}, K); });
     // hi is dead
     read_half(nxt, 1, c.wm, c.wn, c.h, c.li, hi);
     make_pairs<0>(nsa, nsb, p);
@@ -730,11 +790,8 @@ __device__ __forceinline__ void piped_stage(const DmaCtx& c, int s, HalfFrags& l
 // first three stages' direct loads, then the pipelined stages.  On return every direct load
 // has landed and every wave has passed the last stage's barrier; LDS holds nothing needed.
 __device__ __forceinline__ void run_stages(const DmaCtx& c, float16v (&acc)[4][4]) {
-    const int pre = c.nst < kDmaStages ? c.nst : kDmaStages;
-    for (int j = 0; j < pre; ++j)
-        dma_stage(c.g, c.rs, c.lds0 + j * kStageBytes, c.m0, c.n0, c.s0 + j, c.t, c.wid, c.kbytes,
-                  c.kblocks);
-    wait_meet(pre - 1);
+    for (int j = 0; j < kDmaStages; ++j) dma_stage(c, c.s0 + j, c.lds0 + j * kStageBytes);
+    dma_wait_barrier<(kDmaStages - 1) * kDmaLoadsPerStage>();
     HalfFrags lo, hi;
     uint32_t sa[4], sb[4];
     Pairs p;
@@ -745,6 +802,8 @@ __device__ __forceinline__ void run_stages(const DmaCtx& c, float16v (&acc)[4][4
     make_pairs<0>(sa, sb, p);
     decode_slot<0>(lo, p, av, bv);
     for (int s = 0; s < c.nst; ++s) piped_stage(c, s, lo, hi, sa, sb, p, av, bv, acc);
+    // the loads of the (empty) stages past the segment land before LDS is used again
+    dma_wait_barrier<0>();
 }
 
 // The thread's lane coordinates from its index t.
