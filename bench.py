@@ -4,7 +4,8 @@
 A step is one pass of the whole path over the 3B model's FFN at 8192 tokens (hidden 3072,
 FFN 9216), the workload the headline metric is quoted on:
   forward   Q(X) rowwise RNE + columnwise RHT16 copy, Q(W_up) 16x16 2D (both copies),
-            GEMM Y_up = X W_up^T (8192x9216x3072), Q(H) rowwise, Q(W_down) 2D,
+            GEMM H = bf16(X W_up^T) (8192x9216x3072) with its tile maxima, Q(H) rowwise
+            (its tensor amax from those maxima: H is read once), Q(W_down) 2D,
             GEMM Y_down = H W_down^T (8192x3072x9216)
   backward  Q(dY) rowwise SR + columnwise RHT16 SR, dgrad GEMM dX = dY W_up
             (8192x3072x9216), wgrad GEMM dW = dY^T X on the rotated copies (9216x3072x8192)
@@ -376,7 +377,6 @@ def main():
     X = ffn["X"].to(dev)
     W_up = ffn["W_up"].to(dev)
     W_down = ffn["W_down"].to(dev)
-    H = ffn["H"].to(dev)
     dY = wg["dY"].to(dev)
     v = synthetic.qadamw()["v"].to(dev)
 
@@ -400,7 +400,9 @@ def main():
     qh = alloc(TOKENS, FFN, p_h)
     qwd = alloc(HIDDEN, FFN, p_wd)
     qdy = alloc(TOKENS, FFN, p_dy)
-    Y_up = torch.empty((TOKENS, FFN), dtype=torch.float32, device=dev)
+    H = torch.empty((TOKENS, FFN), dtype=torch.bfloat16, device=dev)   # the up projection's output
+    T_up = torch.empty((nv.load_library().nvfp4_gemm_tiles(TOKENS, FFN),), dtype=torch.float32,
+                       device=dev)
     Y_down = torch.empty((TOKENS, HIDDEN), dtype=torch.float32, device=dev)
     dX = torch.empty((TOKENS, HIDDEN), dtype=torch.float32, device=dev)
     dW = torch.empty((FFN, HIDDEN), dtype=torch.float32, device=dev)
@@ -431,8 +433,8 @@ def main():
     work = {
         "quant_X_row+colRHT": ("quant", 2 * TOKENS * HIDDEN + 2 * qbytes(TOKENS, HIDDEN), 0),
         "quant_Wup_2d": ("quant", 2 * FFN * HIDDEN + 2 * qbytes(FFN, HIDDEN), 0),
-        "gemm_ffn_up": ("gemm", qbytes(TOKENS, HIDDEN) + qbytes(FFN, HIDDEN) + 4 * TOKENS * FFN,
-                        2 * TOKENS * FFN * HIDDEN),
+        "gemm_ffn_up": ("gemm", qbytes(TOKENS, HIDDEN) + qbytes(FFN, HIDDEN) + 2 * TOKENS * FFN
+                        + 4 * (TOKENS // 256) * (FFN // 256), 2 * TOKENS * FFN * HIDDEN),
         "quant_H_row": ("quant", 2 * TOKENS * FFN + qbytes(TOKENS, FFN), 0),
         "quant_Wdown_2d": ("quant", 2 * HIDDEN * FFN + qbytes(HIDDEN, FFN), 0),
         "gemm_ffn_down": ("gemm", qbytes(TOKENS, FFN) + qbytes(HIDDEN, FFN) + 4 * TOKENS * HIDDEN,
@@ -453,8 +455,8 @@ def main():
     def calls():
         yield "quant_X_row+colRHT", lambda: nv.nvfp4_quantize(X, p_x, qx[0], qx[1], qx[2])
         yield "quant_Wup_2d", lambda: nv.nvfp4_quantize(W_up, p_w, qw[0], qw[1], qw[2])
-        yield "gemm_ffn_up", lambda: nv.nvfp4_gemm(qx[0], qw[0], out=Y_up)
-        yield "quant_H_row", lambda: nv.nvfp4_quantize(H, p_h, qh[0], None, qh[2])
+        yield "gemm_ffn_up", lambda: nv.nvfp4_gemm_bf16(qx[0], qw[0], out=H, tile_amax=T_up)
+        yield "quant_H_row", lambda: nv.nvfp4_quantize(H, p_h, qh[0], None, amax_parts=T_up)
         yield "quant_Wdown_2d", lambda: nv.nvfp4_quantize(W_down, p_wd, qwd[0], None, qwd[2])
         yield "gemm_ffn_down", lambda: nv.nvfp4_gemm(qh[0], qwd[0], out=Y_down)
         yield "quant_dY_rowSR+colRHTSR", lambda: nv.nvfp4_quantize(dY, p_dy, qdy[0], qdy[1], qdy[2])
@@ -513,7 +515,7 @@ def main():
     q_ms = sum(kernels[n]["ms"] for n in q_names)
     up = kernels["gemm_ffn_up"]
     up_flops = work["gemm_ffn_up"][2]
-    roofline = {"bound": "mfma", "kernel": "k_gemm_sk (FFN-up 8192x9216x3072)",
+    roofline = {"bound": "mfma", "kernel": "k_gemm_dma<EpiBf16> (FFN-up 8192x9216x3072, bf16 out)",
                 "achieved": up["TFLOP/s"], "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(up["TFLOP/s"] / PEAK_F16_TFLOPS, 4),
                 "traffic": counters_for("gemm_ffn_up", "gemm")}
@@ -537,7 +539,8 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": "3B FFN linear hot path: 8192 tokens, hidden 3072, FFN 9216; "
-                               "fwd up+down, bwd up (dgrad, wgrad with RHT16+SR), "
+                               "fwd up (bf16 H with tile maxima) + down, "
+                               "bwd up (dgrad, wgrad with RHT16+SR), "
                                "Q-AdamW v 9216x3072 encode+decode, W_up dequantize",
                    "tokens": TOKENS, "hidden": HIDDEN, "ffn": FFN,
                    "gemm_shapes_MxNxK": ["8192x9216x3072", "8192x3072x9216", "8192x3072x9216",
@@ -671,6 +674,9 @@ def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream, ite
     b16 = torch.randn((HIDDEN, FFN), generator=g16, device=dev, dtype=torch.float16)   # K-major, contiguous
     c16 = torch.empty((TOKENS, FFN), dtype=torch.float16, device=dev)
     dXl = torch.empty((TOKENS, HIDDEN), dtype=torch.float32, device=dev)
+    H16 = torch.empty((TOKENS, FFN), dtype=torch.bfloat16, device=dev)
+    T16 = torch.empty((nv.load_library().nvfp4_gemm_tiles(TOKENS, FFN),), dtype=torch.float32,
+                      device=dev)
     cases = {
         "quant_X_row+colRHT_4/6": (lambda: nv.nvfp4_quantize(X, p46x, qx[0], qx[1], qx[2]),
                                    2 * TOKENS * HIDDEN + 2 * qbytes(TOKENS, HIDDEN), 0),
@@ -703,9 +709,12 @@ def extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream, ite
         "gemm_qkv_8192x6144x3072": (lambda: nv.nvfp4_gemm(qa, qb, out=C),
                                     qbytes(M, K) + qbytes(N, K) + 4 * M * N, 2 * M * N * K),
         "hbm_copy_256MiB": (lambda: dst.copy_(src), 2 * (256 << 20), 0),
-        # the FFN-up GEMM timed like the next line (back to back), for a like-for-like view
+        # the FFN-up GEMM timed like the next line (back to back), for a like-for-like view:
+        # FP32 output (balanced schedule) and bf16 output with tile maxima (the step's)
         "gemm_ffn_up_back_to_back": (lambda: nv.nvfp4_gemm(qx[0], qw[0], out=Yl), 0,
                                      2 * TOKENS * FFN * HIDDEN),
+        "gemm_ffn_up_bf16_back_to_back": (lambda: nv.nvfp4_gemm_bf16(qx[0], qw[0], out=H16, tile_amax=T16),
+                                          0, 2 * TOKENS * FFN * HIDDEN),
         # context, not part of the path: the platform library's dense f16 GEMM (torch.matmul,
         # hipBLASLt) on the FFN-up shape with contiguous operands, the practical ceiling of
         # the f16 datapath on this part

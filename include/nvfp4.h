@@ -139,6 +139,22 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t
                    const nvfp4_quant_params* p, const nvfp4_qtensor* row_out,
                    const nvfp4_qtensor* col_out, void* ws, size_t ws_bytes, void* stream);
 
+/* nvfp4_quantize with the tensor amax taken from caller-supplied partial maxima instead of a
+ * first pass over x, so that x is read once.  The amax is the largest of amax_parts[0 ..
+ * n_parts), the same for both copies; with amax_parts holding the maxima of |x| over any
+ * cover of x (for instance nvfp4_gemm_bf16's tile maxima of the x it wrote), the copies are
+ * bit for bit those of nvfp4_quantize.  Passages: NVFP4 report sec. 2 (per-tensor amax ->
+ * FP32 tensor scale) and sec. 4 (mixed precision: BF16 GEMM outputs are the next layer's
+ * inputs).
+ *   amax_parts  device array of n_parts >= 1 floats (4-byte aligned), not written
+ * Copies with a Hadamard rotation (p->rht_row, p->rht_col) need the amax of the rotated
+ * values and are refused (NVFP4_ERR_MODE).  No workspace.  Other arguments and errors as in
+ * nvfp4_quantize. */
+int nvfp4_quantize_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                        const nvfp4_quant_params* p, const nvfp4_qtensor* row_out,
+                        const nvfp4_qtensor* col_out, const float* amax_parts, int64_t n_parts,
+                        void* stream);
+
 /* nvfp4_quantize without a workspace, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  * Arguments, results and errors are those of nvfp4_quantize with the same x, p and copies.
@@ -214,6 +230,22 @@ int nvfp4_dequantize(const nvfp4_qtensor* q, int64_t n, int64_t k, int out_dtype
  * (they depend on its compute-unit count through this split). */
 int nvfp4_gemm(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
                int64_t K, float* c, int64_t ldc, void* stream);
+
+/* Number of 256 x 256 output tiles of an M x N product (0 if either is <= 0). */
+int64_t nvfp4_gemm_tiles(int64_t M, int64_t N);
+
+/* nvfp4_gemm with C rounded once to bfloat16 (nearest-even) and each output tile's maximum
+ * of |C|.  Passages: NVFP4 report sec. 4 (GEMMs on FP4 inputs produce BF16 or FP32 outputs)
+ * and sec. 2 (the next quantize needs the tensor amax of this output).
+ *   c          bf16 [M][ldc], ldc >= N, 2-byte aligned
+ *   tile_amax  NULL, or nvfp4_gemm_tiles(M, N) floats (4-byte aligned): tile (i, j), rows
+ *              256 i .. and columns 256 j .., at index i * ceil(N/256) + j, gets the largest
+ *              |C| over its elements (a bf16 value; NaN elements are not counted)
+ * One workgroup per tile (no balanced split): every element is bf16_rne of the FP32 value
+ * nvfp4_gemm stores when it takes one workgroup per tile too.  Other arguments and errors
+ * as in nvfp4_gemm. */
+int nvfp4_gemm_bf16(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
+                    int64_t K, uint16_t* c, int64_t ldc, float* tile_amax, void* stream);
 
 /* The W4A4 GEMM with the LoRA-SVD low-rank term fused into its epilogue:
  *   C[M][N] = (nvfp4_gemm's product) + sum_j T[m][j] L[n][j].

@@ -33,7 +33,8 @@ EXPORTED = ["nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantiz
             "qadamw_step", "nvfp4_gemm_lora", "nvfp4_quantize_lora_workspace_bytes",
             "nvfp4_quantize_lora", "nvfp4_requantize_cols_workspace_bytes",
             "nvfp4_requantize_cols", "nvfp4_gemm_axpby", "nvfp4_ns_step_workspace_bytes",
-            "nvfp4_ns_step", "nvfp4_quantize_noalloc"]
+            "nvfp4_ns_step", "nvfp4_quantize_noalloc", "nvfp4_quantize_amax", "nvfp4_gemm_tiles",
+            "nvfp4_gemm_bf16"]
 
 
 class Nvfp4Error(RuntimeError):
@@ -89,6 +90,13 @@ def load_library(path: Optional[str] = None):
     lib.nvfp4_dequantize.argtypes = [P(QTensorC), i64, i64, ctypes.c_int, vp, i64, vp]
     lib.nvfp4_gemm.restype = ctypes.c_int
     lib.nvfp4_gemm.argtypes = [P(QTensorC), P(QTensorC), i64, i64, i64, vp, i64, vp]
+    lib.nvfp4_gemm_tiles.restype = i64
+    lib.nvfp4_gemm_tiles.argtypes = [i64, i64]
+    lib.nvfp4_gemm_bf16.restype = ctypes.c_int
+    lib.nvfp4_gemm_bf16.argtypes = [P(QTensorC), P(QTensorC), i64, i64, i64, vp, i64, vp, vp]
+    lib.nvfp4_quantize_amax.restype = ctypes.c_int
+    lib.nvfp4_quantize_amax.argtypes = [vp, ctypes.c_int, i64, i64, i64, P(QuantParams),
+                                        P(QTensorC), P(QTensorC), vp, i64, vp]
     lib.nvfp4_quantize_lora_workspace_bytes.restype = sz
     lib.nvfp4_quantize_lora_workspace_bytes.argtypes = [i64, i64, i64]
     lib.nvfp4_quantize_lora.restype = ctypes.c_int
@@ -185,11 +193,13 @@ def nvfp4_quantize_workspace_bytes(rows, cols, params):
     return int(load_library().nvfp4_quantize_workspace_bytes(rows, cols, ctypes.byref(params)))
 
 
-def nvfp4_quantize(x, params, row_out=None, col_out=None, workspace=None):
+def nvfp4_quantize(x, params, row_out=None, col_out=None, workspace=None, amax_parts=None):
     """Quantize a 2-D bf16/fp32 CUDA tensor (row stride may exceed its width).
 
     Returns (row_copy, col_copy); a copy not requested is None.  Output buffers and the
-    workspace are allocated with torch unless passed in."""
+    workspace are allocated with torch unless passed in.  amax_parts: a float32 CUDA tensor
+    of partial maxima of |x| (e.g. nvfp4_gemm_bf16's tile maxima) that replaces the amax
+    pass (copies without a Hadamard rotation only; no workspace is used)."""
     lib = load_library()
     _require_cuda(x)
     if x.dim() != 2 or x.stride(1) != 1:
@@ -206,11 +216,20 @@ def nvfp4_quantize(x, params, row_out=None, col_out=None, workspace=None):
         row_out = QTensor.empty(R, C, dev)
     if params.colwise and col_out is None:
         col_out = QTensor.empty(C, R, dev)
+    rc_ = row_out.c() if params.rowwise else None
+    cc_ = col_out.c() if params.colwise else None
+    if amax_parts is not None:
+        _require_cuda(amax_parts)
+        if amax_parts.dtype != torch.float32 or not amax_parts.is_contiguous():
+            raise Nvfp4Error("amax_parts must be a contiguous float32 tensor")
+        _check(lib.nvfp4_quantize_amax(_ptr(x), dt, R, C, x.stride(0), ctypes.byref(params),
+                                       ctypes.byref(rc_) if rc_ is not None else None,
+                                       ctypes.byref(cc_) if cc_ is not None else None,
+                                       _ptr(amax_parts), amax_parts.numel(), _stream(dev)))
+        return (row_out if params.rowwise else None), (col_out if params.colwise else None)
     need = nvfp4_quantize_workspace_bytes(R, C, params)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
-    rc_ = row_out.c() if params.rowwise else None
-    cc_ = col_out.c() if params.colwise else None
     rc = lib.nvfp4_quantize(_ptr(x), dt, R, C, x.stride(0), ctypes.byref(params),
                             ctypes.byref(rc_) if rc_ is not None else None,
                             ctypes.byref(cc_) if cc_ is not None else None,
@@ -270,6 +289,29 @@ def nvfp4_gemm(a, b, out=None):
     _check(lib.nvfp4_gemm(ctypes.byref(ac), ctypes.byref(bc), M, N, K, _ptr(out), out.stride(0),
                           _stream(out.device)))
     return out
+
+
+def nvfp4_gemm_bf16(a, b, out=None, tile_amax=None):
+    """C = A B^T rounded to bfloat16, with each 256 x 256 tile's maximum of |C|; returns
+    (out, tile_amax).  tile_amax: float32 [nvfp4_gemm_tiles(M, N)] (allocated if None)."""
+    lib = load_library()
+    _require_cuda(a.codes, b.codes)
+    M, K = a.shape
+    N, K2 = b.shape
+    if K != K2:
+        raise Nvfp4Error(f"K mismatch {K} vs {K2}")
+    dev = a.codes.device
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1:
+        raise Nvfp4Error("out must be a 2-D bfloat16 tensor with unit column stride")
+    if tile_amax is None:
+        tile_amax = torch.empty((max(int(lib.nvfp4_gemm_tiles(M, N)), 1),), dtype=torch.float32,
+                                device=dev)
+    ac, bc = a.c(), b.c()
+    _check(lib.nvfp4_gemm_bf16(ctypes.byref(ac), ctypes.byref(bc), M, N, K, _ptr(out),
+                               out.stride(0), _ptr(tile_amax), _stream(dev)))
+    return out, tile_amax
 
 
 def nvfp4_quantize_lora(x, params, lora_a, beta, row_out=None, col_out=None, lora_t=None,

@@ -89,13 +89,17 @@ struct GArgs {
     uint64_t sk_epoch;
     uint64_t sk_spin;
     int sk_test;
+    // EpiBf16: C as bfloat16 (row pitch ldc) and each tile's maximum of |C| (or null)
+    uint16_t* c16;
+    float* tmax;
 };
 
 // Epilogue variants: plain product; plus the LoRA-SVD low-rank term; alpha * product +
 // beta * D (the Newton-Schulz updates).
 // EpiPart: the raw accumulators of one K-part of an upper-triangle tile of A A^T go to a
 // partial buffer (k_syrk_reduce sums the parts and mirrors the result).
-enum { EpiPlain = 0, EpiLora = 1, EpiAxpby = 2, EpiPart = 3 };
+// EpiBf16: the plain product rounded to bfloat16, with each tile's maximum of |C|.
+enum { EpiPlain = 0, EpiLora = 1, EpiAxpby = 2, EpiPart = 3, EpiBf16 = 4 };
 
 // Packed tile layout: row r holds 64 bytes as four 16-byte chunks; chunk q sits at slot
 // q ^ (r/4 mod 4), which keeps both the staging stores (four lanes per row) and the
@@ -264,6 +268,50 @@ __device__ __forceinline__ void store_tile(const GArgs& g, const float16v (&acc)
     else store_rows<MODE, false>(g, acc, m0, n0, wm, wn, h, li, scale);
 }
 
+// bfloat16 output: C = bf16_rne(fl(acc s)), one block row at a time as in store_rows.
+// Returns this lane's maximum of fl(|acc| s) over the elements it stores (NaN ignored);
+// rounding is monotone, so the largest |C| is that maximum rounded to bf16.
+template <bool FULL>
+__device__ __forceinline__ float store_rows_bf16(const GArgs& g, const float16v (&acc)[4][4],
+                                                 int64_t m0, int64_t n0, int wm, int wn, int h,
+                                                 int li, float scale) {
+    const int64_t rbase = m0 + wm * 128 + 4 * h, cbase = n0 + wn * 128 + li;
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+            uint16_t* rowp = g.c16 + row * g.ldc + cbase;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (FULL || (row < g.M && cbase + j * 32 < g.N)) {
+                    const float y = acc[i][j][r] * scale;
+                    mx = fmaxf(mx, fabsf(y));
+                    __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, (__bf16)y), rowp + j * 32);
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return mx;
+}
+
+// The tile's maximum of |C| into tmax[tile row * tiles_n + tile column], as the bf16 value
+// (widened to FP32): a wave reduction, then the four waves' values through LDS (free after
+// the main loop).
+__device__ __forceinline__ void tile_max_out(const GArgs& g, uint8_t* lds, float mx, int64_t m0,
+                                             int64_t n0) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float* red = (float*)lds;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        g.tmax[(m0 / GBM) * g.tiles_n + n0 / GBN] = (float)(__bf16)m;
+    }
+}
+
 // The raw accumulators of the tile into its 256 x 256 slot of the partial buffer (row-major),
 // in the row order of store_tile.
 __device__ __forceinline__ void store_part(float* slot, const float16v (&acc)[4][4], int wm, int wn,
@@ -415,6 +463,12 @@ __device__ __forceinline__ void finish_tile(const GArgs& g, uint8_t* lds, float1
         store_tile<StAxpby>(g, acc, m0, n0, wm, wn, h, li, (*g.asg * *g.bsg) * g.alpha);
     } else if constexpr (EPI == EpiPart) {
         store_part(g.part + ((int64_t)blockIdx.x << 16), acc, wm, wn, h, li);
+    } else if constexpr (EPI == EpiBf16) {   // one workgroup per tile: mode is FinResult
+        const float scale = *g.asg * *g.bsg;
+        const float mx = m0 + GBM <= g.M && n0 + GBN <= g.N
+                             ? store_rows_bf16<true>(g, acc, m0, n0, wm, wn, h, li, scale)
+                             : store_rows_bf16<false>(g, acc, m0, n0, wm, wn, h, li, scale);
+        if (g.tmax) tile_max_out(g, lds, mx, m0, n0);
     } else {
         const float scale = mode == FinPark ? 1.0f : (mode == FinNan ? nan : *g.asg * *g.bsg);
         if (mode == FinAdd) store_tile<StAdd>(g, acc, m0, n0, wm, wn, h, li, scale);
@@ -1126,6 +1180,8 @@ int syrk_splitk(const nvfp4_qtensor* a, int64_t m, int64_t k, float* c, int64_t 
     g.sk_epoch = 0;
     g.sk_spin = 0;
     g.sk_test = 0;
+    g.c16 = nullptr;
+    g.tmax = nullptr;
     const int T = (int)(m / GBM), ntri = T * (T + 1) / 2;
     g.tiles_m = T;
     g.tiles_n = T;
@@ -1175,15 +1231,17 @@ static uint64_t next_epoch(int dev) {
     return epoch[dev & 63].fetch_add(1) + 1;
 }
 
+// c16: bf16 output instead of c, with the tile maxima in tmax (may be null).
 static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
                        int64_t K, float* c, int64_t ldc, const uint16_t* lt, const uint16_t* lb,
                        int64_t lr, const float* d, int64_t ldd, float alpha, float beta,
-                       void* stream) {
+                       void* stream, uint16_t* c16 = nullptr, float* tmax = nullptr) {
     if (!a || !b || !a->gscale || !b->gscale) return NVFP4_ERR_NULL;
     if (M < 0 || N < 0 || K < 0 || K % 32 || ldc < N) return NVFP4_ERR_SHAPE;
     if (lr < 0 || lr % 16) return NVFP4_ERR_SHAPE;
     if (M == 0 || N == 0) return NVFP4_OK;
-    if (!c) return NVFP4_ERR_NULL;
+    if (!c && !c16) return NVFP4_ERR_NULL;
+    if (((uintptr_t)c16 & 1) || ((uintptr_t)tmax & 3)) return NVFP4_ERR_ALIGN;
     if (K > 0 && (!a->codes || !a->scales || !b->codes || !b->scales)) return NVFP4_ERR_NULL;
     if (lr > 0 && (!lt || !lb)) return NVFP4_ERR_NULL;
     if (d && ldd < N) return NVFP4_ERR_SHAPE;
@@ -1211,7 +1269,9 @@ static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M
     g.sk_epoch = 0;
     g.sk_spin = 0;
     g.sk_test = 0;
-    const int epi = d ? EpiAxpby : (lr > 0 ? EpiLora : EpiPlain);
+    g.c16 = c16;
+    g.tmax = tmax;
+    const int epi = c16 ? EpiBf16 : d ? EpiAxpby : (lr > 0 ? EpiLora : EpiPlain);
     const int64_t tiles_m = (M + GBM - 1) / GBM, tiles_n = (N + GBN - 1) / GBN;
     g.tiles_m = (int)tiles_m;
     g.tiles_n = (int)tiles_n;
@@ -1222,10 +1282,11 @@ static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M
     const int64_t kbytes = K / 2, limit = (int64_t)kOutOfRange;
     const bool direct = K > 0 && K % 64 == 0 && ((uintptr_t)a->scales & 3) == 0 &&
                         ((uintptr_t)b->scales & 3) == 0 && M * kbytes < limit && N * kbytes < limit;
-    const void* fns[2][3] = {{(const void*)k_gemm<EpiPlain>, (const void*)k_gemm<EpiLora>,
-                              (const void*)k_gemm<EpiAxpby>},
+    const void* fns[2][5] = {{(const void*)k_gemm<EpiPlain>, (const void*)k_gemm<EpiLora>,
+                              (const void*)k_gemm<EpiAxpby>, nullptr, (const void*)k_gemm<EpiBf16>},
                              {(const void*)k_gemm_dma<EpiPlain>, (const void*)k_gemm_dma<EpiLora>,
-                              (const void*)k_gemm_dma<EpiAxpby>}};
+                              (const void*)k_gemm_dma<EpiAxpby>, nullptr,
+                              (const void*)k_gemm_dma<EpiBf16>}};
     const void* fn = fns[direct ? 1 : 0][epi];
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                             direct ? kGemmDmaLds : kGemmLds) != hipSuccess)
@@ -1254,10 +1315,12 @@ static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M
     if (direct) {
         if (epi == EpiAxpby) k_gemm_dma<EpiAxpby><<<grid, GThreads, kGemmDmaLds, st>>>(g);
         else if (epi == EpiLora) k_gemm_dma<EpiLora><<<grid, GThreads, kGemmDmaLds, st>>>(g);
+        else if (epi == EpiBf16) k_gemm_dma<EpiBf16><<<grid, GThreads, kGemmDmaLds, st>>>(g);
         else k_gemm_dma<EpiPlain><<<grid, GThreads, kGemmDmaLds, st>>>(g);
     } else {
         if (epi == EpiAxpby) k_gemm<EpiAxpby><<<grid, GThreads, kGemmLds, st>>>(g);
         else if (epi == EpiLora) k_gemm<EpiLora><<<grid, GThreads, kGemmLds, st>>>(g);
+        else if (epi == EpiBf16) k_gemm<EpiBf16><<<grid, GThreads, kGemmLds, st>>>(g);
         else k_gemm<EpiPlain><<<grid, GThreads, kGemmLds, st>>>(g);
     }
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
@@ -1266,6 +1329,19 @@ static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M
 extern "C" int nvfp4_gemm(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
                           int64_t K, float* c, int64_t ldc, void* stream) {
     return gemm_launch(a, b, M, N, K, c, ldc, nullptr, nullptr, 0, nullptr, 0, 1.0f, 0.0f, stream);
+}
+
+extern "C" int64_t nvfp4_gemm_tiles(int64_t M, int64_t N) {
+    if (M <= 0 || N <= 0) return 0;
+    return ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
+}
+
+extern "C" int nvfp4_gemm_bf16(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M,
+                               int64_t N, int64_t K, uint16_t* c, int64_t ldc, float* tile_amax,
+                               void* stream) {
+    if (M > 0 && N > 0 && !c) return NVFP4_ERR_NULL;
+    return gemm_launch(a, b, M, N, K, nullptr, ldc, nullptr, nullptr, 0, nullptr, 0, 1.0f, 0.0f,
+                       stream, c, tile_amax);
 }
 
 extern "C" int nvfp4_gemm_lora(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M,

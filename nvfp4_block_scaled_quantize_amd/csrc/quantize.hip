@@ -178,12 +178,14 @@ static int scratch_of_current_device(void** out) {
 }
 
 // use_scratch: the partial maxima go to the current device's copy of `scratch` (ws and
-// ws_bytes are ignored).
+// ws_bytes are ignored).  given (n_given of them): the caller's partial maxima of |x|, which
+// replace the first pass for both copies (no workspace is used).
 static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
                          const nvfp4_quant_params* p, const nvfp4_qtensor* row_out,
                          const nvfp4_qtensor* col_out, const uint16_t* lora_a, int64_t rank,
                          float beta, uint16_t* lora_t, void* ws, size_t ws_bytes, void* stream,
-                         bool use_scratch = false) {
+                         bool use_scratch = false, const float* given = nullptr,
+                         int64_t n_given = 0) {
     if (!p) return NVFP4_ERR_NULL;
     if (dtype != NVFP4_F32 && dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
     if (rows < 0 || cols < 0 || rows % 16 || cols % 16 || ld_x < cols) return NVFP4_ERR_SHAPE;
@@ -213,15 +215,22 @@ static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, i
     if (!x) return NVFP4_ERR_NULL;
     const int64_t esize = dtype == NVFP4_BF16 ? 2 : 4;
     if (!aligned(x, 16) || (ld_x * esize) % 16) return NVFP4_ERR_ALIGN;
-    const size_t need = lora_t ? nvfp4_quantize_lora_workspace_bytes(rows, cols, rank)
+    if (given) {
+        // the maxima are of the unrotated values: a copy with a Hadamard rotation needs its own
+        if (lora_t || (p->rowwise && p->rht_row) || (p->colwise && p->rht_col)) return NVFP4_ERR_MODE;
+        if (n_given < 1 || n_given > (1 << 30)) return NVFP4_ERR_SHAPE;
+        if (!aligned(given, 4)) return NVFP4_ERR_ALIGN;
+    }
+    const size_t need = given ? 0
+                      : lora_t ? nvfp4_quantize_lora_workspace_bytes(rows, cols, rank)
                                : nvfp4_quantize_workspace_bytes(rows, cols, p);
-    if (use_scratch) {
+    if (use_scratch && !given) {
         if (lora_t || need > sizeof(scratch)) return NVFP4_ERR_WORKSPACE;
         if ((rc = scratch_of_current_device(&ws)) != NVFP4_OK) return rc;
         ws_bytes = sizeof(scratch);
     }
-    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
-    if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
+    if (!given && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
+    if (!given && !aligned(ws, 16)) return NVFP4_ERR_ALIGN;
 
     QArgs a;
     a.in_codes = nullptr;
@@ -267,9 +276,14 @@ static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, i
         a.lora_parts = (int)sp.parts;
         a.lora_kp = sp.kp;
         a.lora_beta = beta;
+    } else if (given) {
+        a.partial = const_cast<float*>(given);   // read only: no first pass writes it
+        a.npart = (int)n_given;
     } else {
         a.npart = (int)amax_parts(rows, cols);
     }
+    a.cpart = given ? 0 : a.npart;
+    a.amax_given = given != nullptr;
     const int f = a.sr_row | (a.sr_col << 1) | (a.rht_row << 2) | (a.rht_col << 3);
     if (a.is_bf16)
         (f < 8 ? launch_quant_bf16_lo : launch_quant_bf16_hi)(f, a, st);
@@ -284,6 +298,15 @@ extern "C" int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t co
                               void* stream) {
     return quantize_impl(x, dtype, rows, cols, ld_x, p, row_out, col_out, nullptr, 0, 0.0f,
                          nullptr, ws, ws_bytes, stream);
+}
+
+extern "C" int nvfp4_quantize_amax(const void* x, int dtype, int64_t rows, int64_t cols,
+                                   int64_t ld_x, const nvfp4_quant_params* p,
+                                   const nvfp4_qtensor* row_out, const nvfp4_qtensor* col_out,
+                                   const float* amax_parts, int64_t n_parts, void* stream) {
+    if (!amax_parts) return NVFP4_ERR_NULL;
+    return quantize_impl(x, dtype, rows, cols, ld_x, p, row_out, col_out, nullptr, 0, 0.0f,
+                         nullptr, nullptr, 0, stream, false, amax_parts, n_parts);
 }
 
 extern "C" int nvfp4_quantize_noalloc(const void* x, int dtype, int64_t rows, int64_t cols,
@@ -397,6 +420,8 @@ extern "C" int nvfp4_requantize_cols(const nvfp4_qtensor* row_in, int64_t rows, 
     a.lora_kp = 0;
     a.lora_beta = 0.0f;
     a.npart = (int)amax_parts(rows, cols);
+    a.cpart = a.npart;
+    a.amax_given = 0;
     launch_requant_cols((a.sr_col << 1) | (a.rht_col << 3), a, st);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }

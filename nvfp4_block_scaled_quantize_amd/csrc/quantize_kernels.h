@@ -51,6 +51,10 @@ struct QArgs {
     int tiles_c;
     int ntiles;
     int npart;       // first-pass workgroups, one partial maximum each per copy
+    // offset of the columnwise copy's partials in `partial` (npart; 0 when the caller supplies
+    // the maxima, which then serve both copies); amax_given: no first pass is launched
+    int cpart;
+    int amax_given;
     // LoRA-SVD down-projection (lora_t null: none): lora_t[rows][lora_r] = BF16(beta x a^T)
     // with a = lora_a[lora_r][cols]; the first pass leaves one FP32 partial per K-part of
     // lora_kp columns in lora_part[lora_parts][rows][lora_r], the encode pass sums them.
@@ -537,7 +541,7 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
         for (int u = 0; u < 3; ++u) {
             const int i = min(t + kThreads * u, a.npart - 1);
             pmr[u] = a.partial[i];
-            pmc[u] = a.partial[a.npart + i];
+            pmc[u] = a.partial[a.cpart + i];
         }
         // A lane past the tensor's edge (whole 16-row groups and 8-column halves of whole
         // 16-column blocks, so its pair and its column blocks are past it too) encodes the
@@ -564,7 +568,7 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
         mc = fmaxf(fmaxf(pmc[0], pmc[1]), pmc[2]);
         for (int i = t + 3 * kThreads; i < a.npart; i += kThreads) {
             mr = fmaxf(mr, a.partial[i]);
-            mc = fmaxf(mc, a.partial[a.npart + i]);
+            mc = fmaxf(mc, a.partial[a.cpart + i]);
         }
     } else {
         // With the rowwise rotation the whole patch is sign-flipped before the first row is
@@ -580,7 +584,7 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
             for (int u = 0; u < 4; ++u) {
                 const int i = i0 + u * kThreads;
                 pr[u] = i < a.npart ? a.partial[i] : 0.0f;
-                pc[u] = i < a.npart ? a.partial[a.npart + i] : 0.0f;
+                pc[u] = i < a.npart ? a.partial[a.cpart + i] : 0.0f;
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) { mr = fmaxf(mr, pr[u]); mc = fmaxf(mc, pc[u]); }
@@ -994,9 +998,9 @@ template <int IN, int F>
 void launch_quant(const QArgs& a, hipStream_t st) {
     if constexpr (IN == 1) {
         if (a.lora_t) launch_amax_lora<(F >> 2)>(a, st);
-        else k_amax<IN, (F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
+        else if (!a.amax_given) k_amax<IN, (F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
     } else {
-        k_amax<IN, (F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
+        if (!a.amax_given) k_amax<IN, (F >> 2)><<<a.npart, kThreads, 0, st>>>(a);
     }
     k_encode<IN, F><<<a.ntiles, kThreads, 0, st>>>(a);
 }

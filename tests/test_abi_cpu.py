@@ -149,6 +149,34 @@ def test_quantize_lora_argument_errors(nv):
     assert need >= 2 * 8192 * 64 * 4
 
 
+def test_gemm_bf16_and_quantize_amax_argument_errors(nv):
+    """The bf16-output GEMM and the quantize with caller-supplied maxima, refused before
+    anything is enqueued."""
+    lib = nv.load_library()
+    a, b = _qt(FAKE), _qt(FAKE + 0x100000)
+    c = ctypes.c_void_p(FAKE + 0x200000)
+    tm = ctypes.c_void_p(FAKE + 0x280000)
+    g = lambda M, N, K, cc=c, t=tm: lib.nvfp4_gemm_bf16(ctypes.byref(a), ctypes.byref(b), M, N, K,
+                                                         cc, N, t, None)
+    assert g(16, 16, 32, cc=None) == -1                             # no output
+    assert g(16, 16, 32, cc=ctypes.c_void_p(FAKE + 0x200001)) == -3  # bf16 output misaligned
+    assert g(16, 16, 32, t=ctypes.c_void_p(FAKE + 0x280002)) == -3   # tile maxima misaligned
+    assert g(16, 16, 48) == -2                                       # K % 32
+    assert g(0, 16, 32) == 0                                         # empty
+    assert lib.nvfp4_gemm_tiles(8192, 9216) == 32 * 36
+    assert lib.nvfp4_gemm_tiles(257, 1) == 2 and lib.nvfp4_gemm_tiles(0, 5) == 0
+    q = _qt(FAKE + 0x300000)
+    x = ctypes.c_void_p(FAKE + 0x400000)
+    parts = ctypes.c_void_p(FAKE + 0x500000)
+    qa = lambda params, pp=parts, n=4: lib.nvfp4_quantize_amax(
+        x, 1, 64, 64, 64, ctypes.byref(params), ctypes.byref(q), ctypes.byref(q), pp, n, None)
+    assert qa(nv.quant_params(rowwise=True, rht_row=True)) == -5             # rotated copy
+    assert qa(nv.quant_params(rowwise=True, colwise=True, rht_col=True)) == -5
+    assert qa(nv.quant_params(rowwise=True), n=0) == -2                      # no maxima
+    assert qa(nv.quant_params(rowwise=True), pp=None) == -1
+    assert qa(nv.quant_params(rowwise=True), pp=ctypes.c_void_p(FAKE + 0x500002)) == -3
+
+
 def test_gemm_and_dequantize_argument_errors(nv):
     lib = nv.load_library()
     a, b = _qt(FAKE), _qt(FAKE + 0x100000)
