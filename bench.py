@@ -557,6 +557,12 @@ def main():
     out["qadamw_v_error"] = qadamw_error(nv, torch, v, v_out)
     out["kernels_isolated"] = isolated(torch, dev, calls, work, stream)
     out["extras"] = extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream)
+    # each memory-bound kernel's rate also as a fraction of what a plain device copy reaches
+    copy_gbps = out["extras"]["hbm_copy_256MiB"]["GB/s"]
+    out["copy_rate_GB/s"] = copy_gbps
+    for name, (kind, nbytes, flops) in work.items():
+        if kind != "gemm":
+            kernels[name]["frac_copy_rate"] = round(kernels[name]["GB/s"] / copy_gbps, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, synthetic, ffn)
     print(json.dumps(out))
