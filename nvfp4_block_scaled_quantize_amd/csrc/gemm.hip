@@ -27,7 +27,7 @@
 //  * Direct (K % 64 == 0, scale rows 4-byte aligned, each operand under 2 GiB): buffer
 //    loads with the LDS flag write global bytes straight into LDS, lane l of a load to
 //    LDS address base + 16 l (or 4 l), so neither VGPRs nor LDS store instructions are
-//    spent, and three stages are in flight.  A lane whose 16-byte chunk lies outside the
+//    spent, and four stages are in flight.  A lane whose 16-byte chunk lies outside the
 //    operand (row past M or N, k past K) gets an offset past the end of its buffer, and
 //    the buffer range check turns its load into zeros.  The choice of which global
 //    chunk each lane fetches lays the tile out in the swizzled order below.
@@ -51,7 +51,9 @@ constexpr int GThreads = 256;
 constexpr int kStageCodeBytes = GBM * 64;       // per operand
 constexpr int kStageScaleBytes = GBM * 8;       // per operand
 constexpr int kStageBytes = 2 * kStageCodeBytes + 2 * kStageScaleBytes;
-constexpr int kRegStages = 2, kDmaStages = 3;
+// Stage buffers in LDS: two for the register-staged path, four (144 KiB) for the direct
+// path, whose loads then run three stages ahead (three stages measured 1-3% slower).
+constexpr int kRegStages = 2, kDmaStages = 4;
 constexpr int kGemmLds = kRegStages * kStageBytes;
 constexpr int kGemmDmaLds = kDmaStages * kStageBytes;
 // direct loads per wave and stage: 4 + 4 code chunks, 2 + 2 scale words
@@ -796,16 +798,17 @@ __device__ __forceinline__ void piped_stage(const DmaCtx& c, int s, HalfFrags& l
     // carries the next stage's slot 0, and that half becomes VALU-bound.
 #pragma unroll
     for (int x = 0; x < 4; ++x) asm volatile("" : "+v"(av[x]), "+v"(bv[x]));
-    // Stage s + 3 refills this stage's buffer (out of range past the segment's last stage).
+    // Stage s + kDmaStages refills this stage's buffer (out of range past the segment's last
+    // stage).
     StageLoads L;
-    stage_loads(c, c.s0 + s + 3, c.lds0 + (s % kDmaStages) * kStageBytes, L);
-    // lo is dead: stage s + 1 must be in LDS (its loads were issued two stages ago, those
-    // of stage s + 2 may be in flight), and every wave is done with this stage's buffer
-    dma_wait_barrier<kDmaLoadsPerStage>();
+    stage_loads(c, c.s0 + s + kDmaStages, c.lds0 + (s % kDmaStages) * kStageBytes, L);
+    // lo is dead: stage s + 1 must be in LDS (the loads of the stages after it may be in
+    // flight), and every wave is done with this stage's buffer
+    dma_wait_barrier<(kDmaStages - 2) * kDmaLoadsPerStage>();
     const uint8_t* nxt = c.lds + ((s + 1) % kDmaStages) * kStageBytes;
     uint32_t nsa[4], nsb[4];
     // Slots 4 to 6: each MFMA with a quarter of the next slot's decode; the 12 loads of stage
-    // s + 3 go one per kDmaSpread MFMAs from slot 4's first MFMA on, and the reads of the
+    // s + kDmaStages go one per kDmaSpread MFMAs from slot 4's first MFMA on, and the reads of the
     // next stage's lo and scale words two per MFMA over the second half of slot 4.
     const auto extra = [&](auto J, auto K) {
         constexpr int g = J * 16 + K;
@@ -841,7 +844,7 @@ __device__ __forceinline__ void piped_stage(const DmaCtx& c, int s, HalfFrags& l
 }
 
 // Stages [c.s0, c.s0 + c.nst) of the tile at (c.m0, c.n0), c.nst >= 1, added onto acc: the
-// first three stages' direct loads, then the pipelined stages.  On return every direct load
+// first kDmaStages stages' direct loads, then the pipelined stages.  On return every direct load
 // has landed and every wave has passed the last stage's barrier; LDS holds nothing needed.
 __device__ __forceinline__ void run_stages(const DmaCtx& c, float16v (&acc)[4][4]) {
     for (int j = 0; j < kDmaStages; ++j) dma_stage(c, c.s0 + j, c.lds0 + j * kStageBytes);
