@@ -241,9 +241,13 @@ int64_t nvfp4_gemm_tiles(int64_t M, int64_t N);
  *   tile_amax  NULL, or nvfp4_gemm_tiles(M, N) floats (4-byte aligned): tile (i, j), rows
  *              256 i .. and columns 256 j .., at index i * ceil(N/256) + j, gets the largest
  *              |C| over its elements (a bf16 value; NaN elements are not counted)
- * One workgroup per tile (no balanced split): every element is bf16_rne of the FP32 value
- * nvfp4_gemm stores when it takes one workgroup per tile too.  Other arguments and errors
- * as in nvfp4_gemm. */
+ * Every element is bf16_rne of the FP32 value nvfp4_gemm stores when it takes one workgroup
+ * per tile.  When whole rounds of tiles (one per compute unit, rounded down to a multiple of
+ * 8) leave a last round at most half full, that round runs as twice as many 256 x 128 tiles,
+ * each over the whole K range with the MFMA order of a 256 x 256 tile; the first launch
+ * zeroes those tiles' maxima and the second combines its two halves' maxima with an atomic
+ * maximum (NVFP4_GEMM_SK=0 keeps one workgroup per tile).  Other arguments and errors as in
+ * nvfp4_gemm. */
 int nvfp4_gemm_bf16(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
                     int64_t K, uint16_t* c, int64_t ldc, float* tile_amax, void* stream);
 

@@ -94,6 +94,9 @@ struct GArgs {
     // EpiBf16: C as bfloat16 (row pitch ldc) and each tile's maximum of |C| (or null)
     uint16_t* c16;
     float* tmax;
+    // bf16 product with a last round of half-width tiles (k_gemm_half): sk_g workgroups per
+    // round, sk_rounds whole rounds, sk_rem remaining tiles; 0 when there is none
+    int sk_g;
 };
 
 // Epilogue variants: plain product; plus the LoRA-SVD low-rank term; alpha * product +
@@ -489,6 +492,22 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
     const int q = total / kXcds, r = total % kXcds;
     const int x = bid % kXcds, k = bid / kXcds;
     const int id = x * q + (x < r ? x : r) + k;
+    const int group = id / (kGroupRows * tiles_n);
+    const int first = group * kGroupRows;
+    const int rows = tiles_m - first < kGroupRows ? tiles_m - first : kGroupRows;
+    const int in = id - group * kGroupRows * tiles_n;
+    tm = first + in % rows;
+    tn = in / rows;
+}
+
+// Workgroup number of blockIdx b in a grid of G (G % 8 == 0) whose blocks go to the 8 XCDs in
+// turn: XCD x gets the contiguous numbers [x G/8, (x+1) G/8).
+__device__ __forceinline__ int sk_virtual(int b, int G) {
+    return (b & 7) * (G >> 3) + (b >> 3);
+}
+
+// Tile id -> (tm, tn): groups of kGroupRows tile rows, column by column within a group.
+__device__ __forceinline__ void grouped_tile(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int group = id / (kGroupRows * tiles_n);
     const int first = group * kGroupRows;
     const int rows = tiles_m - first < kGroupRows ? tiles_m - first : kGroupRows;
@@ -904,6 +923,18 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
         tri_tile(blockIdx.x - kp * ntri, g.tiles_m, tm, tn);
         c.s0 = (int)((int64_t)kp * nst_all / g.kparts);
         c.nst = (int)((int64_t)(kp + 1) * nst_all / g.kparts) - c.s0;
+    } else if (EPI == EpiBf16 && g.sk_g > 0) {
+        // whole rounds before a round of half-width tiles: block b takes tile id
+        // (b / G) G + sk_virtual(b mod G) (as the balanced FP32 kernel's whole rounds), and
+        // block 0 zeroes the remaining tiles' maxima, which k_gemm_half then combines
+        const int b = blockIdx.x, G = g.sk_g;
+        grouped_tile((b / G) * G + sk_virtual(b % G, G), g.tiles_m, g.tiles_n, tm, tn);
+        if (b == 0 && g.tmax)
+            for (int i = c.t; i < g.sk_rem; i += GThreads) {
+                int rm, rn;
+                grouped_tile(g.sk_rounds * G + i, g.tiles_m, g.tiles_n, rm, rn);
+                g.tmax[rm * g.tiles_n + rn] = 0.0f;
+            }
     } else {
         tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
     }
@@ -914,6 +945,307 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
     zero_acc(acc);
     run_stages(c, acc);
     finish_tile<EPI>(g, lds, acc, c.m0, c.n0, c.wm, c.wn, c.h, c.li);
+}
+
+// ---------------------------------------------------------------- half-width tiles
+// A 256 x 128 tile per workgroup, on the direct path's stages and LDS layout (B rows 0..127
+// of each stage used): wave (wm, wn) owns a 128 x 64 sub-tile as 4 x 2 MFMA 32x32x16
+// accumulators.  Every element of C sees the same MFMAs in the same order as in a 256 x 256
+// tile, so the two agree bit for bit.  Used for the last round of a bf16 product when it is
+// at most half full: its tiles then run as twice as many half-width tiles, each over the
+// whole K range, so no partial sums are handed between workgroups.  A wave issues 9 direct
+// loads per stage: 4 + 2 code chunks, 2 + 1 scale words (A, then B).
+constexpr int kNrLoadsPerStage = 9;
+
+struct NrLoads {
+    uint32_t ca[4], sa[2], cb[2], sb;
+    uint32_t buf;
+};
+struct NrHalf {
+    uint4 a[4], b[2];
+};
+struct NrPairs {
+    half2v a[4], b[2];
+};
+
+__device__ __forceinline__ void nr_stage_loads(const DmaCtx& c, int s, uint32_t buf, NrLoads& L) {
+    const bool live = s < c.s0 + c.nst;
+    const uint32_t k0b = (uint32_t)s * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = i * 256 + c.t, row = p >> 2, q = p & 3;
+        const uint32_t off = k0b + (uint32_t)((q ^ ((row >> 2) & 3)) << 4);
+        const bool kin = live && off < c.kbytes;
+        L.ca[i] = (kin && c.m0 + row < c.g.M) ? (uint32_t)(c.m0 + row) * c.kbytes + off : kOutOfRange;
+        if (i < 2)
+            L.cb[i] = (kin && c.n0 + row < c.g.N) ? (uint32_t)(c.n0 + row) * c.kbytes + off : kOutOfRange;
+    }
+    const uint32_t kb0 = (uint32_t)s * 8;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int j = i * 256 + c.t, row = j >> 1;
+        const uint32_t kb = kb0 + 4 * (j & 1);
+        const bool kin = live && kb < c.kblocks;
+        L.sa[i] = (kin && c.m0 + row < c.g.M) ? (uint32_t)(c.m0 + row) * c.kblocks + kb : kOutOfRange;
+        if (i == 0)
+            L.sb = (kin && c.n0 + row < c.g.N) ? (uint32_t)(c.n0 + row) * c.kblocks + kb : kOutOfRange;
+    }
+    L.buf = buf;
+}
+
+// Load K of a stage: code chunks of A (0..3) and B (4, 5), scale words of A (6, 7) and B (8).
+template <int K>
+__device__ __forceinline__ void nr_issue(const Rsrc4& rs, const NrLoads& L, int wid) {
+    if constexpr (K < 4) {
+        dma16(rs.ac, L.buf + (uint32_t)(K * 256 + wid * 64) * 16, L.ca[K]);
+    } else if constexpr (K < 6) {
+        dma16(rs.bc, L.buf + kStageCodeBytes + (uint32_t)((K - 4) * 256 + wid * 64) * 16, L.cb[K - 4]);
+    } else if constexpr (K < 8) {
+        dma4(rs.as, L.buf + 2 * kStageCodeBytes + (uint32_t)((K - 6) * 256 + wid * 64) * 4, L.sa[K - 6]);
+    } else {
+        dma4(rs.bs, L.buf + 2 * kStageCodeBytes + kStageScaleBytes + (uint32_t)(wid * 64) * 4, L.sb);
+    }
+}
+
+__device__ __forceinline__ void nr_dma_stage(const DmaCtx& c, int s, uint32_t buf) {
+    NrLoads L;
+    nr_stage_loads(c, s, buf, L);
+    static_for<0, kNrLoadsPerStage>([&](auto K) { nr_issue<K>(c.rs, L, c.wid); });
+}
+
+__device__ __forceinline__ void nr_read_half(const uint8_t* cur, int c2, const DmaCtx& c, NrHalf& f) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+        f.a[x] = *(const uint4*)(cur + code_off(c.wm * 128 + x * 32 + c.li, 2 * c.h + c2));
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+        f.b[y] = *(const uint4*)(cur + kStageCodeBytes + code_off(c.wn * 64 + y * 32 + c.li, 2 * c.h + c2));
+}
+
+__device__ __forceinline__ void nr_read_scales(const uint8_t* cur, const DmaCtx& c, uint32_t (&sa)[4],
+                                               uint32_t (&sb)[2]) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+        sa[x] = *(const uint32_t*)(cur + 2 * kStageCodeBytes + (c.wm * 128 + x * 32 + c.li) * 8 + 4 * c.h);
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+        sb[y] = *(const uint32_t*)(cur + 2 * kStageCodeBytes + kStageScaleBytes +
+                                   (c.wn * 64 + y * 32 + c.li) * 8 + 4 * c.h);
+}
+
+template <int B>
+__device__ __forceinline__ void nr_make_pairs(const uint32_t (&sa)[4], const uint32_t (&sb)[2], NrPairs& p) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) p.a[x] = scale_pair<B>(sa[x]);
+#pragma unroll
+    for (int y = 0; y < 2; ++y) p.b[y] = scale_pair<B>(sb[y]);
+}
+
+template <int T>
+__device__ __forceinline__ void nr_decode_slot(const NrHalf& f, const NrPairs& p, half8v (&av)[4],
+                                               half8v (&bv)[2]) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) av[x] = decode8(dword_of(f.a[x], T & 3), p.a[x]);
+#pragma unroll
+    for (int y = 0; y < 2; ++y) bv[y] = decode8(dword_of(f.b[y], T & 3), p.b[y]);
+}
+
+__device__ __forceinline__ void nr_mma(const half8v (&av)[4], const half8v (&bv)[2], float16v (&acc)[4][2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+}
+
+// Each of a slot's 8 MFMAs followed by K VALU instructions.
+template <int K>
+__device__ __forceinline__ void nr_pace() {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, K, 0);
+    }
+}
+
+// A slot's 8 MFMAs on (av, bv), the next slot T's decode (12 half-operand steps) spread over
+// them, and X(k) after MFMA k, each in a scheduling region of its own.
+template <int T, class Fx>
+__device__ __forceinline__ void nr_slot_steps(const half8v (&av)[4], const half8v (&bv)[2],
+                                              float16v (&acc)[4][2], const NrHalf& f,
+                                              const NrPairs& p, half8v (&an)[4], half8v (&bn)[2],
+                                              Fx&& X) {
+    static_for<0, 8>([&](auto K) {
+        constexpr int k = K;
+        acc[k >> 1][k & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[k >> 1], bv[k & 1],
+                                                                    acc[k >> 1][k & 1], 0, 0, 0);
+        static_for<(12 * k) / 8, (12 * (k + 1)) / 8>([&](auto D) {
+            constexpr int d = D, o = d >> 1, q = d & 1;
+            if constexpr (o < 4) decode4<q>(dword_of(f.a[o], T & 3), p.a[o], an[o]);
+            else decode4<q>(dword_of(f.b[o - 4], T & 3), p.b[o - 4], bn[o - 4]);
+        });
+        X(K);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+// Stage s, pipelined as piped_stage: on entry lo, hi, sa, sb hold stage s, p the scale pairs
+// of its block 0 and (av, bv) its decoded slot 0; on return the same for stage s + 1.
+__device__ __forceinline__ void nr_piped_stage(const DmaCtx& c, int s, NrHalf& lo, NrHalf& hi,
+                                               uint32_t (&sa)[4], uint32_t (&sb)[2], NrPairs& p,
+                                               half8v (&av)[4], half8v (&bv)[2],
+                                               float16v (&acc)[4][2]) {
+    half8v an[4], bn[2];
+    nr_decode_slot<1>(lo, p, an, bn);
+    nr_mma(av, bv, acc);
+    nr_pace<6>();
+    nr_make_pairs<1>(sa, sb, p);
+    nr_decode_slot<2>(lo, p, av, bv);
+    nr_mma(an, bn, acc);
+    nr_pace<7>();
+    nr_decode_slot<3>(lo, p, an, bn);
+    nr_mma(av, bv, acc);
+    nr_pace<6>();
+    nr_make_pairs<2>(sa, sb, p);
+    nr_decode_slot<4>(hi, p, av, bv);
+    nr_mma(an, bn, acc);
+    nr_pace<7>();
+#pragma unroll
+    for (int x = 0; x < 4; ++x) asm volatile("" : "+v"(av[x]));
+#pragma unroll
+    for (int y = 0; y < 2; ++y) asm volatile("" : "+v"(bv[y]));
+    NrLoads L;
+    nr_stage_loads(c, c.s0 + s + kDmaStages, c.lds0 + (s % kDmaStages) * kStageBytes, L);
+    // stage s + 1 is in LDS, every wave is done with stage s's buffer
+    dma_wait_barrier<(kDmaStages - 2) * kNrLoadsPerStage>();
+    const uint8_t* nxt = c.lds + ((s + 1) % kDmaStages) * kStageBytes;
+    uint32_t nsa[4], nsb[2];
+    // slots 5 to 7: the 9 loads of stage s + kDmaStages, one per kDmaSpread MFMAs; slot 5
+    // also reads the next stage's lo and scale words, two per MFMA from its third MFMA on
+    const auto extra = [&](auto J, auto K) {
+        constexpr int g = J * 8 + K;
+        if constexpr (g % kDmaSpread == 0 && g / kDmaSpread < kNrLoadsPerStage)
+            nr_issue<g / kDmaSpread>(c.rs, L, c.wid);
+        if constexpr (J == 0 && K >= 2) {
+            constexpr int e0 = 2 * (K - 2);
+            static_for<e0, e0 + 2>([&](auto E) {
+                constexpr int e = E;
+                if constexpr (e < 4) {
+                    lo.a[e] = *(const uint4*)(nxt + code_off(c.wm * 128 + e * 32 + c.li, 2 * c.h));
+                } else if constexpr (e < 6) {
+                    lo.b[e - 4] = *(const uint4*)(nxt + kStageCodeBytes +
+                                                  code_off(c.wn * 64 + (e - 4) * 32 + c.li, 2 * c.h));
+                } else if constexpr (e < 10) {
+                    nsa[e - 6] = *(const uint32_t*)(nxt + 2 * kStageCodeBytes +
+                                                    (c.wm * 128 + (e - 6) * 32 + c.li) * 8 + 4 * c.h);
+                } else {
+                    nsb[e - 10] = *(const uint32_t*)(nxt + 2 * kStageCodeBytes + kStageScaleBytes +
+                                                     (c.wn * 64 + (e - 10) * 32 + c.li) * 8 + 4 * c.h);
+                }
+            });
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    nr_slot_steps<5>(av, bv, acc, hi, p, an, bn, [&](auto K) { extra(I0{}, K); });
+    nr_make_pairs<3>(sa, sb, p);
+    nr_slot_steps<6>(an, bn, acc, hi, p, av, bv, [&](auto K) { extra(I1{}, K); });
+    nr_slot_steps<7>(av, bv, acc, hi, p, an, bn, [&](auto K) { extra(I2{}, K); });
+    nr_read_half(nxt, 1, c, hi);
+    nr_make_pairs<0>(nsa, nsb, p);
+    nr_decode_slot<0>(lo, p, av, bv);
+    nr_mma(an, bn, acc);
+    nr_pace<7>();
+#pragma unroll
+    for (int x = 0; x < 4; ++x) sa[x] = nsa[x];
+#pragma unroll
+    for (int y = 0; y < 2; ++y) sb[y] = nsb[y];
+}
+
+// bf16 output of a half-width tile, as store_rows_bf16 with a 128 x 64 sub-tile per wave.
+template <bool FULL>
+__device__ __forceinline__ float nr_store_bf16(const GArgs& g, const float16v (&acc)[4][2], const DmaCtx& c,
+                                               float scale) {
+    const int64_t rbase = c.m0 + c.wm * 128 + 4 * c.h, cbase = c.n0 + c.wn * 64 + c.li;
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+            uint16_t* rowp = g.c16 + row * g.ldc + cbase;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                if (FULL || (row < g.M && cbase + j * 32 < g.N)) {
+                    const float y = acc[i][j][r] * scale;
+                    mx = fmaxf(mx, fabsf(y));
+                    __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, (__bf16)y), rowp + j * 32);
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return mx;
+}
+
+// The last round of a bf16 product as half-width tiles: block u takes column half `half` of
+// tile id base + i (base = sk_rounds sk_g, grouped_tile order), both halves of a tile on one
+// XCD when sk_rem % 8 == 0 (blocks 16 k + x and 16 k + 8 + x take tile 8 k + x), else on
+// blocks 2 i and 2 i + 1.  The tile's maximum of |C| is the larger of its halves' maxima,
+// combined by an atomic maximum on the binary32 bits (non-negative values order like their
+// bits) into an entry that k_gemm_dma<EpiBf16> zeroed before this launch.
+__global__ __launch_bounds__(GThreads, 1) void k_gemm_half(GArgs g) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    DmaCtx c;
+    init_ctx(c, g, lds);
+    const int u = blockIdx.x, base = g.sk_rounds * g.sk_g;
+    const bool xcd = (g.sk_rem & 7) == 0;
+    const int i = xcd ? (u >> 4) * 8 + (u & 7) : u >> 1;
+    const int half = xcd ? (u >> 3) & 1 : u & 1;
+    int tm, tn;
+    grouped_tile(base + i, g.tiles_m, g.tiles_n, tm, tn);
+    c.m0 = (int64_t)tm * GBM;
+    c.n0 = (int64_t)tn * GBN + half * (GBN / 2);
+    if (c.n0 >= g.N) return;   // a right half wholly past the last column (uniform)
+    c.s0 = 0;
+    c.nst = (int)((g.K + GBK - 1) / GBK);
+
+    float16v acc[4][2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+    for (int j = 0; j < kDmaStages; ++j) nr_dma_stage(c, j, c.lds0 + j * kStageBytes);
+    dma_wait_barrier<(kDmaStages - 1) * kNrLoadsPerStage>();
+    NrHalf lo, hi;
+    uint32_t sa[4], sb[2];
+    NrPairs p;
+    half8v av[4], bv[2];
+    nr_read_half(c.lds, 0, c, lo);
+    nr_read_half(c.lds, 1, c, hi);
+    nr_read_scales(c.lds, c, sa, sb);
+    nr_make_pairs<0>(sa, sb, p);
+    nr_decode_slot<0>(lo, p, av, bv);
+    for (int s = 0; s < c.nst; ++s) nr_piped_stage(c, s, lo, hi, sa, sb, p, av, bv, acc);
+    dma_wait_barrier<0>();
+
+    const float scale = *g.asg * *g.bsg;
+    float mx = c.m0 + GBM <= g.M && c.n0 + GBN / 2 <= g.N ? nr_store_bf16<true>(g, acc, c, scale)
+                                                           : nr_store_bf16<false>(g, acc, c, scale);
+    if (g.tmax) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        float* red = (float*)lds;
+        if ((c.t & 63) == 0) red[c.wid] = mx;
+        __syncthreads();
+        if (c.t == 0) {
+            const float m = (float)(__bf16)fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+            __hip_atomic_fetch_max((uint32_t*)&g.tmax[tm * g.tiles_n + tn], __float_as_uint(m),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 // ---------------------------------------------------------------- balanced schedule
@@ -946,19 +1278,6 @@ constexpr int kSkMaxGroups = 1024;
 __device__ uint64_t g_sk_flag[kSkMaxGroups];
 constexpr uint64_t kSkWriteTicks = 100000000ull;   // 1 s at 100 MHz: a reserved tail must publish
 
-__device__ __forceinline__ int sk_virtual(int b, int G) {   // G % 8 == 0
-    return (b & 7) * (G >> 3) + (b >> 3);
-}
-
-// Tile id -> (tm, tn): groups of kGroupRows tile rows, column by column within a group.
-__device__ __forceinline__ void grouped_tile(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
-    const int group = id / (kGroupRows * tiles_n);
-    const int first = group * kGroupRows;
-    const int rows = tiles_m - first < kGroupRows ? tiles_m - first : kGroupRows;
-    const int in = id - group * kGroupRows * tiles_n;
-    tm = first + in % rows;
-    tn = in / rows;
-}
 
 // Tail side: reserve the hand-off (1) unless the head has claimed the tile (0).  The caller
 // then writes the part and publishes it.
@@ -1274,6 +1593,7 @@ static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M
     g.sk_test = 0;
     g.c16 = c16;
     g.tmax = tmax;
+    g.sk_g = 0;
     const int epi = c16 ? EpiBf16 : d ? EpiAxpby : (lr > 0 ? EpiLora : EpiPlain);
     const int64_t tiles_m = (M + GBM - 1) / GBM, tiles_n = (N + GBN - 1) / GBN;
     g.tiles_m = (int)tiles_m;
@@ -1300,9 +1620,23 @@ static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M
     // holds the tail halves), and so does the low-rank one (in this loop its epilogue spills
     // and runs slower than the rounds it saves)
     int dev = 0;
-    const int G = direct && epi == EpiPlain && env_int("NVFP4_GEMM_SK", 1) ? sk_groups(&dev) : 0;
+    const int G = direct && (epi == EpiPlain || epi == EpiBf16) && env_int("NVFP4_GEMM_SK", 1)
+                      ? sk_groups(&dev) : 0;
     const int sk_nst = (int)((K + GBK - 1) / GBK), sk_rem = G > 0 ? (int)(grid % G) : 0;
-    if (G > 0 && sk_rem > 0 && 2 * sk_rem <= G && sk_nst >= 2) {
+    if (epi == EpiBf16 && sk_rem > 0 && 2 * sk_rem <= G && (int)(grid / G) > 0) {
+        // bf16: the whole rounds, then the remaining tiles as twice as many half-width tiles
+        // (k_gemm_half), each over the whole K range: the same sums as one workgroup per tile
+        if (hipFuncSetAttribute((const void*)k_gemm_half, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kGemmDmaLds) != hipSuccess)
+            return NVFP4_ERR_HIP;
+        g.sk_g = G;
+        g.sk_rounds = (int)(grid / G);
+        g.sk_rem = sk_rem;
+        k_gemm_dma<EpiBf16><<<g.sk_rounds * G, GThreads, kGemmDmaLds, st>>>(g);
+        k_gemm_half<<<2 * sk_rem, GThreads, kGemmDmaLds, st>>>(g);
+        return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+    }
+    if (epi == EpiPlain && sk_rem > 0 && 2 * sk_rem <= G && sk_nst >= 2) {
         if (hipFuncSetAttribute((const void*)k_gemm_sk<EpiPlain>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 kGemmDmaLds) != hipSuccess)
             return NVFP4_ERR_HIP;

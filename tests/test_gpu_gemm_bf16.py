@@ -2,16 +2,20 @@
 its amax from caller-supplied partial maxima (the two halves of a single-read quantize of a
 GEMM's output).
 
-nvfp4_gemm_bf16 (one workgroup per tile) stores bf16_rne of the FP32 result, so on every
-shape:
+nvfp4_gemm_bf16 stores bf16_rne of the FP32 result that one workgroup per tile forms (its last
+round, when at most half full after whole rounds, runs as half-width tiles whose elements see
+the same MFMAs in the same order), so on every shape:
   * the output is bit for bit nvfp4_gemm's FP32 output with one workgroup per tile
     (NVFP4_GEMM_SK=0) rounded to bfloat16 by torch, and within the GEMM tolerance plus one
     bf16 rounding of the oracle's binary64 product;
   * each tile maximum equals the largest |C| over that 256 x 256 tile of the output.
 nvfp4_quantize with amax_parts is bit for bit nvfp4_quantize of the same tensor whenever
 the parts' maximum is the tensor's amax (tile maxima, per-row maxima, one value).
-Shapes: 2000 x 4000 x 192 and 4112 x 4112 x 192 (shapes where nvfp4_gemm splits its last
-round); 300 x 520 x 256 has ragged tiles; K = 96 takes the generic staging path.
+Shapes: 2000 x 4000 x 192 (one round, half full); 4112 x 4112 x 192 (one whole round, then 33
+ragged tiles as half-width tiles, some right halves wholly past N); 4352 x 4096 x 320 (one
+whole round, 16 half-width tile pairs on their XCDs, three K stages); 300 x 520 x 256 has
+ragged tiles; K = 96 takes the generic staging path.  The FFN-up shape 8192 x 9216 x 3072
+(four whole rounds, then 128 tiles as half-width tiles) is compared whole, twice in a row.
 """
 import numpy as np
 import pytest
@@ -21,7 +25,7 @@ from gpu_util import GEMM_TOL, dev, to_gpu_qtensor
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(2000, 4000, 192), (4112, 4112, 192), (300, 520, 256), (256, 512, 96)]
+SHAPES = [(2000, 4000, 192), (4112, 4112, 192), (4352, 4096, 320), (300, 520, 256), (256, 512, 96)]
 BF16_U = 2.0 ** -8   # unit roundoff of bfloat16 nearest-even (8 significant bits)
 
 
@@ -78,6 +82,26 @@ def test_bf16_is_the_fp32_result_rounded(nv, operands, monkeypatch):
     torch.cuda.synchronize()
     assert torch.equal(bits16(c16), bits16(c32.to(torch.bfloat16)))
     assert torch.equal(tmax.view(torch.int32), tile_maxima(c16).view(torch.int32))
+
+
+def test_bf16_ffn_up_full_size(nv, monkeypatch):
+    """8192 x 9216 x 3072 as the benchmark runs it (whole rounds, then half-width tiles): bit for
+    bit the per-tile FP32 product rounded, and the tile maxima, on two calls in a row."""
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    ffn = synthetic.ffn()
+    print("gemm bf16 FFN-up 8192x9216x3072", flush=True)
+    qx, _ = nv.nvfp4_quantize(ffn["X"].to(dev()), nv.quant_params(rowwise=True))
+    qw, _ = nv.nvfp4_quantize(ffn["W_up"].to(dev()), nv.quant_params(rowwise=True, block2d=True))
+    setenv(monkeypatch, NVFP4_GEMM_SK=0)
+    ref = nv.nvfp4_gemm(qx, qw).to(torch.bfloat16)
+    setenv(monkeypatch)
+    out = torch.empty_like(ref)
+    tmax = torch.full((nv.load_library().nvfp4_gemm_tiles(8192, 9216),), -1.0, device=dev())
+    for rep in range(2):
+        nv.nvfp4_gemm_bf16(qx, qw, out=out, tile_amax=tmax)
+        torch.cuda.synchronize()
+        assert torch.equal(bits16(out), bits16(ref)), f"call {rep}"
+        assert torch.equal(tmax.view(torch.int32), tile_maxima(out).view(torch.int32)), f"call {rep}"
 
 
 def test_bf16_vs_oracle(nv, oracle, operands, monkeypatch):
