@@ -220,8 +220,8 @@ int nvfp4_dequantize(const nvfp4_qtensor* q, int64_t n, int64_t k, int out_dtype
  * NVFP4 operands); NVFP4 report sec. 4 (FP4 inputs, FP32 output) and A.2 (decode scales
  * stored for the GEMM).  Every product of a decoded element and its block scale is
  * exact in binary16, so the only rounding is the FP32 accumulation.
- * K must be a multiple of 16; M and N any size >= 0; codes 16-byte aligned with row pitch
- * K/2 a multiple of 16 bytes (K % 32 == 0), C 4-byte aligned.
+ * K must be a multiple of 16; M and N any size >= 0; codes 16-byte aligned (row pitch K/2
+ * bytes; when K % 32 == 16 the rows are read 8 bytes at a time), C 4-byte aligned.
  * Schedule: 256 x 256 output tiles, one workgroup per compute unit at a time.  When the
  * last round of tiles would keep at most half the units busy (and K > 128), each of its
  * tiles is split into two K halves computed by two workgroups and summed as

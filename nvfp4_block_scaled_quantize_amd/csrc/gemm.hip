@@ -31,7 +31,7 @@
 //    operand (row past M or N, k past K) gets an offset past the end of its buffer, and
 //    the buffer range check turns its load into zeros.  The choice of which global
 //    chunk each lane fetches lays the tile out in the swizzled order below.
-//  * Generic (any K % 32 == 0): each thread loads its chunks into registers with bounds
+//  * Generic (any K % 16 == 0): each thread loads its chunks into registers with bounds
 //    checks and stores them to LDS; two stages.
 //
 // K ordering.  An MFMA sums over 16 k-slots; lanes 0-31 supply slots 0-7 and lanes
@@ -545,19 +545,32 @@ __device__ __forceinline__ uint2 load_scales8(const uint8_t* base, int64_t row, 
     return make_uint2(w[0], w[1]);
 }
 
+// 16 code bytes at p, the last 8 zero when only 8 are left in the row: rows of K % 32 == 16
+// codes are 8-byte aligned and end in a half chunk.
+__device__ __forceinline__ uint4 load_chunk8(const uint8_t* p, int64_t left) {
+    const uint2 lo = *(const uint2*)p;
+    const uint2 hi = left >= 16 ? *(const uint2*)(p + 8) : make_uint2(0u, 0u);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 __device__ __forceinline__ void load_stage(const GArgs& g, int64_t m0, int64_t n0, int s,
                                            StageRegs& r) {
     const int t = threadIdx.x;
     const int64_t kbytes = g.K / 2, k0b = (int64_t)s * 64;
+    const bool whole = (kbytes & 15) == 0;   // K % 32 == 0: 16-byte aligned whole chunks
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int q = t + GThreads * i, row = q >> 2, ch = q & 3;
         const int64_t off = k0b + ch * 16;
         const int64_t gm = m0 + row, gn = n0 + row;
-        r.a[i] = (gm < g.M && off < kbytes) ? *(const uint4*)(g.ac + gm * kbytes + off)
-                                             : make_uint4(0u, 0u, 0u, 0u);
-        r.b[i] = (gn < g.N && off < kbytes) ? *(const uint4*)(g.bc + gn * kbytes + off)
-                                             : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        if (whole) {
+            r.a[i] = (gm < g.M && off < kbytes) ? *(const uint4*)(g.ac + gm * kbytes + off) : z;
+            r.b[i] = (gn < g.N && off < kbytes) ? *(const uint4*)(g.bc + gn * kbytes + off) : z;
+        } else {
+            r.a[i] = (gm < g.M && off < kbytes) ? load_chunk8(g.ac + gm * kbytes + off, kbytes - off) : z;
+            r.b[i] = (gn < g.N && off < kbytes) ? load_chunk8(g.bc + gn * kbytes + off, kbytes - off) : z;
+        }
     }
     const int64_t kblocks = g.K / 16, kb0 = (int64_t)s * 8;
     r.sa = load_scales8(g.as, m0 + t, g.M, kb0, kblocks);
@@ -1559,7 +1572,7 @@ static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M
                        int64_t lr, const float* d, int64_t ldd, float alpha, float beta,
                        void* stream, uint16_t* c16 = nullptr, float* tmax = nullptr) {
     if (!a || !b || !a->gscale || !b->gscale) return NVFP4_ERR_NULL;
-    if (M < 0 || N < 0 || K < 0 || K % 32 || ldc < N) return NVFP4_ERR_SHAPE;
+    if (M < 0 || N < 0 || K < 0 || K % 16 || ldc < N) return NVFP4_ERR_SHAPE;
     if (lr < 0 || lr % 16) return NVFP4_ERR_SHAPE;
     if (M == 0 || N == 0) return NVFP4_OK;
     if (!c && !c16) return NVFP4_ERR_NULL;

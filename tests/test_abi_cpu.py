@@ -161,7 +161,7 @@ def test_gemm_bf16_and_quantize_amax_argument_errors(nv):
     assert g(16, 16, 32, cc=None) == -1                             # no output
     assert g(16, 16, 32, cc=ctypes.c_void_p(FAKE + 0x200001)) == -3  # bf16 output misaligned
     assert g(16, 16, 32, t=ctypes.c_void_p(FAKE + 0x280002)) == -3   # tile maxima misaligned
-    assert g(16, 16, 48) == -2                                       # K % 32
+    assert g(16, 16, 40) == -2                                       # K % 16
     assert g(0, 16, 32) == 0                                         # empty
     assert lib.nvfp4_gemm_tiles(8192, 9216) == 32 * 36
     assert lib.nvfp4_gemm_tiles(257, 1) == 2 and lib.nvfp4_gemm_tiles(0, 5) == 0
@@ -182,7 +182,7 @@ def test_gemm_and_dequantize_argument_errors(nv):
     a, b = _qt(FAKE), _qt(FAKE + 0x100000)
     c = ctypes.c_void_p(FAKE + 0x200000)
     assert lib.nvfp4_gemm(None, ctypes.byref(b), 16, 16, 32, c, 16, None) == -1
-    assert lib.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), 16, 16, 48, c, 16, None) == -2  # K % 32
+    assert lib.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), 16, 16, 40, c, 16, None) == -2  # K % 16
     assert lib.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), 16, 16, 32, c, 8, None) == -2   # ldc < N
     assert lib.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), -1, 16, 32, c, 16, None) == -2
     assert lib.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), 16, 16, 32, None, 16, None) == -1

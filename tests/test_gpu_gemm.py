@@ -36,7 +36,9 @@ def quantized_pair(oracle, M, N, K, seed, wstd=0.02):
 
 @pytest.mark.parametrize("M,N,K", [(16, 16, 32), (128, 128, 256), (48, 80, 64), (272, 400, 160),
                                    (528, 272, 416), (256, 256, 128 * 3 + 32), (64, 96, 1024),
-                                   (16, 512, 32)])
+                                   (16, 512, 32),
+                                   # K % 32 == 16: rows end in a half chunk, read 8 bytes at a time
+                                   (16, 16, 16), (48, 80, 48), (272, 400, 144), (304, 272, 16 * 27)])
 def test_gemm_small_shapes_full_matrix(nv, oracle, M, N, K):
     print(f"gemm case {M}x{N}x{K}", flush=True)
     qa, qb = quantized_pair(oracle, M, N, K, 100 + M + N + K)
