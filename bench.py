@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the step as eager launches instead of replays of a HIP graph")
     ap.add_argument("--cpu-sample-rows", type=int, default=8192,
                     help="rows of X for the oracle's bounded CPU sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -484,13 +486,26 @@ def main():
     for _ in range(args.warmup):
         step(None)
     torch.cuda.synchronize()
+    # per-call times: K eager steps with HIP events between the calls
     events = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(events)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_eager = (t1 - t0) * 1e3 / args.steps
+    # the step time: the same step captured once as a HIP graph, W replays, then K timed
+    # replays (eager launches with --eager, or if the capture is refused)
+    timing = {"mode": "eager", "eager_ms_per_step": round(ms_eager, 4)}
+    ms_per_step = ms_eager
+    if not args.eager:
+        try:
+            ms_graph = graph_step(torch, step, args.steps, args.warmup)
+            timing = {"mode": "hip_graph", "eager_ms_per_step": round(ms_eager, 4),
+                      "graph_ms_per_step": round(ms_graph, 4)}
+            ms_per_step = ms_graph
+        except RuntimeError as exc:
+            timing["graph_error"] = str(exc)[:200]
 
     per = {}
     for name, s, e in events:
@@ -554,6 +569,7 @@ def main():
         "kernels": kernels,
     }
 
+    out["step_timing"] = timing
     out["qadamw_v_error"] = qadamw_error(nv, torch, v, v_out)
     out["kernels_isolated"] = isolated(torch, dev, calls, work, stream)
     out["extras"] = extras(nv, synthetic, torch, dev, X, dY, p_x, p_dy, qx, qdy, qw, stream)
@@ -566,6 +582,29 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, synthetic, ffn)
     print(json.dumps(out))
+
+
+def graph_step(torch, step, steps, warmup):
+    """ms per step of the step captured once into a HIP graph (every call is allocation-,
+    memset- and synchronisation-free) and replayed: W untimed replays, then K timed ones
+    bracketed by device synchronisations."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(None)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(None)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
 
 
 def qadamw_error(nv, torch, v, v_hat):
