@@ -80,7 +80,7 @@ SOURCES = {
 FAMILY = {"gemm": "gemm", "quant": "quant", "qadamw_encode": "qadamw", "qadamw_decode": "qadamw",
           "qadamw_step": "qadamw", "dequant": "quant"}
 # kernels each call of the step launches, in order (name prefixes; '?' marks optional)
-CALL_KERNELS = {"quant": ["?k_amax", "k_encode|k_quant"], "gemm": ["k_gemm"],
+CALL_KERNELS = {"quant": ["?k_amax", "k_encode|k_quant"], "gemm": ["k_gemm", "?k_gemm_half"],
                 "qadamw_encode": ["k_qv_pass1", "k_max_partials", "k_qv_pass2"],
                 "qadamw_decode": ["k_qv_decode"],
                 "qadamw_step": ["k_qs_pass1", "k_max_partials", "k_qs_pass2"],
@@ -218,8 +218,8 @@ def counter_summary(dirs):
     order = STEP_ORDER
     lines = ["# HBM traffic per launch from rocprofv3 --pmc (TCC FETCH_SIZE, WRITE_SIZE; one pass each)",
              "# commands (from the repository root, cd /tmp && TMPDIR=/tmp first):",
-             "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <f> -o bench -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
-             "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <w> -o bench -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
+             "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <f> -o bench -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --eager",
+             "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <w> -o bench -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --eager",
              "#   rocprofv3 --pmc FETCH_SIZE ... -d <cf> -o copy -- python3 bench.py --copy-calibration   (and WRITE_SIZE -> <cw>)",
              "#   python3 bench.py --counter-summary <f> <w> <cf> <cw>",
              f"# calibration: a 256 MiB device copy reads {sum(fc[-5:]) / 5 / 2**20:.1f} MiB FETCH_SIZE and "
@@ -257,7 +257,7 @@ def mfma_summary(d):
     lines = ["# Matrix-core busy fraction and effective clock of the step's GEMMs (rocprofv3 --pmc)",
              "# commands (from the repository root, cd /tmp && TMPDIR=/tmp first):",
              "#   rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES --kernel-trace --output-format csv \\",
-             "#       -d <m> -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+             "#       -d <m> -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --eager",
              "#   python3 bench.py --mfma-summary <m>   (the last of the two steps)",
              "# clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs",
              "# x GRBM_GUI_ACTIVE / 8); durations are longer than uncounted ones (collection overhead)",
@@ -313,7 +313,7 @@ def valu_summary(d):
     lines = ["# Vector-ALU work of the step's quantize, optimizer-state and decode kernels (rocprofv3 --pmc)",
              "# commands (from the repository root, cd /tmp && TMPDIR=/tmp first):",
              "#   rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_ACTIVE_INST_VALU --kernel-trace \\",
-             "#       --output-format csv -d <v> -o bench -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
+             "#       --output-format csv -d <v> -o bench -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --eager",
              "#   python3 bench.py --valu-summary <v>",
              "# valu/elem = SQ_INSTS_VALU x 64 / input elements; issue_us = SQ_INSTS_VALU x 2 cycles / 1024 SIMDs",
              "# / 2.4 GHz (fp32-add rate; 64-bit integer products ~4 cycles, sqrt/rcp ~8); issue/us = issue_us / us.",
@@ -530,7 +530,9 @@ def main():
     q_ms = sum(kernels[n]["ms"] for n in q_names)
     up = kernels["gemm_ffn_up"]
     up_flops = work["gemm_ffn_up"][2]
-    roofline = {"bound": "mfma", "kernel": "k_gemm_dma<EpiBf16> (FFN-up 8192x9216x3072, bf16 out)",
+    roofline = {"bound": "mfma", "kernel": "k_gemm_dma<EpiBf16> + k_gemm_half (FFN-up 8192x9216x3072, "
+                                                 "bf16 out: 4 whole rounds of 256x256 tiles, then "
+                                                 "the last 128 tiles as 256 half-width tiles)",
                 "achieved": up["TFLOP/s"], "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(up["TFLOP/s"] / PEAK_F16_TFLOPS, 4),
                 "traffic": counters_for("gemm_ffn_up", "gemm")}
