@@ -223,11 +223,13 @@ int nvfp4_dequantize(const nvfp4_qtensor* q, int64_t n, int64_t k, int out_dtype
  * K must be a multiple of 16; M and N any size >= 0; codes 16-byte aligned (row pitch K/2
  * bytes; when K % 32 == 16 the rows are read 8 bytes at a time), C 4-byte aligned.
  * Schedule: 256 x 256 output tiles, one workgroup per compute unit at a time.  When the
- * last round of tiles would keep at most half the units busy (and K > 128), each of its
- * tiles is split into two K halves computed by two workgroups and summed as
+ * last round of tiles would keep at most half the units busy, it runs either as twice as
+ * many 256 x 128 tiles, each over the whole K range (every element is then the sum one
+ * workgroup per tile forms), or, when the whole rounds are long (rounds x ceil(K/128) >= 64),
+ * with each of its tiles split into two K halves computed by two workgroups and summed as
  * fl(head + tail) of the two FP32 partial accumulations; the tail half is parked in the
  * tile's own region of C meanwhile.  Results are bitwise reproducible on a given device
- * (they depend on its compute-unit count through this split). */
+ * (they depend on its compute-unit count through that choice and split). */
 int nvfp4_gemm(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M, int64_t N,
                int64_t K, float* c, int64_t ldc, void* stream);
 

@@ -936,7 +936,7 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
         tri_tile(blockIdx.x - kp * ntri, g.tiles_m, tm, tn);
         c.s0 = (int)((int64_t)kp * nst_all / g.kparts);
         c.nst = (int)((int64_t)(kp + 1) * nst_all / g.kparts) - c.s0;
-    } else if (EPI == EpiBf16 && g.sk_g > 0) {
+    } else if ((EPI == EpiBf16 || EPI == EpiPlain) && g.sk_g > 0) {
         // whole rounds before a round of half-width tiles: block b takes tile id
         // (b / G) G + sk_virtual(b mod G) (as the balanced FP32 kernel's whole rounds), and
         // block 0 zeroes the remaining tiles' maxima, which k_gemm_half then combines
@@ -1201,13 +1201,36 @@ __device__ __forceinline__ float nr_store_bf16(const GArgs& g, const float16v (&
     return mx;
 }
 
-// The last round of a bf16 product as half-width tiles: block u takes column half `half` of
+// FP32 output of a half-width tile (non-temporal, as store_rows).
+template <bool FULL>
+__device__ __forceinline__ void nr_store_f32(const GArgs& g, const float16v (&acc)[4][2], const DmaCtx& c,
+                                             float scale) {
+    const int64_t rbase = c.m0 + c.wm * 128 + 4 * c.h, cbase = c.n0 + c.wn * 64 + c.li;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+            float* rowp = g.c + row * g.ldc + cbase;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                if (FULL || (row < g.M && cbase + j * 32 < g.N))
+                    __builtin_nontemporal_store(acc[i][j][r] * scale, rowp + j * 32);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The last round of a product as half-width tiles: block u takes column half `half` of
 // tile id base + i (base = sk_rounds sk_g, grouped_tile order), both halves of a tile on one
 // XCD when sk_rem % 8 == 0 (blocks 16 k + x and 16 k + 8 + x take tile 8 k + x), else on
 // blocks 2 i and 2 i + 1.  The tile's maximum of |C| is the larger of its halves' maxima,
 // combined by an atomic maximum on the binary32 bits (non-negative values order like their
-// bits) into an entry that k_gemm_dma<EpiBf16> zeroed before this launch.
+// bits) into an entry that k_gemm_dma<EpiBf16> zeroed before this launch.  EPI: EpiBf16 or
+// EpiPlain (FP32 C).
+template <int EPI>
 __global__ __launch_bounds__(GThreads, 1) void k_gemm_half(GArgs g) {
+    static_assert(EPI == EpiBf16 || EPI == EpiPlain, "bf16 and FP32 epilogues");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     DmaCtx c;
     init_ctx(c, g, lds);
@@ -1245,8 +1268,13 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm_half(GArgs g) {
     dma_wait_barrier<0>();
 
     const float scale = *g.asg * *g.bsg;
-    float mx = c.m0 + GBM <= g.M && c.n0 + GBN / 2 <= g.N ? nr_store_bf16<true>(g, acc, c, scale)
-                                                           : nr_store_bf16<false>(g, acc, c, scale);
+    const bool full = c.m0 + GBM <= g.M && c.n0 + GBN / 2 <= g.N;
+    if constexpr (EPI == EpiPlain) {
+        if (full) nr_store_f32<true>(g, acc, c, scale);
+        else nr_store_f32<false>(g, acc, c, scale);
+        return;
+    }
+    float mx = full ? nr_store_bf16<true>(g, acc, c, scale) : nr_store_bf16<false>(g, acc, c, scale);
     if (g.tmax) {
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
@@ -1533,10 +1561,11 @@ int syrk_splitk(const nvfp4_qtensor* a, int64_t m, int64_t k, float* c, int64_t 
 
 using namespace nvfp4;
 
-// Balanced schedule settings, for tests and measurements: NVFP4_GEMM_SK=0 keeps one
-// workgroup per tile; NVFP4_GEMM_SK_SPIN sets the head's wait for a tail part (wall-clock
-// ticks, 100 MHz; default 20 ms); NVFP4_GEMM_SK_TEST=1 makes every tail skip its hand-off
-// so that every split tile takes the head's fallback.
+// Schedule settings, for tests and measurements: NVFP4_GEMM_SK=0 keeps one workgroup per
+// tile, 1 (the default) chooses as below, 2 takes the balanced K split and 3 the half-width
+// tiles whenever the last round qualifies; NVFP4_GEMM_SK_SPIN sets the balanced schedule's
+// wait for a tail part (wall-clock ticks, 100 MHz; default 20 ms); NVFP4_GEMM_SK_TEST=1 makes
+// every tail skip its hand-off so that every split tile takes the head's fallback.
 static int env_int(const char* name, int dflt) {
     const char* e = getenv(name);
     return e && *e ? atoi(e) : dflt;
@@ -1628,28 +1657,48 @@ static int gemm_launch(const nvfp4_qtensor* a, const nvfp4_qtensor* b, int64_t M
                             direct ? kGemmDmaLds : kGemmLds) != hipSuccess)
         return NVFP4_ERR_HIP;
     hipStream_t st = (hipStream_t)stream;
-    // balanced schedule (plain epilogue): a last round at most half full and at least two K
-    // stages per tile.  The axpby epilogue keeps one workgroup per tile (D may be C, which
-    // holds the tail halves), and so does the low-rank one (in this loop its epilogue spills
-    // and runs slower than the rounds it saves)
+    // A last round of tiles at most half full (plain and bf16 epilogues, direct path) runs
+    // either as twice as many half-width tiles over the whole K range (the per-tile sums), or,
+    // for FP32 output, with each of its tiles split into two K halves on two workgroups (the
+    // balanced schedule, fl(head + tail)).  The split pays where a workgroup's whole rounds
+    // are long (rounds x K stages >= 64: FFN-down 1 x 72, FP32 FFN-up 4 x 24, 3-4% ahead);
+    // below that its hand-off costs more than it saves (2000 x 4000 x 192: 58 us against
+    // 19 us), and bf16 has no room for the parked half.  The axpby epilogue keeps one
+    // workgroup per tile (D may be C), and so does the low-rank one (its epilogue spills in
+    // the balanced loop and runs slower than the rounds it saves).
     int dev = 0;
-    const int G = direct && (epi == EpiPlain || epi == EpiBf16) && env_int("NVFP4_GEMM_SK", 1)
-                      ? sk_groups(&dev) : 0;
+    const int sk_mode = env_int("NVFP4_GEMM_SK", 1);
+    const int G = direct && (epi == EpiPlain || epi == EpiBf16) && sk_mode ? sk_groups(&dev) : 0;
     const int sk_nst = (int)((K + GBK - 1) / GBK), sk_rem = G > 0 ? (int)(grid % G) : 0;
-    if (epi == EpiBf16 && sk_rem > 0 && 2 * sk_rem <= G && (int)(grid / G) > 0) {
+    const int sk_q = G > 0 ? (int)(grid / G) : 0;
+    const bool tail = sk_rem > 0 && 2 * sk_rem <= G;
+    const bool balanced = epi == EpiPlain && tail && sk_nst >= 2 && sk_mode != 3 &&
+                          (sk_mode == 2 || sk_q * sk_nst >= 64);
+    if (epi == EpiBf16 && tail && sk_q > 0) {
         // bf16: the whole rounds, then the remaining tiles as twice as many half-width tiles
         // (k_gemm_half), each over the whole K range: the same sums as one workgroup per tile
-        if (hipFuncSetAttribute((const void*)k_gemm_half, hipFuncAttributeMaxDynamicSharedMemorySize,
+        if (hipFuncSetAttribute((const void*)k_gemm_half<EpiBf16>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 kGemmDmaLds) != hipSuccess)
             return NVFP4_ERR_HIP;
         g.sk_g = G;
         g.sk_rounds = (int)(grid / G);
         g.sk_rem = sk_rem;
         k_gemm_dma<EpiBf16><<<g.sk_rounds * G, GThreads, kGemmDmaLds, st>>>(g);
-        k_gemm_half<<<2 * sk_rem, GThreads, kGemmDmaLds, st>>>(g);
+        k_gemm_half<EpiBf16><<<2 * sk_rem, GThreads, kGemmDmaLds, st>>>(g);
         return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
     }
-    if (epi == EpiPlain && sk_rem > 0 && 2 * sk_rem <= G && sk_nst >= 2) {
+    if (epi == EpiPlain && tail && !balanced) {
+        if (hipFuncSetAttribute((const void*)k_gemm_half<EpiPlain>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kGemmDmaLds) != hipSuccess)
+            return NVFP4_ERR_HIP;
+        g.sk_g = G;
+        g.sk_rounds = (int)(grid / G);
+        g.sk_rem = sk_rem;
+        if (g.sk_rounds > 0) k_gemm_dma<EpiPlain><<<g.sk_rounds * G, GThreads, kGemmDmaLds, st>>>(g);
+        k_gemm_half<EpiPlain><<<2 * sk_rem, GThreads, kGemmDmaLds, st>>>(g);
+        return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+    }
+    if (balanced) {
         if (hipFuncSetAttribute((const void*)k_gemm_sk<EpiPlain>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 kGemmDmaLds) != hipSuccess)
             return NVFP4_ERR_HIP;

@@ -1,11 +1,13 @@
 """GPU parity of the GEMM's balanced (stream-K) schedule.
 
 When the last round of 256 x 256 output tiles would keep at most half of the compute units
-busy, nvfp4_gemm runs the whole rounds with one tile per workgroup and splits each
-remaining tile into two K halves on two workgroups; such a tile is summed as
-fl(head + tail) of two partial FP32 accumulations.  Checks, on two ragged shapes with two
+busy, nvfp4_gemm runs the whole rounds with one tile per workgroup and either splits each
+remaining tile into two K halves on two workgroups (such a tile is summed as fl(head + tail)
+of two partial FP32 accumulations) or runs the remaining tiles as twice as many half-width
+tiles.  It picks the split for long whole rounds only; NVFP4_GEMM_SK=2 forces the split and
+NVFP4_GEMM_SK=3 the half-width tiles, so both are checked here on two ragged shapes with two
 K stages per tile (one stage per half): 2000 x 4000 x 192 (8 x 16 = 128 tiles, every one
-split) and 4112 x 4112 x 192 (289 tiles: one whole round, then 33 split tiles):
+split) and 4112 x 4112 x 192 (289 tiles: one whole round, then 33 split tiles).  Split:
   * the whole output against the oracle's binary64 GEMM, to the GEMM tolerance;
   * the schedule against one workgroup per tile (NVFP4_GEMM_SK=0), to the same tolerance;
   * the head's fallback (the tail part computed by the head after it claims the tile) is bit
@@ -14,6 +16,8 @@ split) and 4112 x 4112 x 192 (289 tiles: one whole round, then 33 split tiles):
     (heads and tails race for each tile);
   * nvfp4_gemm_lora at the same shapes (one workgroup per tile: its epilogue does not take
     the balanced schedule) against the oracle.
+Half-width tiles: bit for bit one workgroup per tile (NVFP4_GEMM_SK=0), and what the default
+choice runs on these short-K shapes.
 """
 import numpy as np
 import pytest
@@ -53,8 +57,10 @@ def cus():
 
 
 def run(nv, qa, qb, monkeypatch, lora=None, **env):
+    """nvfp4_gemm (or its LoRA form) with the balanced split forced unless env says otherwise."""
     for k in ("NVFP4_GEMM_SK", "NVFP4_GEMM_SK_SPIN", "NVFP4_GEMM_SK_TEST"):
         monkeypatch.delenv(k, raising=False)
+    env.setdefault("NVFP4_GEMM_SK", 2)
     for k, v in env.items():
         monkeypatch.setenv(k, str(v))
     ga, gb = to_gpu_qtensor(nv, qa), to_gpu_qtensor(nv, qb)
@@ -146,3 +152,13 @@ def test_balanced_graph_replays(nv, operands, monkeypatch):
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"replay {rep}"
         assert torch.equal(other.view(torch.int32), ref.view(torch.int32)), f"eager {rep}"
+
+
+def test_half_width_tiles_are_the_per_tile_sums(nv, operands, monkeypatch):
+    qa, qb = operands
+    print(f"half-width last round {qa.shape[0]}x{qb.shape[0]}x{K}", flush=True)
+    per_tile = run(nv, qa, qb, monkeypatch, NVFP4_GEMM_SK=0)
+    half = run(nv, qa, qb, monkeypatch, NVFP4_GEMM_SK=3)
+    auto = run(nv, qa, qb, monkeypatch, NVFP4_GEMM_SK=1)
+    assert torch.equal(half.view(torch.int32), per_tile.view(torch.int32))
+    assert torch.equal(auto.view(torch.int32), half.view(torch.int32))
