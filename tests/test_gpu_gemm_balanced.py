@@ -162,3 +162,26 @@ def test_half_width_tiles_are_the_per_tile_sums(nv, operands, monkeypatch):
     auto = run(nv, qa, qb, monkeypatch, NVFP4_GEMM_SK=1)
     assert torch.equal(half.view(torch.int32), per_tile.view(torch.int32))
     assert torch.equal(auto.view(torch.int32), half.view(torch.int32))
+
+
+@pytest.mark.parametrize("M,N,Kf", [(8192, 3072, 9216), (8192, 9216, 3072)])
+def test_half_width_full_size(nv, monkeypatch, M, N, Kf):
+    """The step's FFN-down / dgrad shape (one whole round, 128 tiles left, 72 K stages) and the
+    FP32 FFN-up shape (four whole rounds, 128 left), with the half-width last round forced:
+    bit for bit one workgroup per tile.  GPU-quantized operands (the quantizer is checked bit
+    for bit against the oracle elsewhere)."""
+    from nvfp4_block_scaled_quantize_amd import synthetic
+    print(f"half-width last round at full size {M}x{N}x{Kf}", flush=True)
+    a = synthetic.outlier_channels((M, Kf), 7001).to(torch.bfloat16).to(dev())
+    b = synthetic.normal((N, Kf), 7002, 0.02).to(torch.bfloat16).to(dev())
+    qa, _ = nv.nvfp4_quantize(a, nv.quant_params(rowwise=True))
+    qb, _ = nv.nvfp4_quantize(b, nv.quant_params(rowwise=True))
+    del a, b
+    for k in ("NVFP4_GEMM_SK", "NVFP4_GEMM_SK_SPIN", "NVFP4_GEMM_SK_TEST"):
+        monkeypatch.delenv(k, raising=False)
+    monkeypatch.setenv("NVFP4_GEMM_SK", "0")
+    per_tile = nv.nvfp4_gemm(qa, qb)
+    monkeypatch.setenv("NVFP4_GEMM_SK", "3")
+    half = nv.nvfp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    assert torch.equal(half.view(torch.int32), per_tile.view(torch.int32))
