@@ -94,7 +94,7 @@ struct GArgs {
     // EpiBf16: C as bfloat16 (row pitch ldc) and each tile's maximum of |C| (or null)
     uint16_t* c16;
     float* tmax;
-    // bf16 product with a last round of half-width tiles (k_gemm_half): sk_g workgroups per
+    // a product whose last round runs as half-width tiles (k_gemm_half): sk_g workgroups per
     // round, sk_rounds whole rounds, sk_rem remaining tiles; 0 when there is none
     int sk_g;
 };
@@ -964,10 +964,11 @@ __global__ __launch_bounds__(GThreads, 1) void k_gemm_dma(GArgs g) {
 // A 256 x 128 tile per workgroup, on the direct path's stages and LDS layout (B rows 0..127
 // of each stage used): wave (wm, wn) owns a 128 x 64 sub-tile as 4 x 2 MFMA 32x32x16
 // accumulators.  Every element of C sees the same MFMAs in the same order as in a 256 x 256
-// tile, so the two agree bit for bit.  Used for the last round of a bf16 product when it is
-// at most half full: its tiles then run as twice as many half-width tiles, each over the
-// whole K range, so no partial sums are handed between workgroups.  A wave issues 9 direct
-// loads per stage: 4 + 2 code chunks, 2 + 1 scale words (A, then B).
+// tile, so the two agree bit for bit.  Used for a last round at most half full (bf16 output
+// always, FP32 output where the balanced K split does not pay): its tiles then run as twice
+// as many half-width tiles, each over the whole K range, so no partial sums are handed
+// between workgroups.  A wave issues 9 direct loads per stage: 4 + 2 code chunks, 2 + 1
+// scale words (A, then B).
 constexpr int kNrLoadsPerStage = 9;
 
 struct NrLoads {
