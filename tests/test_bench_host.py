@@ -12,14 +12,14 @@ import bench  # noqa: E402
 
 # the kernels one step launches, in order, as rocprofv3 names them
 STEP = [
-    "void nvfp4::k_amax<1, 2>(nvfp4::QArgs)", "void nvfp4::k_encode<1, 8>(nvfp4::QArgs)",
-    "void nvfp4::k_amax<1, 0>(nvfp4::QArgs)", "void nvfp4::k_encode<1, 0>(nvfp4::QArgs)",
-    "void nvfp4::k_gemm_dma<0>(nvfp4::GArgs)",
-    "void nvfp4::k_amax<1, 0>(nvfp4::QArgs)", "void nvfp4::k_encode<1, 0>(nvfp4::QArgs)",
-    "void nvfp4::k_amax<1, 0>(nvfp4::QArgs)", "void nvfp4::k_encode<1, 0>(nvfp4::QArgs)",
-    "void nvfp4::k_gemm_dma<0>(nvfp4::GArgs)",
-    "void nvfp4::k_amax<1, 2>(nvfp4::QArgs)", "void nvfp4::k_encode<1, 11>(nvfp4::QArgs)",
-    "void nvfp4::k_gemm_dma<0>(nvfp4::GArgs)", "void nvfp4::k_gemm_dma<0>(nvfp4::GArgs)",
+    "void nvfp4::k_amax<1, 2>(nvfp4::QArgs)", "void nvfp4::k_encode<1, 8, false>(nvfp4::QArgs)",
+    "void nvfp4::k_amax<1, 0>(nvfp4::QArgs)", "void nvfp4::k_encode<1, 0, false>(nvfp4::QArgs)",
+    "void nvfp4::k_gemm_dma<4>(nvfp4::GArgs)", "void nvfp4::k_gemm_half<4>(nvfp4::GArgs)",
+    "void nvfp4::k_encode<1, 0, true>(nvfp4::QArgs)",          # H: maxima from the GEMM
+    "void nvfp4::k_amax<1, 0>(nvfp4::QArgs)", "void nvfp4::k_encode<1, 0, false>(nvfp4::QArgs)",
+    "void nvfp4::k_gemm_sk<0>(nvfp4::GArgs)",
+    "void nvfp4::k_amax<1, 2>(nvfp4::QArgs)", "void nvfp4::k_encode<1, 11, false>(nvfp4::QArgs)",
+    "void nvfp4::k_gemm_sk<0>(nvfp4::GArgs)", "void nvfp4::k_gemm_dma<0>(nvfp4::GArgs)",
     "nvfp4::k_qv_pass1(nvfp4::QVArgs)", "nvfp4::k_max_partials(float const*, int, int, float*)",
     "nvfp4::k_qv_pass2(nvfp4::QVArgs)",
     "nvfp4::k_qv_decode_w(unsigned short const*, unsigned char const*)",
@@ -42,7 +42,10 @@ def test_split_step_assigns_every_dispatch():
     calls = dict(got[:len(bench.STEP_ORDER)])
     assert [names[i].split("(")[0] for i in calls["qadamw_step_Wup"]] == [
         "nvfp4::k_qs_pass1", "nvfp4::k_max_partials", "nvfp4::k_qs_pass2"]
-    assert len(calls["gemm_ffn_up"]) == 1 and len(calls["quant_H_row"]) == 2
+    # FFN-up: whole rounds, then the half-width last round; H's quantize: the encode alone
+    assert [names[i].split("(")[0] for i in calls["gemm_ffn_up"]] == [
+        "void nvfp4::k_gemm_dma<4>", "void nvfp4::k_gemm_half<4>"]
+    assert len(calls["quant_H_row"]) == 1 and len(calls["gemm_wgrad"]) == 1
 
 
 def test_split_step_rejects_a_partial_step():
