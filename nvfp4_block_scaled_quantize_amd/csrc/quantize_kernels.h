@@ -495,7 +495,9 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
 // Specialised on the input dtype and on F: bit 0 rowwise SR, bit 1 columnwise SR,
 // bit 2 rowwise Hadamard, bit 3 columnwise Hadamard.  ROW1: the rowwise 1-D copy alone (no
 // columnwise copy, 2-D blocks, 4/6 scaling or low-rank term), which leaves out their registers
-// and LDS, so that more workgroups are resident.
+// and LDS, so that more workgroups are resident.  PLAIN: no 2-D blocks, 4/6 scaling or
+// low-rank term (either copy or both), for the same reason (X's row + column-RHT encode:
+// 92 VGPRs and five waves per SIMD instead of 106 and four).
 //
 // The rowwise copy is encoded first, from the patch as loaded (with the row signs flipped in
 // place when it is rotated); the patch is then flipped to the column signs and the
@@ -504,7 +506,7 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
 // exact for every block whose codes can differ: no 4/6 scaling (its squared errors use the
 // rotated values themselves) and 2^-92 <= s_g <= 2^110 (no reciprocal is then subnormal,
 // and elements small enough to be rounded by the 1/4 quantize to 0 either way).
-template <int IN, int F, bool ROW1 = false>
+template <int IN, int F, bool ROW1 = false, bool PLAIN = ROW1>
 __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
     constexpr bool SR_ROW = F & 1, SR_COL = (F >> 1) & 1;
     constexpr bool RHT_ROW = (F >> 2) & 1, RHT_COL = (F >> 3) & 1;
@@ -606,15 +608,15 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
     __syncthreads();
     const CopyScale rsc{sg_r, __fdiv_rn(1.0f, sg_r), sg_r >= 0x1p-92f, rtab[0], conv_scale(tiny_r)};
     const CopyScale csc{sg_c, __fdiv_rn(1.0f, sg_c), sg_c >= 0x1p-92f, rtab[1], conv_scale(tiny_c)};
-    const bool fold_r = RHT_ROW && !(!ROW1 && a.scale46) && sg_r >= 0x1p-92f && sg_r <= 0x1p110f;
-    const bool fold_c = RHT_COL && !(!ROW1 && a.scale46) && sg_c >= 0x1p-92f && sg_c <= 0x1p110f;
+    const bool fold_r = RHT_ROW && !(!PLAIN && a.scale46) && sg_r >= 0x1p-92f && sg_r <= 0x1p110f;
+    const bool fold_c = RHT_COL && !(!PLAIN && a.scale46) && sg_c >= 0x1p-92f && sg_c <= 0x1p110f;
     const uint32_t signs =
         (RHT_ROW || RHT_COL) ? __builtin_amdgcn_readfirstlane(rht_sign_bits(a.k0, a.k1)) : 0u;
 
     // LoRA-SVD down-projection: T = BF16(beta * sum of the K-part partials, in part order)
     // (after the tensor scales, so that this uniform branch does not stand between the
     // loads above and their first use)
-    if ((!ROW1 && a.lora_t)) {
+    if ((!PLAIN && a.lora_t)) {
         const int64_t total = a.rows * a.lora_r;
         for (int64_t e = (int64_t)blockIdx.x * kThreads + t; e < total;
              e += (int64_t)gridDim.x * kThreads) {
@@ -627,7 +629,7 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
     // A rowwise NVFP4 input (IN == 2) asks for the columnwise 1-D copy alone.
     constexpr bool kRowsOrTiles = IN != 2;
     uint32_t scode2d = 0;
-    if (kRowsOrTiles && (!ROW1 && a.block2d)) {  // one scale per 16x16 tile = this patch and its neighbour's
+    if (kRowsOrTiles && (!PLAIN && a.block2d)) {  // one scale per 16x16 tile = this patch and its neighbour's
         scode2d = rsc.code(pair_max(P.amax()), 6.0f, kRcp6);
     }
 
@@ -652,13 +654,13 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
             uint32_t scode, rcodes = 0;
             bool have = false;   // nearest-even codes already formed by the 4/6 choice
             float rscale = 1.0f; // 1/4 when the rotation's factor is folded in
-            if ((!ROW1 && a.block2d)) {
+            if ((!PLAIN && a.block2d)) {
                 scode = scode2d;
             } else {
                 float am = pair_max(amax8(w));
                 if (RHT_ROW && fold_r) { am = am * 0.25f; rscale = 0.25f; }
                 scode = rsc.code(am, 6.0f, kRcp6);
-                if ((!ROW1 && a.scale46)) {
+                if ((!PLAIN && a.scale46)) {
                     // the block's halves sit in this lane and lane ^ 1; a + b == b + a, so
                     // both lanes form the same (elements 0..7) + (elements 8..15) sum
                     const uint32_t sc4 = rsc.code(am, 4.0f, 0.25f);
@@ -715,13 +717,13 @@ __global__ __launch_bounds__(kThreads) void k_encode(QArgs a) {
             uint32_t scode, rlo = 0, rhi = 0;
             bool have = false;   // nearest-even codes already formed by the 4/6 choice
             float rscale = 1.0f;
-            if ((!ROW1 && a.block2d)) {
+            if ((!PLAIN && a.block2d)) {
                 scode = scode2d;
             } else {
                 float am = fmaxf(amax8(&w[0]), amax8(&w[8]));
                 if (RHT_COL && fold_c) { am = am * 0.25f; rscale = 0.25f; }
                 scode = csc.code(am, 6.0f, kRcp6);
-                if ((!ROW1 && a.scale46)) {
+                if ((!PLAIN && a.scale46)) {
                     const uint32_t sc4 = csc.code(am, 4.0f, 0.25f);
                     const float s6 = e4m3_value(scode), s4 = e4m3_value(sc4);
                     uint32_t l6, h6, l4, h4;
@@ -1007,6 +1009,12 @@ void launch_quant(const QArgs& a, hipStream_t st) {
     if constexpr ((F & 10) == 0) {   // no columnwise option bits: a rowwise-only variant
         if (a.rowwise && !a.colwise && !a.block2d && !a.scale46 && !a.lora_t) {
             k_encode<IN, F, true><<<a.ntiles, kThreads, 0, st>>>(a);
+            return;
+        }
+    }
+    if constexpr (IN != 2) {
+        if (!a.block2d && !a.scale46 && !a.lora_t) {
+            k_encode<IN, F, false, true><<<a.ntiles, kThreads, 0, st>>>(a);
             return;
         }
     }
