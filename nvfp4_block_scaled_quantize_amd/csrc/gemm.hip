@@ -275,7 +275,10 @@ __device__ __forceinline__ void store_tile(const GArgs& g, const float16v (&acc)
 
 // bfloat16 output: C = bf16_rne(fl(acc s)), one block row at a time as in store_rows.
 // Returns this lane's maximum of fl(|acc| s) over the elements it stores (NaN ignored);
-// rounding is monotone, so the largest |C| is that maximum rounded to bf16.
+// rounding is monotone, so the largest |C| is that maximum rounded to bf16.  Ordinary stores,
+// unlike the FP32 output's non-temporal ones: a bf16 C of FFN-up size (151 MB) then stays in
+// the 256 MB last-level cache for the kernel that reads it next (its quantize), at no cost
+// to this kernel.
 template <bool FULL>
 __device__ __forceinline__ float store_rows_bf16(const GArgs& g, const float16v (&acc)[4][4],
                                                  int64_t m0, int64_t n0, int wm, int wn, int h,
@@ -293,7 +296,7 @@ __device__ __forceinline__ float store_rows_bf16(const GArgs& g, const float16v 
                 if (FULL || (row < g.M && cbase + j * 32 < g.N)) {
                     const float y = acc[i][j][r] * scale;
                     mx = fmaxf(mx, fabsf(y));
-                    __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, (__bf16)y), rowp + j * 32);
+                    rowp[j * 32] = __builtin_bit_cast(uint16_t, (__bf16)y);
                 }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1194,7 +1197,7 @@ __device__ __forceinline__ float nr_store_bf16(const GArgs& g, const float16v (&
                 if (FULL || (row < g.M && cbase + j * 32 < g.N)) {
                     const float y = acc[i][j][r] * scale;
                     mx = fmaxf(mx, fabsf(y));
-                    __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, (__bf16)y), rowp + j * 32);
+                    rowp[j * 32] = __builtin_bit_cast(uint16_t, (__bf16)y);
                 }
         }
         __builtin_amdgcn_sched_barrier(0);
